@@ -1,0 +1,197 @@
+"""MI355X (gfx950) hybrid attention: chunked gated linear attention plus a
+sliding-window + meta-memory softmax branch, with backward and a constant-memory
+decode step.
+
+The functions below are a thin torch-facing binding over the C ABI in
+include/lizard.h (same names without the `lizard_` prefix).  torch only
+allocates device memory and supplies the current HIP stream; every step of the
+computation runs in liblizard.so.  Shapes follow the ABI: q, k [B,H,T,dk];
+v [B,H,T,dv]; log_alpha [B,H,T,dk] float32; meta_k [H,M,dk]; meta_v [H,M,dv];
+states [B,H,dk,dv] float32.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _abi
+from ._abi import LizardError, lib  # noqa: F401
+
+__all__ = ["gla_fwd", "swa_fwd", "hybrid_fwd", "hybrid_bwd", "decode_step",
+           "workspace_bytes", "make_desc", "LizardError", "lib"]
+
+_DTYPES = {torch.float32: _abi.LIZARD_F32, torch.bfloat16: _abi.LIZARD_BF16}
+
+
+def make_desc(B, H, T, dk, dv, window=1, n_meta=0, scale=None, mix=1.0, dtype=torch.bfloat16,
+              chunk=64):
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _abi.Desc(B, H, T, dk, dv, chunk, window, n_meta,
+                     0.0 if scale is None else float(scale), float(mix), _DTYPES[dtype])
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, shape, dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtype):
+    return None if t is None else _need(t, name, shape, dtype)
+
+
+def _meta_pair(meta_k, meta_v, H, dk, dv, dt):
+    if meta_k is None:
+        meta_k = torch.empty(H, 0, dk, device="cuda", dtype=dt)
+        meta_v = torch.empty(H, 0, dv, device="cuda", dtype=dt)
+    M = meta_k.shape[1]
+    _need(meta_k, "meta_k", (H, M, dk), dt)
+    _need(meta_v, "meta_v", (H, M, dv), dt)
+    return meta_k, meta_v, M
+
+
+def workspace_bytes(desc, op):
+    return int(lib().lizard_workspace_bytes(ctypes.byref(desc), op))
+
+
+def gla_fwd(q, k, v, log_alpha, h0=None, return_state=False):
+    """GLA branch alone: o_t = q_t S_t.  Returns o, or (o, hT) with return_state."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q", (B, H, T, dk), dt)
+    _need(k, "k", (B, H, T, dk), dt)
+    _need(v, "v", (B, H, T, dv), dt)
+    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    _opt(h0, "h0", (B, H, dk, dv), torch.float32)
+    o = torch.empty_like(v)
+    hT = torch.empty(B, H, dk, dv, device=q.device, dtype=torch.float32) if return_state else None
+    d = make_desc(B, H, T, dk, dv, dtype=dt)
+    _abi.check("lizard_gla_fwd", lib().lizard_gla_fwd(
+        ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(h0), _p(o), _p(hT),
+        None, 0, _stream()))
+    return (o, hT) if return_state else o
+
+
+def swa_fwd(q, k, v, meta_k, meta_v, window, scale=None, return_lse=False):
+    """Window + meta branch alone.  Returns o_swa, or (o_swa, lse)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q", (B, H, T, dk), dt)
+    _need(k, "k", (B, H, T, dk), dt)
+    _need(v, "v", (B, H, T, dv), dt)
+    meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
+    o = torch.empty_like(v)
+    lse = torch.empty(B, H, T, device=q.device, dtype=torch.float32) if return_lse else None
+    d = make_desc(B, H, T, dk, dv, window, M, scale, 1.0, dt)
+    _abi.check("lizard_swa_fwd", lib().lizard_swa_fwd(
+        ctypes.byref(d), _p(q), _p(k), _p(v), _p(meta_k), _p(meta_v), _p(o), _p(lse), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, h0=None,
+               save_for_backward=False, return_state=False, return_ring=False):
+    """o = o_gla + mix * o_swa.  Returns a dict with "o" and, on request, "lse" and
+    "o_swa" (save_for_backward), "hT" (return_state), "ring_k"/"ring_v" (return_ring)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q", (B, H, T, dk), dt)
+    _need(k, "k", (B, H, T, dk), dt)
+    _need(v, "v", (B, H, T, dv), dt)
+    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
+    _opt(h0, "h0", (B, H, dk, dv), torch.float32)
+    dev = q.device
+    out = {"o": torch.empty_like(v)}
+    if save_for_backward:
+        out["lse"] = torch.empty(B, H, T, device=dev, dtype=torch.float32)
+        out["o_swa"] = torch.empty_like(v)
+    if return_state:
+        out["hT"] = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    if return_ring:
+        out["ring_k"] = torch.empty(B, H, window, dk, device=dev, dtype=dt)
+        out["ring_v"] = torch.empty(B, H, window, dv, device=dev, dtype=dt)
+    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
+    _abi.check("lizard_hybrid_fwd", lib().lizard_hybrid_fwd(
+        ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
+        _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
+        _p(out.get("ring_k")), _p(out.get("ring_v")), None, 0, _stream()))
+    return out
+
+
+def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale=None, mix=1.0,
+               h0=None):
+    """Gradients of sum(dO * o).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _need(q, "q", (B, H, T, dk), dt)
+    _need(k, "k", (B, H, T, dk), dt)
+    _need(v, "v", (B, H, T, dv), dt)
+    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
+    _opt(h0, "h0", (B, H, dk, dv), torch.float32)
+    _need(o_swa, "o_swa", (B, H, T, dv), dt)
+    _need(lse, "lse", (B, H, T), torch.float32)
+    _need(dO, "dO", (B, H, T, dv), dt)
+    dev = q.device
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dlog_alpha": torch.empty_like(log_alpha),
+         "dmeta_k": torch.empty(H, M, dk, device=dev, dtype=torch.float32),
+         "dmeta_v": torch.empty(H, M, dv, device=dev, dtype=torch.float32)}
+    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
+    nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
+    ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
+    _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
+        ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
+        _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]), _p(g["dlog_alpha"]),
+        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(ws), nws, _stream()))
+    return g
+
+
+def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, scale=None,
+                mix=1.0, out=None):
+    """One generation step for B sequences.  Updates state, ring_k/ring_v and pos
+    (int64 [B], device) in place and returns o [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    window = ring_k.shape[2]
+    _need(q, "q", (B, H, dk), dt)
+    _need(k, "k", (B, H, dk), dt)
+    _need(v, "v", (B, H, dv), dt)
+    _need(log_alpha, "log_alpha", (B, H, dk), torch.float32)
+    _need(state, "state", (B, H, dk, dv), torch.float32)
+    _need(ring_k, "ring_k", (B, H, window, dk), dt)
+    _need(ring_v, "ring_v", (B, H, window, dv), dt)
+    _need(pos, "pos", (B,), torch.int64)
+    meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
+    o = torch.empty(B, H, dv, device=q.device, dtype=dt) if out is None else out
+    d = make_desc(B, H, 0, dk, dv, window, M, scale, mix, dt)
+    _abi.check("lizard_decode_step", lib().lizard_decode_step(
+        ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(state), _p(ring_k), _p(ring_v),
+        _p(pos), _p(meta_k), _p(meta_v), _p(o), _stream()))
+    return o
+
+
+def default_scale(dk):
+    return 1.0 / math.sqrt(dk)

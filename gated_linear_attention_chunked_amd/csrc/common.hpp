@@ -1,0 +1,115 @@
+// Device helpers shared by the gfx950 kernels: element types, 16x16 matrix-core
+// tiles and their register layouts.
+//
+// Every matrix product here is a chain of 16x16 output tiles D += A * B with a
+// contraction length of 32 per step:
+//   bf16: one v_mfma_f32_16x16x32_bf16
+//   fp32: eight v_mfma_f32_16x16x4_f32 (one per contraction sub-slice)
+// Both use the same "fragment" layout, so kernels are written once:
+//   lane l = 16*g + r (r = 0..15, g = 0..3)
+//   A fragment: row r of A, eight contraction indices K(g, 0..7)
+//   B fragment: column r of B, the same eight contraction indices K(g, 0..7)
+//   accumulator: column r of D, rows 4*g + 0..3
+// Any fixed map K(g, i) works as long as A and B use the same one; kernels use
+// either K = 8g + i (contiguous) or the "split" map K = 4g + i for i < 4 and
+// 16 + 4g + (i-4) otherwise, which is exactly what an accumulator tile pair
+// holds and so lets a product's result feed the next product without moving.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lz {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware base-2 exponential (v_exp_f32).  Arguments are log2-domain values.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ void mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+// 8 contiguous elements (16 B for bf16, 32 B for fp32).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type ld8(const T* p) {
+  return *reinterpret_cast<const typename Frag<T>::type*>(p);
+}
+
+// Split-map fragment: elements p[0..3] then p[16..19].
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type ld4x2(const T* p);
+template <> __device__ __forceinline__ bf16x8 ld4x2<bf16>(const bf16* p) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <> __device__ __forceinline__ f32x8 ld4x2<float>(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Fragment from an accumulator tile pair (rows 4g..4g+3 of tile a, then of tile b).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type pack_acc(const f32x4& a, const f32x4& b);
+template <> __device__ __forceinline__ bf16x8 pack_acc<bf16>(const f32x4& a, const f32x4& b) {
+  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+template <> __device__ __forceinline__ f32x8 pack_acc<float>(const f32x4& a, const f32x4& b) {
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Store 4 values (one accumulator column slice) as 4 consecutive elements.
+template <typename T> __device__ __forceinline__ void st4(T* p, const f32x4& x);
+template <> __device__ __forceinline__ void st4<bf16>(bf16* p, const f32x4& x) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+template <> __device__ __forceinline__ void st4<float>(float* p, const f32x4& x) {
+  *reinterpret_cast<f32x4*>(p) = x;
+}
+template <typename T> __device__ __forceinline__ f32x4 ld4f(const T* p);
+template <> __device__ __forceinline__ f32x4 ld4f<bf16>(const bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <> __device__ __forceinline__ f32x4 ld4f<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+
+__device__ __forceinline__ float wave_max16(float x) {  // over lanes with equal (lane & 15)
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum16(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace lz

@@ -1,0 +1,47 @@
+// Internal launcher interface between the C ABI host layer and the kernels.
+// Launchers assume the host layer has validated every argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lz {
+
+struct Shape {
+  int B, H, T, dk, dv, window, n_meta;
+  float scale;  // resolved (> 0)
+  float mix;
+  int dtype;    // 0 = f32, 1 = bf16
+};
+
+// GLA branch.  accumulate != 0: o += result instead of o = result.
+hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                          const float* la, const float* h0, void* o, float* hT,
+                          int accumulate, hipStream_t st);
+
+// Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
+// accumulate != 0); o_swa and lse are optional extra outputs.
+hipError_t launch_swa_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                          const void* mk, const void* mv, void* o, float out_scale,
+                          int accumulate, void* o_swa, float* lse, hipStream_t st);
+
+// Window cache after a prefill (slot p mod w <- token p for the last min(T,w) tokens).
+hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* ring_k,
+                            void* ring_v, hipStream_t st);
+
+// hT <- h0 (or zeros) for T == 0.
+hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStream_t st);
+
+hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
+                         const float* la, float* state, void* ring_k, void* ring_v,
+                         int64_t* pos, const void* mk, const void* mv, void* o, hipStream_t st);
+
+// Backward.  Workspace layout is owned by gla_bwd / swa_bwd.
+size_t bwd_workspace_bytes(const Shape& s);
+hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
+                             const float* la, const void* mk, const void* mv, const float* h0,
+                             const void* o_swa, const float* lse, const void* dO, void* dq,
+                             void* dk, void* dv, float* dla, float* dmk, float* dmv, void* ws,
+                             hipStream_t st);
+
+}  // namespace lz

@@ -1,0 +1,164 @@
+// C ABI host layer: argument checks, workspace sizing and dispatch.
+// Every check runs before anything is enqueued; no C++ exception leaves a call.
+#include "../../include/lizard.h"
+
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace {
+
+using lz::Shape;
+
+constexpr int32_t kVersion = 10000;  // 1.0.0
+
+lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
+  if (!d) return LIZARD_E_NULL;
+  if (d->dtype != LIZARD_F32 && d->dtype != LIZARD_BF16) return LIZARD_E_DTYPE;
+  if (d->B < 0 || d->H < 0 || (need_T && d->T < 0)) return LIZARD_E_SHAPE;
+  if (d->dk <= 0 || d->dv <= 0 || d->chunk <= 0 || d->window < 1 || d->n_meta < 0)
+    return LIZARD_E_SHAPE;
+  if (!std::isfinite(d->scale) || !std::isfinite(d->mix)) return LIZARD_E_SHAPE;
+  if (d->chunk != 64) return LIZARD_E_UNSUPPORTED;
+  if (d->dk != d->dv) return LIZARD_E_UNSUPPORTED;
+  if (d->dk != 64 && d->dk != 128) return LIZARD_E_UNSUPPORTED;
+  if (d->dtype == LIZARD_F32 && d->dk != 64) return LIZARD_E_UNSUPPORTED;
+  if (d->n_meta > 16) return LIZARD_E_UNSUPPORTED;
+  const long long bh = (long long)d->B * d->H;
+  if (bh > 65535) return LIZARD_E_UNSUPPORTED;  // work-group grid limit of the prefill kernels
+  if (need_T && bh * (long long)d->T * d->dk > (1LL << 40)) return LIZARD_E_UNSUPPORTED;
+  return LIZARD_OK;
+}
+
+Shape to_shape(const lizard_desc_t* d) {
+  Shape s;
+  s.B = d->B;
+  s.H = d->H;
+  s.T = d->T;
+  s.dk = d->dk;
+  s.dv = d->dv;
+  s.window = d->window;
+  s.n_meta = d->n_meta;
+  s.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  s.mix = d->mix;
+  s.dtype = d->dtype;
+  return s;
+}
+
+bool has_tokens(const lizard_desc_t* d) { return (long long)d->B * d->H * d->T > 0; }
+
+lizard_status_t hip_status(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lizard_status_str(lizard_status_t s) {
+  switch (s) {
+    case LIZARD_OK: return "ok";
+    case LIZARD_E_NULL: return "a required pointer is NULL";
+    case LIZARD_E_SHAPE: return "invalid size or parameter";
+    case LIZARD_E_DTYPE: return "unknown dtype";
+    case LIZARD_E_UNSUPPORTED: return "configuration not supported by this build";
+    case LIZARD_E_WORKSPACE: return "workspace too small";
+    case LIZARD_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t lizard_version(void) { return kVersion; }
+
+size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op) {
+  if (op != LIZARD_OP_HYBRID_BWD) return 0;
+  if (check_desc(desc, true) != LIZARD_OK) return 0;
+  return lz::bwd_workspace_bytes(to_shape(desc));
+}
+
+lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                               const void* v, const float* log_alpha, const float* h0, void* o,
+                               float* hT, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, log_alpha, h0, o, hT, 0, stream));
+}
+
+lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                               const void* v, const void* meta_k, const void* meta_v, void* o,
+                               float* lse, hipStream_t stream) {
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (has_tokens(desc) && (!q || !k || !v || !o)) return LIZARD_E_NULL;
+  if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
+  if (!has_tokens(desc)) return LIZARD_OK;
+  return hip_status(
+      lz::launch_swa_fwd(to_shape(desc), q, k, v, meta_k, meta_v, o, 1.0f, 0, nullptr, lse, stream));
+}
+
+lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* meta_v, const float* h0, void* o, float* lse,
+                                  void* o_swa, float* hT, void* ring_k, void* ring_v, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
+  if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  const Shape s = to_shape(desc);
+  hipError_t e = hipSuccess;
+  if (desc->T > 0) {
+    // window branch first: o = mix * o_swa; then the GLA branch adds o_gla in place
+    e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 0, o_swa, lse, stream);
+    if (e == hipSuccess) e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, 1, stream);
+  } else if (hT) {
+    e = lz::launch_state_copy(s, h0, hT, stream);
+  }
+  if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, k, v, ring_k, ring_v, stream);
+  return hip_status(e);
+}
+
+lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* meta_v, const float* h0, const void* o_swa,
+                                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                  float* dlog_alpha, float* dmeta_k, float* dmeta_v, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  const bool meta = desc->n_meta > 0 && desc->H > 0;
+  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o_swa || !lse || !dO || !dq || !dk ||
+                           !dv || !dlog_alpha))
+    return LIZARD_E_NULL;
+  if (meta && (!meta_k || !meta_v || !dmeta_k || !dmeta_v)) return LIZARD_E_NULL;
+  const Shape s = to_shape(desc);
+  const size_t need = lz::bwd_workspace_bytes(s);
+  if (ws_bytes < need) return LIZARD_E_WORKSPACE;
+  if (need > 0 && !ws) return LIZARD_E_NULL;
+  return hip_status(lz::launch_hybrid_bwd(s, q, k, v, log_alpha, meta_k, meta_v, h0, o_swa, lse,
+                                          dO, dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, ws, stream));
+}
+
+lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
+                                   const void* v, const float* log_alpha, float* state,
+                                   void* ring_k, void* ring_v, int64_t* pos, const void* meta_k,
+                                   const void* meta_v, void* o, hipStream_t stream) {
+  lizard_status_t st = check_desc(desc, false);
+  if (st != LIZARD_OK) return st;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  if (!q || !k || !v || !log_alpha || !state || !ring_k || !ring_v || !pos || !o)
+    return LIZARD_E_NULL;
+  if (desc->n_meta > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
+  // the window softmax keeps w + M logits in LDS
+  if ((long long)desc->window + desc->n_meta > 16384) return LIZARD_E_UNSUPPORTED;
+  return hip_status(lz::launch_decode(to_shape(desc), q, k, v, log_alpha, state, ring_k, ring_v,
+                                      pos, meta_k, meta_v, o, stream));
+}
+
+}  // extern "C"

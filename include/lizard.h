@@ -1,0 +1,154 @@
+/*
+ * lizard.h -- C ABI of the MI355X (gfx950) hybrid-attention library.
+ *
+ * The hybrid layer (source: "Lizard: An Efficient Linearization Framework for
+ * Large Language Models", gist.science technical summary, section 2(a) "Hybrid
+ * attention architecture") adds two branches that read the same q, k, v:
+ *
+ *   GLA branch    S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,   o_gla,t = q_t S_t
+ *                 (the section's constant-memory state update; phi is applied
+ *                 by the caller, alpha_t = exp(log_alpha_t) per key channel)
+ *   window branch one softmax over the keys j in [t-w+1, t] and M meta-memory
+ *                 key/value slots (the section's anchor window whose learnable
+ *                 meta tokens sit in the softmax denominator)
+ *   combine       o_t = o_gla,t + mix * o_swa,t   (the section's weighted sum;
+ *                 the page calls the weight alpha, here it is `mix`)
+ *
+ * Section 2(c) "Hardware-aware algorithm" of the same page absorbs the
+ * cumulative gate into q and k in log space so that the chunk work is a plain
+ * matrix product.  The kernels behind this ABI do that per 64-token chunk with
+ * bf16 matrix-core products and fp32 log-space gates.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, device memory owned by the caller:
+ *       q, k        [B, H, T, dk]      dtype of desc->dtype
+ *       v, o        [B, H, T, dv]      dtype of desc->dtype
+ *       log_alpha   [B, H, T, dk]      float32, finite, <= 0
+ *       meta_k      [H, M, dk]         dtype of desc->dtype (shared by the batch)
+ *       meta_v      [H, M, dv]         dtype of desc->dtype
+ *       state/h0/hT [B, H, dk, dv]     float32 (row = key channel)
+ *       ring_k      [B, H, w, dk]      dtype; slot p mod w holds token p
+ *       ring_v      [B, H, w, dv]      dtype
+ *       lse         [B, H, T]          float32, natural-log sum of exp of the logits
+ *   - The library never allocates, frees or keeps a pointer after a call returns.
+ *     Scratch memory comes from the caller through (ws, ws_bytes); size it with
+ *     lizard_workspace_bytes.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default stream).
+ *     There is no global mutable state: calls on different streams may overlap
+ *     as long as their buffers do not.  Results are deterministic (no float
+ *     atomics; fixed reduction orders).
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns a non-zero status and enqueues nothing.  A launch failure
+ *     returns LIZARD_E_HIP.  NaN/Inf inputs propagate to the outputs.
+ *   - Supported in this version: dk == dv, dk in {64, 128}, chunk == 64,
+ *     window >= 1, 0 <= M <= 16, T >= 0; dtype BF16 for dk in {64, 128},
+ *     F32 for dk == 64.  Output gradients dq, dk, dv use desc->dtype; every
+ *     other output is float32.
+ */
+#ifndef LIZARD_H
+#define LIZARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIZARD_OK = 0,
+  LIZARD_E_NULL = 1,        /* a required pointer is NULL                         */
+  LIZARD_E_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+  LIZARD_E_DTYPE = 3,       /* unknown dtype code                                 */
+  LIZARD_E_UNSUPPORTED = 4, /* valid but not built (e.g. dk = 96, F32 at dk = 128)  */
+  LIZARD_E_WORKSPACE = 5,   /* ws_bytes smaller than lizard_workspace_bytes()     */
+  LIZARD_E_HIP = 6          /* a HIP launch or query failed                       */
+} lizard_status_t;
+
+typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype_t;
+
+typedef enum {
+  LIZARD_OP_GLA_FWD = 0,
+  LIZARD_OP_SWA_FWD = 1,
+  LIZARD_OP_HYBRID_FWD = 2,
+  LIZARD_OP_HYBRID_BWD = 3,
+  LIZARD_OP_DECODE = 4
+} lizard_op_t;
+
+/* Problem description shared by every call. */
+typedef struct {
+  int32_t B, H, T;   /* batch, heads, sequence length (T ignored by decode)          */
+  int32_t dk, dv;    /* key/query and value head sizes                               */
+  int32_t chunk;     /* GLA chunk length; must be 64                                 */
+  int32_t window;    /* w: keys t-w+1 .. t are visible to query t (w >= 1)            */
+  int32_t n_meta;    /* M: always-visible meta-memory slots (0..16)                   */
+  float scale;       /* softmax logit scale; <= 0 selects 1/sqrt(dk)                 */
+  float mix;         /* weight of the window branch in the combine                   */
+  int32_t dtype;     /* lizard_dtype_t of q, k, v, o, meta, ring, dq, dk, dv          */
+} lizard_desc_t;
+
+/* Bytes of scratch memory `op` needs for `desc` (0 if none).  Never fails: an
+ * invalid desc yields 0, and the call itself then reports the problem. */
+size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op);
+
+/* Chunked gated linear attention forward (GLA branch alone).
+ *   o_t = q_t S_t with S_t = diag(exp(log_alpha_t)) S_{t-1} + k_t^T v_t, S_{-1} = h0.
+ * h0 (nullable, NULL = zeros) is read; o is written; hT (nullable) receives S_{T-1}
+ * (h0, or zeros, when T == 0).  ws may be NULL when lizard_workspace_bytes is 0. */
+lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                               const void* v, const float* log_alpha, const float* h0,
+                               void* o, float* hT, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* Sliding-window + meta-memory softmax attention forward (window branch alone).
+ * o receives o_swa (no mix applied); lse (nullable) receives the log-sum-exp of
+ * each query's logits. */
+lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                               const void* v, const void* meta_k, const void* meta_v,
+                               void* o, float* lse, hipStream_t stream);
+
+/* Hybrid forward: o = o_gla + mix * o_swa.  Optional outputs (each nullable):
+ * lse and o_swa (needed by lizard_hybrid_bwd), hT = final GLA state, and the
+ * window cache ring_k/ring_v for a prefill -> decode handoff (slot p mod w holds
+ * token p for the last min(T, w) tokens; slots no token reached are zeroed). */
+lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* meta_v, const float* h0, void* o, float* lse,
+                                  void* o_swa, float* hT, void* ring_k, void* ring_v,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Hybrid backward for the loss sum(dO * o).  Reads the forward inputs plus the
+ * o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv (desc->dtype),
+ * dlog_alpha [B,H,T,dk], dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all float32 except
+ * dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as in the forward.
+ * ws must hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_BWD) bytes. */
+lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* meta_v, const float* h0, const void* o_swa,
+                                  const float* lse, const void* dO, void* dq, void* dk,
+                                  void* dv, float* dlog_alpha, float* dmeta_k, float* dmeta_v,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One constant-memory generation step for B sequences (desc->T is ignored).
+ * q, k [B,H,dk], v [B,H,dv] in desc->dtype; log_alpha [B,H,dk] float32.
+ * pos [B] int64 (device): tokens already seen by each sequence.  The call
+ * updates state in place, writes (k, v) to ring slot pos mod w, attends over the
+ * min(pos+1, w) filled slots plus the M meta slots, writes o [B,H,dv] and then
+ * increments every pos[b] by one. */
+lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
+                                   const void* v, const float* log_alpha, float* state,
+                                   void* ring_k, void* ring_v, int64_t* pos,
+                                   const void* meta_k, const void* meta_v, void* o,
+                                   hipStream_t stream);
+
+/* Static description of a status code. */
+const char* lizard_status_str(lizard_status_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t lizard_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIZARD_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library validates every argument before it touches HIP, so these run on a
+machine without a GPU: the shared library loads, exports every function that
+include/lizard.h declares, and maps each kind of bad argument to its status.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from gated_linear_attention_chunked_amd import _abi
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_abi.LIB_PATH),
+                                reason="liblizard.so not built")
+
+NULLP = None
+
+
+def desc(**kw):
+    base = dict(B=1, H=2, T=128, dk=64, dv=64, chunk=64, window=64, n_meta=4, scale=0.0, mix=1.0,
+                dtype=_abi.LIZARD_BF16)
+    base.update(kw)
+    return _abi.Desc(base["B"], base["H"], base["T"], base["dk"], base["dv"], base["chunk"],
+                     base["window"], base["n_meta"], base["scale"], base["mix"], base["dtype"])
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+def gla(d, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, h0=None, o=FAKE, hT=None)
+    p.update(ptrs)
+    return _abi.lib().lizard_gla_fwd(ctypes.byref(d) if d is not None else None, p["q"], p["k"],
+                                     p["v"], p["la"], p["h0"], p["o"], p["hT"], None, 0, None)
+
+
+def test_exports_every_declared_symbol():
+    declared = _abi.header_symbols()
+    assert set(declared) >= {"lizard_gla_fwd", "lizard_swa_fwd", "lizard_hybrid_fwd",
+                             "lizard_hybrid_bwd", "lizard_decode_step", "lizard_status_str",
+                             "lizard_workspace_bytes", "lizard_version"}
+    lib = _abi.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared) <= exported
+
+
+def test_status_strings_and_version():
+    lib = _abi.lib()
+    for code in range(7):
+        assert lib.lizard_status_str(code)
+    assert lib.lizard_status_str(99) == b"unknown status"
+    assert lib.lizard_version() == 10000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 3),
+    (dict(B=-1), 2), (dict(T=-5), 2), (dict(dk=0), 2), (dict(window=0), 2), (dict(n_meta=-1), 2),
+    (dict(chunk=0), 2), (dict(scale=float("nan")), 2), (dict(mix=float("inf")), 2),
+    (dict(chunk=32), 4), (dict(dk=96, dv=96), 4), (dict(dk=64, dv=128), 4),
+    (dict(dk=128, dv=128, dtype=_abi.LIZARD_F32), 4), (dict(n_meta=17), 4),
+    (dict(B=300, H=300), 4),
+])
+def test_bad_descriptor_is_rejected_before_launch(kw, status):
+    assert gla(desc(**kw)) == status
+
+
+def test_null_pointers():
+    assert gla(None) == 1
+    assert gla(desc(), q=None) == 1
+    assert gla(desc(), la=None) == 1
+    lib = _abi.lib()
+    d = desc()
+    # meta slots requested but no meta pointers
+    assert lib.lizard_swa_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 1
+    # one ring pointer without the other
+    assert lib.lizard_hybrid_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                 None, None, None, FAKE, None, None, 0, None) == 1
+    assert lib.lizard_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, None) == 1
+
+
+def test_empty_problems_enqueue_nothing():
+    # B*H == 0: valid, nothing to do, no HIP call
+    assert gla(desc(B=0), q=None, k=None, v=None, la=None, o=None) == 0
+    lib = _abi.lib()
+    d = desc(H=0)
+    assert lib.lizard_swa_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
+
+
+def test_workspace_query():
+    lib = _abi.lib()
+    for op in (0, 1, 2, 4):
+        assert lib.lizard_workspace_bytes(ctypes.byref(desc()), op) == 0
+    assert lib.lizard_workspace_bytes(None, 3) == 0
+    assert lib.lizard_workspace_bytes(ctypes.byref(desc(dtype=9)), 3) == 0
+    a = lib.lizard_workspace_bytes(ctypes.byref(desc(T=1024)), 3)
+    b = lib.lizard_workspace_bytes(ctypes.byref(desc(T=4096)), 3)
+    assert a >= 0 and b >= a
+
+
+def test_backward_rejects_small_workspace():
+    lib = _abi.lib()
+    d = desc(T=256)
+    need = lib.lizard_workspace_bytes(ctypes.byref(d), 3)
+    if need == 0:
+        pytest.skip("backward needs no workspace for this shape")
+    st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 16), FAKE, need - 1, None)
+    assert st == 5
