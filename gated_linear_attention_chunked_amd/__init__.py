@@ -84,9 +84,11 @@ def gla_fwd(q, k, v, log_alpha, h0=None, return_state=False):
     o = torch.empty_like(v)
     hT = torch.empty(B, H, dk, dv, device=q.device, dtype=torch.float32) if return_state else None
     d = make_desc(B, H, T, dk, dv, dtype=dt)
+    nws = workspace_bytes(d, _abi.OP_GLA_FWD)
+    ws = torch.empty(nws, device=q.device, dtype=torch.uint8) if nws else None
     _abi.check("lizard_gla_fwd", lib().lizard_gla_fwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(h0), _p(o), _p(hT),
-        None, 0, _stream()))
+        _p(ws), nws, _stream()))
     return (o, hT) if return_state else o
 
 
@@ -131,10 +133,12 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
         out["ring_k"] = torch.empty(B, H, window, dk, device=dev, dtype=dt)
         out["ring_v"] = torch.empty(B, H, window, dv, device=dev, dtype=dt)
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
+    nws = workspace_bytes(d, _abi.OP_HYBRID_FWD)
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8) if nws else None
     _abi.check("lizard_hybrid_fwd", lib().lizard_hybrid_fwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
-        _p(out.get("ring_k")), _p(out.get("ring_v")), None, 0, _stream()))
+        _p(out.get("ring_k")), _p(out.get("ring_v")), _p(ws), nws, _stream()))
     return out
 
 

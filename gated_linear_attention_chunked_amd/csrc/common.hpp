@@ -101,6 +101,70 @@ template <> __device__ __forceinline__ f32x4 ld4f<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+// Work-group barrier that waits only for this wave's LDS traffic.  The plain
+// __syncthreads() also drains outstanding global loads, which would stall the
+// next-chunk prefetch at every barrier.  Global data is never exchanged
+// through these barriers, only LDS.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Raw buffer view of one tensor slice.  Reads at byte offsets >= `bytes` return
+// zero, so ragged tails need neither clamping nor branches, and constant row
+// offsets fold into the instruction's immediate field.
+typedef unsigned int u32;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+struct U2 {
+  u32 a, b;
+};
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void* base, u32 bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                            0x00020000)) {}
+  __device__ __forceinline__ u32 ld32(u32 off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  // 8 bytes as two scalars.  Building a two-element vector from buffer-load
+  // results and then taking its elements apart compiles (hipcc for gfx950) to a
+  // single dword load copied into both elements, so pairs stay plain structs.
+  __device__ __forceinline__ U2 ld64(u32 off) const {
+    return U2{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0),
+              __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0)};
+  }
+  // 16 bytes; only ever stored whole (to LDS), never split into elements.
+  __device__ __forceinline__ u32x4 ld128(u32 off) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+};
+// Two consecutive elements as fp32.
+__device__ __forceinline__ f32x2 unpack2(u32 x, bf16) {
+  return f32x2{__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x2 unpack2(U2 x, float) {
+  return f32x2{__builtin_bit_cast(float, x.a), __builtin_bit_cast(float, x.b)};
+}
+template <typename T> struct Pair;                  // raw storage of two elements
+template <> struct Pair<bf16> { typedef u32 type; };
+template <> struct Pair<float> { typedef U2 type; };
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type ld_pair(const Buf& b, u32 off);
+template <> __device__ __forceinline__ u32 ld_pair<bf16>(const Buf& b, u32 off) { return b.ld32(off); }
+template <> __device__ __forceinline__ U2 ld_pair<float>(const Buf& b, u32 off) { return b.ld64(off); }
+
+// Two fp32 values as a packed pair of T (one LDS store).
+template <typename T> __device__ __forceinline__ void st_pair(T* p, float a, float b);
+template <> __device__ __forceinline__ void st_pair<bf16>(bf16* p, float a, float b) {
+  *reinterpret_cast<bf16x2*>(p) = bf16x2{(bf16)a, (bf16)b};
+}
+template <> __device__ __forceinline__ void st_pair<float>(float* p, float a, float b) {
+  *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
+}
+
+__device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 __device__ __forceinline__ float wave_max16(float x) {  // over lanes with equal (lane & 15)
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));

@@ -14,10 +14,13 @@ struct Shape {
   int dtype;    // 0 = f32, 1 = bf16
 };
 
-// GLA branch.  accumulate != 0: o += result instead of o = result.
+// GLA branch: o = o_gla; hT (optional) = final state.  ws holds
+// gla_fwd_workspace_bytes(s) bytes (segment states; independent of T once
+// T >= 16 chunks).
+size_t gla_fwd_workspace_bytes(const Shape& s);
 hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                          const float* la, const float* h0, void* o, float* hT,
-                          int accumulate, hipStream_t st);
+                          const float* la, const float* h0, void* o, float* hT, void* ws,
+                          hipStream_t st);
 
 // Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
 // accumulate != 0); o_swa and lse are optional extra outputs.

@@ -26,7 +26,8 @@ lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
   if (d->n_meta > 16) return LIZARD_E_UNSUPPORTED;
   const long long bh = (long long)d->B * d->H;
   if (bh > 65535) return LIZARD_E_UNSUPPORTED;  // work-group grid limit of the prefill kernels
-  if (need_T && bh * (long long)d->T * d->dk > (1LL << 40)) return LIZARD_E_UNSUPPORTED;
+  // per-head slices are addressed with 32-bit byte offsets
+  if (need_T && (long long)d->T * d->dk * 4 >= (1LL << 31)) return LIZARD_E_UNSUPPORTED;
   return LIZARD_OK;
 }
 
@@ -69,21 +70,25 @@ const char* lizard_status_str(lizard_status_t s) {
 int32_t lizard_version(void) { return kVersion; }
 
 size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op) {
-  if (op != LIZARD_OP_HYBRID_BWD) return 0;
+  if (op == LIZARD_OP_SWA_FWD || op == LIZARD_OP_DECODE) return 0;
   if (check_desc(desc, true) != LIZARD_OK) return 0;
-  return lz::bwd_workspace_bytes(to_shape(desc));
+  if (op == LIZARD_OP_GLA_FWD || op == LIZARD_OP_HYBRID_FWD)
+    return lz::gla_fwd_workspace_bytes(to_shape(desc));
+  if (op == LIZARD_OP_HYBRID_BWD) return lz::bwd_workspace_bytes(to_shape(desc));
+  return 0;
 }
 
 lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                const void* v, const float* log_alpha, const float* h0, void* o,
                                float* hT, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
   if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  const size_t need = lz::gla_fwd_workspace_bytes(to_shape(desc));
+  if (ws_bytes < need) return LIZARD_E_WORKSPACE;
+  if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
-  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, log_alpha, h0, o, hT, 0, stream));
+  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, log_alpha, h0, o, hT, ws, stream));
 }
 
 lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
@@ -103,20 +108,22 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* meta_v, const float* h0, void* o, float* lse,
                                   void* o_swa, float* hT, void* ring_k, void* ring_v, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
   if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
   if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
-  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   const Shape s = to_shape(desc);
+  const size_t need = lz::gla_fwd_workspace_bytes(s);
+  if (ws_bytes < need) return LIZARD_E_WORKSPACE;
+  if (need > 0 && !ws) return LIZARD_E_NULL;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   hipError_t e = hipSuccess;
   if (desc->T > 0) {
-    // window branch first: o = mix * o_swa; then the GLA branch adds o_gla in place
-    e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 0, o_swa, lse, stream);
-    if (e == hipSuccess) e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, 1, stream);
+    // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
+    e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, ws, stream);
+    if (e == hipSuccess)
+      e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, stream);
   } else if (hT) {
     e = lz::launch_state_copy(s, h0, hT, stream);
   }

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
   typedef typename Frag<T>::type F;
   __shared__ SwaSmem<T, DK, DV> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int bh = blockIdx.y, h = bh % H;
   const int t0 = blockIdx.x * kQT;
@@ -49,53 +49,54 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
   const int tq = tq0 + r16;           // this lane's query (column of the logit tiles)
   const size_t qk_base = (size_t)bh * T_len * DK;
   const size_t v_base = (size_t)bh * T_len * DV;
+  const Buf bk(k + qk_base, (u32)((size_t)T_len * DK * sizeof(T)));
+  const Buf bv(v + v_base, (u32)((size_t)T_len * DV * sizeof(T)));
 
   // q fragments (B operand, contiguous channel map)
+  // (rows past the end load the last row; their outputs are never stored)
   F qf[KS];
+  const int tq_ld = min(tq, T_len - 1);
 #pragma unroll
-  for (int p = 0; p < KS; ++p) {
-    if (tq < T_len) qf[p] = ld8<T>(q + qk_base + (size_t)tq * DK + 32 * p + 8 * g);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[p][e] = to_t<T>(0.f);
-  }
+  for (int p = 0; p < KS; ++p) qf[p] = ld8<T>(q + qk_base + (size_t)tq_ld * DK + 32 * p + 8 * g);
 
   f32x4 O[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig, l_run = 0.f;
 
-  // loader for a [rows x D] row-major tile into LDS, zero outside [0, nrows)
-  auto stage_rows = [&](T* dst, int ld_dst, const T* src, int nrows, int D, int rows) {
+  // Tile loaders.  Rows past the end of the buffer read as zero (buffer bounds),
+  // so there are no branches around the loads.
+  // row-major [rows x D] tile from rows row0.. of `src` into dst (leading dim ld_dst)
+  auto stage_rows = [&](T* dst, int ld_dst, const Buf& src, int row0, int D, int rows) {
     const int per_row = D / 8;
     for (int e = tid; e < rows * per_row; e += 256) {
       const int r = e / per_row, c8 = (e % per_row) * 8;
-      F val;
-      if (r < nrows) val = ld8<T>(src + (size_t)r * D + c8);
-      else
-#pragma unroll
-        for (int x = 0; x < 8; ++x) val[x] = to_t<T>(0.f);
-      *reinterpret_cast<F*>(dst + r * ld_dst + c8) = val;
+      const u32 off = (u32)(((row0 + r) * D + c8) * sizeof(T));
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<u32x4*>(dst + r * ld_dst + c8) = src.ld128(off);
+      } else {
+        *reinterpret_cast<u32x4*>(dst + r * ld_dst + c8) = src.ld128(off);
+        *reinterpret_cast<u32x4*>(dst + r * ld_dst + c8 + 4) = src.ld128(off + 16);
+      }
     }
   };
-  // transposed loader: dst[c][r] = src[r][c]; rows >= nrows are zero
-  auto stage_cols = [&](T* dst, int ld_dst, const T* src, int nrows, int D, int rows) {
+  // transposed: dst[c][r] = src[row0 + r][c]
+  auto stage_cols = [&](T* dst, int ld_dst, const Buf& src, int row0, int D, int rows) {
     for (int e = tid; e < (rows / 8) * (D / 2); e += 256) {
       const int cp = e % (D / 2), rg = e / (D / 2);
-      T c0v[8], c1v[8];
+      float c0v[8], c1v[8];
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        const int r = 8 * rg + rr;
-        if (r < nrows) {
-          c0v[rr] = src[(size_t)r * D + 2 * cp];
-          c1v[rr] = src[(size_t)r * D + 2 * cp + 1];
-        } else {
-          c0v[rr] = to_t<T>(0.f);
-          c1v[rr] = to_t<T>(0.f);
-        }
+        const u32 off = (u32)(((row0 + 8 * rg + rr) * D + 2 * cp) * sizeof(T));
+        const f32x2 x = unpack2(ld_pair<T>(src, off), T());
+        c0v[rr] = x[0];
+        c1v[rr] = x[1];
       }
-      *reinterpret_cast<F*>(dst + (2 * cp) * ld_dst + 8 * rg) = *reinterpret_cast<F*>(&c0v[0]);
-      *reinterpret_cast<F*>(dst + (2 * cp + 1) * ld_dst + 8 * rg) = *reinterpret_cast<F*>(&c1v[0]);
+      typename Frag<T>::type f0, f1;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) { f0[rr] = to_t<T>(c0v[rr]); f1[rr] = to_t<T>(c1v[rr]); }
+      *reinterpret_cast<typename Frag<T>::type*>(dst + (2 * cp) * ld_dst + 8 * rg) = f0;
+      *reinterpret_cast<typename Frag<T>::type*>(dst + (2 * cp + 1) * ld_dst + 8 * rg) = f1;
     }
   };
 
@@ -143,8 +144,10 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
 
   // ---- meta slots (always visible)
   if (M > 0) {
-    stage_rows(&sm.mk[0][0], SwaSmem<T, DK, DV>::DKP, mk + (size_t)h * M * DK, M, DK, 16);
-    stage_cols(&sm.mvT[0][0], 32 + 8, mv + (size_t)h * M * DV, M, DV, 32);
+    const Buf bmk(mk + (size_t)h * M * DK, (u32)(M * DK * sizeof(T)));
+    const Buf bmv(mv + (size_t)h * M * DV, (u32)(M * DV * sizeof(T)));
+    stage_rows(&sm.mk[0][0], SwaSmem<T, DK, DV>::DKP, bmk, 0, DK, 16);
+    stage_cols(&sm.mvT[0][0], 32 + 8, bmv, 0, DV, 32);
     __syncthreads();
     f32x4 P[4];
     bool act[4] = {true, false, false, false};
@@ -165,9 +168,8 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
   const int last_key = min(T_len - 1, t0 + kQT - 1);
   for (int kt0 = (first_key / kKT) * kKT; kt0 <= last_key; kt0 += kKT) {
     __syncthreads();  // previous tile's readers are done
-    const int nrows = min(kKT, T_len - kt0);
-    stage_rows(&sm.kt[0][0], SwaSmem<T, DK, DV>::DKP, k + qk_base + (size_t)kt0 * DK, nrows, DK, kKT);
-    stage_cols(&sm.vT[0][0], kKT + 8, v + v_base + (size_t)kt0 * DV, nrows, DV, kKT);
+    stage_rows(&sm.kt[0][0], SwaSmem<T, DK, DV>::DKP, bk, kt0, DK, kKT);
+    stage_cols(&sm.vT[0][0], kKT + 8, bv, kt0, DV, kKT);
     __syncthreads();
 
     f32x4 P[4];

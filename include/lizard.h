@@ -41,8 +41,8 @@
  *     check returns a non-zero status and enqueues nothing.  A launch failure
  *     returns LIZARD_E_HIP.  NaN/Inf inputs propagate to the outputs.
  *   - Supported in this version: dk == dv, dk in {64, 128}, chunk == 64,
- *     window >= 1, 0 <= M <= 16, T >= 0; dtype BF16 for dk in {64, 128},
- *     F32 for dk == 64.  Output gradients dq, dk, dv use desc->dtype; every
+ *     window >= 1, 0 <= M <= 16, T >= 0 with T*dk*4 < 2^31, B*H <= 65535;
+ *     dtype BF16 for dk in {64, 128}, F32 for dk == 64.  Output gradients dq, dk, dv use desc->dtype; every
  *     other output is float32.
  */
 #ifndef LIZARD_H
@@ -89,13 +89,17 @@ typedef struct {
 } lizard_desc_t;
 
 /* Bytes of scratch memory `op` needs for `desc` (0 if none).  Never fails: an
- * invalid desc yields 0, and the call itself then reports the problem. */
+ * invalid desc yields 0, and the call itself then reports the problem.
+ * LIZARD_OP_GLA_FWD / LIZARD_OP_HYBRID_FWD: per-segment GLA states, at most
+ * 15 * B*H * (dk*dv + dk) * 4 bytes and independent of T once T >= 1024.
+ * The workspace holds no state between calls. */
 size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op);
 
 /* Chunked gated linear attention forward (GLA branch alone).
  *   o_t = q_t S_t with S_t = diag(exp(log_alpha_t)) S_{t-1} + k_t^T v_t, S_{-1} = h0.
  * h0 (nullable, NULL = zeros) is read; o is written; hT (nullable) receives S_{T-1}
- * (h0, or zeros, when T == 0).  ws may be NULL when lizard_workspace_bytes is 0. */
+ * (h0, or zeros, when T == 0).  ws must hold lizard_workspace_bytes(desc,
+ * LIZARD_OP_GLA_FWD) bytes (it may be NULL when that is 0). */
 lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                const void* v, const float* log_alpha, const float* h0,
                                void* o, float* hT, void* ws, size_t ws_bytes,
@@ -111,7 +115,8 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
 /* Hybrid forward: o = o_gla + mix * o_swa.  Optional outputs (each nullable):
  * lse and o_swa (needed by lizard_hybrid_bwd), hT = final GLA state, and the
  * window cache ring_k/ring_v for a prefill -> decode handoff (slot p mod w holds
- * token p for the last min(T, w) tokens; slots no token reached are zeroed). */
+ * token p for the last min(T, w) tokens; slots no token reached are zeroed).
+ * ws must hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) bytes. */
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,

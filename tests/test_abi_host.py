@@ -95,13 +95,28 @@ def test_empty_problems_enqueue_nothing():
 
 def test_workspace_query():
     lib = _abi.lib()
-    for op in (0, 1, 2, 4):
+    for op in (1, 4):
         assert lib.lizard_workspace_bytes(ctypes.byref(desc()), op) == 0
+    # forward: per-segment states, bounded and independent of T for long sequences
+    f1 = lib.lizard_workspace_bytes(ctypes.byref(desc(B=1, H=32, T=4096, dk=128, dv=128)), 0)
+    f2 = lib.lizard_workspace_bytes(ctypes.byref(desc(B=1, H=32, T=32768, dk=128, dv=128)), 2)
+    assert f1 == f2 == 32 * 7 * (128 * 128 + 128) * 4
+    assert lib.lizard_workspace_bytes(ctypes.byref(desc(B=64, H=32, T=4096)), 0) == 0
     assert lib.lizard_workspace_bytes(None, 3) == 0
     assert lib.lizard_workspace_bytes(ctypes.byref(desc(dtype=9)), 3) == 0
     a = lib.lizard_workspace_bytes(ctypes.byref(desc(T=1024)), 3)
     b = lib.lizard_workspace_bytes(ctypes.byref(desc(T=4096)), 3)
     assert a >= 0 and b >= a
+
+
+def test_forward_rejects_small_workspace():
+    lib = _abi.lib()
+    d = desc(T=4096)
+    need = lib.lizard_workspace_bytes(ctypes.byref(d), 0)
+    assert need > 0
+    assert gla(d) == 5  # no workspace passed
+    st = lib.lizard_hybrid_fwd(ctypes.byref(d), *([FAKE] * 13), FAKE, need - 1, None)
+    assert st == 5
 
 
 def test_backward_rejects_small_workspace():

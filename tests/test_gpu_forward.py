@@ -105,6 +105,8 @@ def test_outputs_fully_written_and_deterministic():
     B, H, T, d, w, M = 2, 3, 333, 128, 128, 4
     inp = to_dev(make_inputs(B, H, T, d, d, M, dtype="bf16", seed=5))
     dsc = lz.make_desc(B, H, T, d, d, w, M, None, 1.0, torch.bfloat16)
+    nws = lz.workspace_bytes(dsc, _abi.OP_HYBRID_FWD)
+    ws = torch.full((max(nws, 1),), 255, device="cuda", dtype=torch.uint8)  # NaN-filled floats
     outs = []
     for _ in range(2):
         o = torch.full((B, H, T, d), float("nan"), device="cuda", dtype=torch.bfloat16)
@@ -117,7 +119,7 @@ def test_outputs_fully_written_and_deterministic():
         st = lz.lib().lizard_hybrid_fwd(
             ctypes.byref(dsc), p(inp["q"]), p(inp["k"]), p(inp["v"]), p(inp["log_alpha"]),
             p(inp["meta_k"]), p(inp["meta_v"]), None, p(o), p(lse), p(osw), p(hT), p(rk), p(rv),
-            None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            p(ws), nws, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         assert st == 0
         torch.cuda.synchronize()
         for t in (o, lse, osw, hT, rk, rv):
