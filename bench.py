@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid attention hot path on one MI355X.
+
+A step is one hybrid prefill forward (GLA branch + window/meta branch + combine
++ state and window-cache handoff) over one batch of the bf16 workload
+B=2, H=32, T=4096, d=128, chunk 64, w=128, M=4, with inputs resident in HBM.
+Prints one JSON line with prefill tokens/s (value), the fraction of bf16 MFMA
+peak, the HBM roofline of the dominant kernel, the fp64 oracle timed on the host
+as a CPU baseline, and secondary lines for the decode workload (B=64, H=32,
+1024 steps after a 2048-token prefill) and the training workload (B=8, H=16,
+T=2048, d=64, forward + backward).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_flops(B, H, T, d, C, w, M):
+    """Causal-triangle and real-window work only (no padded tiles), FLOP = 2 MAC."""
+    nc = T // C
+    gla = nc * C * (C + 1) / 2 * (2 * d) + T * d * d * 2
+    win = sum(min(t + 1, w) for t in range(T)) + M * T
+    return 2.0 * B * H * (gla + win * 2 * d)
+
+
+def gla_bytes(B, H, T, d):
+    """GLA branch: q, k, v (bf16) and log_alpha (fp32) read once, o written once,
+    final state written once."""
+    return B * H * (T * (3 * d * 2 + d * 4 + d * 2) + d * d * 4)
+
+
+def decode_bytes_per_step(B, H, d, w, M, pos):
+    """Per step and (b,h): fp32 state read+write, the min(pos+1,w)-1 older ring
+    slots read (K and V), the new K,V written, q,k,v,log_alpha read, o written."""
+    n_old = min(pos + 1, w) - 1
+    per = 2 * d * d * 4 + n_old * d * 2 * 2 + 2 * d * 2 + 3 * d * 2 + d * 4 + d * 2
+    return B * H * per + H * M * d * 2 * 2
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, digest):
+    """HBM bytes per call measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled by
+    a copy-kernel calibration), as recorded in profiles/*.md; None when no record
+    matches the current kernel source."""
+    if not os.path.isdir(PROFILES):
+        return None
+    for fn in sorted(os.listdir(PROFILES)):
+        if not fn.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, fn)) as f:
+            for line in f:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("workload") == workload and rec.get("source_digest") == digest:
+                        return rec.get("bytes_per_launch")
+    return None
+
+
+def event_time_ms(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def cpu_baseline(wl, seconds):
+    """The fp64 oracle as it stands, on one host core, on whole heads of the same
+    workload until about `seconds` of CPU work; reported in tokens/s."""
+    import numpy as np
+    import oracle
+    from workloads import make_inputs, to_f64_numpy
+    from threadpoolctl import threadpool_limits
+    inp = make_inputs(1, 1, wl["T"], wl["dk"], wl["dv"], wl["n_meta"], dtype=wl["dtype"], seed=0)
+    x = {n: to_f64_numpy(t) for n, t in inp.items()}
+    heads, tokens = 0, 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.hybrid_forward(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"],
+                                  x["meta_v"], wl["window"], wl["scale"], mix=wl["mix"])
+            heads += 1
+            tokens += wl["T"]
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    # one head of T tokens is 1/H of a batch element's work: tokens/s of the
+    # whole layer = head-tokens/s / H
+    return {"value": tokens / dt / wl["H"], "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} head(s) x T={wl['T']} of the same workload "
+                      f"(one head of one sequence per pass), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode and training lines")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        a = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on a single GPU; multi-GPU runs are not supported "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_linear_attention_chunked_amd as lz
+    from gated_linear_attention_chunked_amd import _abi
+    from workloads import WORKLOADS, make_inputs
+
+    name = "prefill_bf16_b2_h32_t4096_d128"
+    wl = WORKLOADS[name]
+    B, H, T, d, w, M, C = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta, wl.chunk
+    dev = torch.device("cuda:0")
+    inp = make_inputs(B, H, T, d, d, M, dtype=wl.dtype, seed=0)
+    x = {n: t.to(dev) for n, t in inp.items()}
+    o = torch.empty_like(x["v"])
+    hT = torch.empty(B, H, d, d, device=dev)
+    rk = torch.empty(B, H, w, d, device=dev, dtype=torch.bfloat16)
+    rv = torch.empty_like(rk)
+    desc = lz.make_desc(B, H, T, d, d, w, M, wl.scale, wl.mix, torch.bfloat16)
+    nws = lz.workspace_bytes(desc, _abi.OP_HYBRID_FWD)
+    ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    lib = lz.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    dref = ctypes.byref(desc)
+    hyb_args = (dref, P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["meta_k"]),
+                P(x["meta_v"]), None, P(o), None, None, P(hT), P(rk), P(rv), P(ws), nws, stream)
+
+    def step():
+        st = lib.lizard_hybrid_fwd(*hyb_args)
+        if st != 0:
+            raise RuntimeError(f"lizard_hybrid_fwd: status {st}")
+
+    # ---- timed region: exactly K steps between two synchronisations
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = B * T / (ms / 1e3)
+    flops = algorithmic_flops(B, H, T, d, C, w, M)
+
+    # ---- dominant part: the GLA branch, timed alone on the same stream
+    gws_n = lz.workspace_bytes(desc, _abi.OP_GLA_FWD)
+    gla_args = (dref, P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), None, P(o), P(hT),
+                P(ws), gws_n, stream)
+    gla_ms = event_time_ms(lambda: lib.lizard_gla_fwd(*gla_args), args.steps, args.warmup)
+    swa_ms = event_time_ms(lambda: lib.lizard_swa_fwd(dref, P(x["q"]), P(x["k"]), P(x["v"]),
+                                                      P(x["meta_k"]), P(x["meta_v"]), P(o), None,
+                                                      stream), args.steps, args.warmup)
+    gbytes = gla_bytes(B, H, T, d)
+    achieved = gbytes / (gla_ms / 1e3) / 1e9
+    traffic = counter_traffic(name, source_digest("gla_fwd.hip"))
+
+    out = {
+        "metric": "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "T": T, "dk": d, "dv": d, "chunk": C,
+                   "window": w, "n_meta": M, "parallelism": "single GPU"},
+        "mfma": {"algorithmic_tflop_per_step": flops / 1e12,
+                 "achieved_tflops": flops / (ms / 1e3) / 1e12,
+                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "roofline": {"kernel": "GLA branch (lizard_gla_fwd: state, carry and output passes)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_ms": gla_ms, "algorithmic_bytes": gbytes},
+        "breakdown_ms": {"gla_branch": gla_ms, "window_branch": swa_ms},
+    }
+
+    if not args.no_extras:
+        out["decode"] = bench_decode(lz, torch, dev)
+        try:
+            out["train"] = bench_train(lz, torch, dev, args)
+        except lz.LizardError as e:
+            out["train"] = {"error": str(e)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(lz, torch, dev):
+    """1024 decode steps (B=64, H=32, d=128, w=128, M=4) after a 2048-token hybrid
+    prefill; inputs drawn on the device with a seeded generator (same recipe)."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS["decode_bf16_b64_h32_d128"]
+    B, H, T, d, w, M, steps = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta, wl.steps
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape, mean=0.0, scale=1.0, dt=torch.bfloat16):
+        return (torch.randn(*shape, device=dev, generator=g) * scale + mean).to(dt)
+
+    s = 1.0 / math.sqrt(d)
+    q, k, v = (rnd(B, H, T, d, scale=s) for _ in range(3))
+    la = torch.nn.functional.logsigmoid(rnd(B, H, T, d, mean=2.0, dt=torch.float32))
+    mk, mv = rnd(H, M, d), rnd(H, M, d)
+    pre = lz.hybrid_fwd(q, k, v, la, mk, mv, w, return_state=True, return_ring=True)
+    del q, k, v, la
+    dq, dk_, dv_ = (rnd(steps, B, H, d, scale=s) for _ in range(3))
+    dla = torch.nn.functional.logsigmoid(rnd(steps, B, H, d, mean=2.0, dt=torch.float32))
+    state, rk, rv = pre["hT"], pre["ring_k"], pre["ring_v"]
+    pos = torch.full((B,), T, dtype=torch.int64, device=dev)
+    o = torch.empty(B, H, d, device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        lz.decode_step(dq[i], dk_[i], dv_[i], dla[i], state, rk, rv, pos, mk, mv, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    nbytes = sum(decode_bytes_per_step(B, H, d, w, M, T + i) for i in range(steps))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "decode_bf16_b64_h32_d128", "steps": steps, "ms_total": ms,
+            "us_per_step": ms * 1e3 / steps, "tokens_per_s": B * steps / (ms / 1e3),
+            "algorithmic_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "note": "working set (state 128 MiB + ring 128 MiB) is about the MALL size; "
+                    "see profiles/ for counter-measured DRAM bytes"}
+
+
+def bench_train(lz, torch, dev, args):
+    """Forward (saving lse and o_swa) + backward of B=8, H=16, T=2048, d=64, w=64, M=4."""
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["train_bf16_b8_h16_t2048_d64"]
+    B, H, T, d, w, M = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta
+    x = {n: t.to(dev) for n, t in make_inputs(B, H, T, d, d, M, dtype=wl.dtype, seed=0,
+                                              with_grad_out=True).items()}
+
+    def step():
+        f = lz.hybrid_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], w,
+                          save_for_backward=True)
+        lz.hybrid_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], w,
+                      f["o_swa"], f["lse"], x["dO"])
+
+    ms = event_time_ms(step, max(3, args.steps // 2), 2)
+    return {"workload": "train_bf16_b8_h16_t2048_d64", "ms_per_step": ms,
+            "tokens_per_s": B * T / (ms / 1e3)}
+
+
+if __name__ == "__main__":
+    main()
