@@ -165,6 +165,40 @@ __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) 
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// Row-major [rows x D] tile, rows row0.. of `src`, into dst (leading dim ld).
+// Out-of-range rows read as zero through the buffer bounds.
+template <typename T>
+__device__ __forceinline__ void stage_rows(T* dst, int ld, const Buf& src, int row0, int D,
+                                           int rows, int tid, int nthr) {
+  const int per_row = D / 8;
+  for (int e = tid; e < rows * per_row; e += nthr) {
+    const int r = e / per_row, c8 = (e % per_row) * 8;
+    const u32 off = (u32)(((row0 + r) * D + c8) * sizeof(T));
+    *reinterpret_cast<u32x4*>(dst + r * ld + c8) = src.ld128(off);
+    if constexpr (sizeof(T) == 4)
+      *reinterpret_cast<u32x4*>(dst + r * ld + c8 + 4) = src.ld128(off + 16);
+  }
+}
+
+// Transposed tile: dst[c][r] = src[row0 + r][c] for r < rows (rows % 8 == 0).
+template <typename T>
+__device__ __forceinline__ void stage_cols(T* dst, int ld, const Buf& src, int row0, int D,
+                                           int rows, int tid, int nthr) {
+  for (int e = tid; e < (rows / 8) * (D / 2); e += nthr) {
+    const int cp = e % (D / 2), rg = e / (D / 2);
+    typename Frag<T>::type f0, f1;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const u32 off = (u32)(((row0 + 8 * rg + rr) * D + 2 * cp) * sizeof(T));
+      const f32x2 x = unpack2(ld_pair<T>(src, off), T());
+      f0[rr] = to_t<T>(x[0]);
+      f1[rr] = to_t<T>(x[1]);
+    }
+    *reinterpret_cast<typename Frag<T>::type*>(dst + (2 * cp) * ld + 8 * rg) = f0;
+    *reinterpret_cast<typename Frag<T>::type*>(dst + (2 * cp + 1) * ld + 8 * rg) = f1;
+  }
+}
+
 __device__ __forceinline__ float wave_max16(float x) {  // over lanes with equal (lane & 15)
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));

@@ -28,9 +28,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
   constexpr int LPR = 16;          // lanes per key row in the logit pass
   constexpr int EPL = D / LPR;     // elements per lane in the logit pass
   extern __shared__ float logit[];  // W + M floats
-  __shared__ float sq[D], sk[D], sv[D], sa[D];
-  __shared__ f32x4 red[RG][CQ];
-  __shared__ float wred[8];
+  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[D], sa[D];
+  __shared__ __attribute__((aligned(16))) f32x4 red[RG][CQ];
+  __shared__ __attribute__((aligned(16))) float wred[8];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x, b = bh / H, h = bh % H;

@@ -39,7 +39,9 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* k, const voi
                          const float* la, float* state, void* ring_k, void* ring_v,
                          int64_t* pos, const void* mk, const void* mv, void* o, hipStream_t st);
 
-// Backward.  Workspace layout is owned by gla_bwd / swa_bwd.
+// Backward (bf16, dk = dv = 64 in this version).  Workspace layout is owned by
+// gla_bwd / swa_bwd; it grows with T (two states per chunk).
+bool bwd_supported(const Shape& s);
 size_t bwd_workspace_bytes(const Shape& s);
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
                              const float* la, const void* mk, const void* mv, const float* h0,

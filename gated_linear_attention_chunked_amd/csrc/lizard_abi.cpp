@@ -145,9 +145,11 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
     return LIZARD_E_NULL;
   if (meta && (!meta_k || !meta_v || !dmeta_k || !dmeta_v)) return LIZARD_E_NULL;
   const Shape s = to_shape(desc);
+  if (!lz::bwd_supported(s)) return LIZARD_E_UNSUPPORTED;
   const size_t need = lz::bwd_workspace_bytes(s);
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   return hip_status(lz::launch_hybrid_bwd(s, q, k, v, log_alpha, meta_k, meta_v, h0, o_swa, lse,
                                           dO, dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, ws, stream));
 }
