@@ -161,6 +161,17 @@ template <> __device__ __forceinline__ void st_pair<float>(float* p, float a, fl
   *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
 }
 
+// Work-groups are handed to the 8 XCDs round-robin by linear id.  This maps
+// linear id L to a logical index so that each XCD receives one contiguous run
+// of logical indices: neighbouring tiles (which share K/V rows) then run on the
+// same XCD and meet in its L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int L, int n) {
+  constexpr int kXcd = 8;
+  const int xcd = L % kXcd, idx = L / kXcd;
+  const int base = n / kXcd, rem = n % kXcd;
+  return xcd * base + min(xcd, rem) + idx;
+}
+
 __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

@@ -304,16 +304,19 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int c = 2 * cp + x;
-      float incl[8];  // inclusive prefix through row group r
-      float run = 0.f;
+      // prefix sums over row groups with selects only (run-time indices into a
+      // register array would put it in scratch memory)
+      const int pi = rg < 6 ? pair_i(rg) : 0, pj = rg < 6 ? pair_j(rg) : 0;
+      float pre = 0.f, blast = 0.f, Ri = 0.f, Rpi = 0.f, Rpj = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        run += sm.tot[r][c];
-        incl[r] = run;
+        const float tr = sm.tot[r][c];
+        blast += tr;
+        pre += (r < rg) ? tr : 0.f;
+        Ri += (r <= 2 * i_sub) ? tr : 0.f;  // b at row 16 i + 7
+        Rpi += (r <= 2 * pi) ? tr : 0.f;
+        Rpj += (r <= 2 * pj) ? tr : 0.f;
       }
-      const float pre = rg > 0 ? incl[rg - 1] : 0.f;
-      const float blast = incl[7];
-      const float Ri = incl[2 * i_sub];  // b at row 16 i + 7
       const float eRi = exp2_fast(Ri);
       const float eKh = exp2_fast(blast - Ri);
       float kh[8], vc[8];
@@ -331,8 +334,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
       store8<T>(&sm.khT[c][8 * rg], kh);
       store8<T>(&sm.vT[c][8 * rg], vc);
       if (rg < 6) {
-        const int pi = pair_i(rg), pj = pair_j(rg);
-        sm.vij[rg][c] = exp2_fast(incl[2 * pi] - incl[2 * pj]);
+        sm.vij[rg][c] = exp2_fast(Rpi - Rpj);
       } else if (rg == 7) {
         sm.decay[c] = exp2_fast(blast);
       }

@@ -47,8 +47,11 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
   __shared__ __attribute__((aligned(16))) float red[kD * 2][17];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.y, h = bh % H;
-  const int t0 = blockIdx.x * kT;
+  const int ntile = gridDim.x;
+  const int logical = xcd_remap(blockIdx.y * ntile + blockIdx.x, ntile * gridDim.y);
+  const int bh = logical / ntile, h = bh % H;
+  const int tile = logical % ntile;
+  const int t0 = tile * kT;
   const int tq = t0 + 16 * wave + r16;  // this lane's query (column of S^T tiles)
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
       __syncthreads();
     }
     // partial layout per (bh, tile): [M][kD] for meta_k then [M][kD] for meta_v
-    float* mp = metap + ((size_t)bh * gridDim.x + blockIdx.x) * (size_t)M * 2 * kD;
+    float* mp = metap + ((size_t)bh * ntile + tile) * (size_t)M * 2 * kD;
     for (int e = tid; e < M * 2 * kD; e += kThreads) {
       const int which = e / (M * kD), rem = e % (M * kD), i = rem / kD, cc = rem % kD;
       mp[e] = red[which * kD + cc][i];
@@ -229,8 +232,10 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
   __shared__ __attribute__((aligned(16))) float slse[kT], sD[kT];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.y;
-  const int s0 = blockIdx.x * kT;
+  const int ntile = gridDim.x;
+  const int logical = xcd_remap(blockIdx.y * ntile + blockIdx.x, ntile * gridDim.y);
+  const int bh = logical / ntile;
+  const int s0 = (logical % ntile) * kT;
   const int sk0 = s0 + 16 * wave;      // first key of this wave
   const int sk = sk0 + r16;            // this lane's key (column of the S tiles)
   const size_t off = (size_t)bh * T_len * kD;

@@ -43,8 +43,10 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int bh = blockIdx.y, h = bh % H;
-  const int t0 = blockIdx.x * kQT;
+  const int nqt = gridDim.x;
+  const int logical = xcd_remap(blockIdx.y * nqt + blockIdx.x, nqt * gridDim.y);
+  const int bh = logical / nqt, h = bh % H;
+  const int t0 = (logical % nqt) * kQT;
   const int tq0 = t0 + 16 * wave;     // first query of this wave
   const int tq = tq0 + r16;           // this lane's query (column of the logit tiles)
   const size_t qk_base = (size_t)bh * T_len * DK;
