@@ -125,18 +125,38 @@ struct Buf {
   __device__ __forceinline__ u32 ld32(u32 off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
-  // 8 bytes as two scalars.  Building a two-element vector from buffer-load
-  // results and then taking its elements apart compiles (hipcc for gfx950) to a
-  // single dword load copied into both elements, so pairs stay plain structs.
+  // 8 bytes as two scalars.
   __device__ __forceinline__ U2 ld64(u32 off) const {
     return U2{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0),
               __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0)};
   }
-  // 16 bytes; only ever stored whole (to LDS), never split into elements.
+  // 16 bytes.  Elements are read out through as_f() / bf_at(), never by
+  // __builtin_bit_cast on a vector element: hipcc for gfx950 lowers a bit_cast
+  // whose operand is an ext-vector element to element 0 of that vector.
   __device__ __forceinline__ u32x4 ld128(u32 off) const {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   }
 };
+// Bit patterns to fp32, from a scalar (see the note on Buf::ld128).
+__device__ __forceinline__ float as_f(u32 x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ float bf_lo(u32 x) { return as_f(x << 16); }
+__device__ __forceinline__ float bf_hi(u32 x) { return as_f(x & 0xffff0000u); }
+// bf16 element c (0..7) of a 16-byte word as fp32
+__device__ __forceinline__ float bf_at(const u32x4& v, int c) {
+  const u32 w = v[c >> 1];
+  return (c & 1) ? bf_hi(w) : bf_lo(w);
+}
+// fp32 element c (0..3)
+__device__ __forceinline__ float f_at(const u32x4& v, int c) {
+  const u32 w = v[c];
+  return as_f(w);
+}
+// two fp32 values rounded to a packed bf16 pair (a in the low half)
+__device__ __forceinline__ u32 pack_bf2(float a, float b) {
+  const bf16x2 p = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(u32, p);
+}
+
 // Two consecutive elements as fp32.
 __device__ __forceinline__ f32x2 unpack2(u32 x, bf16) {
   return f32x2{__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xffff0000u)};

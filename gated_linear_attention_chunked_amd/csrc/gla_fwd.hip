@@ -73,7 +73,7 @@ struct OutSmem {
   T a[kC][CP];       // masked intra scores A[t][s]
   float tot[8][DK];  // per-8-row-group sums of log2 gates
   float vij[6][DK];  // 2^{R_i - R_j} for the off-diagonal pairs
-  float decay[DK];   // 2^{b_last}
+  alignas(16) float decay[DK];  // 2^{b_last}
 };
 
 template <typename T, int DK>
@@ -244,6 +244,14 @@ __global__ __launch_bounds__(256) void gla_carry_pass(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ pass 3
+// A chunk whose per-channel decay 2^{b_last} stays above 2^-kFastLog2 in every
+// channel takes one reference for all its intra scores, the chunk start:
+// q_t 2^{b_t} (<= |q_t|) against k_s 2^{-b_s} (<= 2^kFastLog2 |k_s|), both far
+// inside the bf16/fp32 range.  Other chunks take the 16-token sub-block
+// references.  The choice is made per chunk from the same shared totals by
+// every wave, so it is uniform over the work-group.
+constexpr float kFastLog2 = 64.f;
+
 template <typename T, int DK>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -252,13 +260,15 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
   constexpr int NCB = DK / 16;
   constexpr int KS = DK / 32;
   constexpr int NW = DK / 16;
+  constexpr int NB = (10 + NW - 1) / NW;  // score blocks per wave, at most
   typedef typename Frag<T>::type F;
   __shared__ OutSmem<T, DK> sm;
+  constexpr int DKP = OutSmem<T, DK>::DKP;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int cp = tid % (DK / 2), rg = tid / (DK / 2);
-  const int i_sub = rg >> 1;  // 16-row sub-block of this thread's rows (uniform per wave)
+  const int i_sub = rg >> 1;  // 16-row sub-block of this thread's rows
   const int seg = blockIdx.x, bh = blockIdx.y;
   const size_t off = (size_t)bh * T_len * DK;
   const u32 nbytes = (u32)((size_t)T_len * DK * sizeof(T));
@@ -299,110 +309,184 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     sm.tot[rg][2 * cp + 1] = tot[1];
     lds_barrier();  // (A) group totals visible; previous chunk's LDS reads are done
 
-    // ---- gated operands for rows 8rg..8rg+7, channels 2cp, 2cp+1
-    float qgv[8][2], kgv[8][2], qhv[8][2];
+    // prefix sums over row groups with selects only (run-time indices into a
+    // register array would put it in scratch memory)
+    const int pi = rg < 6 ? pair_i(rg) : 0, pj = rg < 6 ? pair_j(rg) : 0;
+    float pre[2], blast[2], Ri[2], Rpi[2], Rpj[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int c = 2 * cp + x;
-      // prefix sums over row groups with selects only (run-time indices into a
-      // register array would put it in scratch memory)
-      const int pi = rg < 6 ? pair_i(rg) : 0, pj = rg < 6 ? pair_j(rg) : 0;
-      float pre = 0.f, blast = 0.f, Ri = 0.f, Rpi = 0.f, Rpj = 0.f;
+      pre[x] = blast[x] = Ri[x] = Rpi[x] = Rpj[x] = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const float tr = sm.tot[r][c];
-        blast += tr;
-        pre += (r < rg) ? tr : 0.f;
-        Ri += (r <= 2 * i_sub) ? tr : 0.f;  // b at row 16 i + 7
-        Rpi += (r <= 2 * pi) ? tr : 0.f;
-        Rpj += (r <= 2 * pj) ? tr : 0.f;
-      }
-      const float eRi = exp2_fast(Ri);
-      const float eKh = exp2_fast(blast - Ri);
-      float kh[8], vc[8];
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const float d = b[rr][x] + pre - Ri;
-        const float qv = unpack2(qq[rr], T())[x];
-        const float kv = unpack2(kk[rr], T())[x];
-        qgv[rr][x] = qv * exp2_fast(d);
-        kgv[rr][x] = kv * exp2_fast(-d);
-        qhv[rr][x] = qgv[rr][x] * eRi;
-        kh[rr] = kgv[rr][x] * eKh;
-        vc[rr] = unpack2(vv[rr], T())[x];
-      }
-      store8<T>(&sm.khT[c][8 * rg], kh);
-      store8<T>(&sm.vT[c][8 * rg], vc);
-      if (rg < 6) {
-        sm.vij[rg][c] = exp2_fast(Rpi - Rpj);
-      } else if (rg == 7) {
-        sm.decay[c] = exp2_fast(blast);
+        blast[x] += tr;
+        pre[x] += (r < rg) ? tr : 0.f;
+        Ri[x] += (r <= 2 * i_sub) ? tr : 0.f;  // b at row 16 i + 7
+        Rpi[x] += (r <= 2 * pi) ? tr : 0.f;
+        Rpj[x] += (r <= 2 * pj) ? tr : 0.f;
       }
     }
+    // every wave's lanes cover all DK channels, so each wave reaches the same answer
+    const bool fast = !__any(fminf(blast[0], blast[1]) < -kFastLog2);
+
+    // ---- gated operands for rows 8rg..8rg+7, channels 2cp, 2cp+1
+    if (fast) {
+      float qhv[8][2], kiv[8][2];
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int t = 8 * rg + rr;
-      st_pair<T>(&sm.qg[t][2 * cp], qgv[rr][0], qgv[rr][1]);
-      st_pair<T>(&sm.kg[t][2 * cp], kgv[rr][0], kgv[rr][1]);
-      st_pair<T>(&sm.qh[t][2 * cp], qhv[rr][0], qhv[rr][1]);
+      for (int x = 0; x < 2; ++x) {
+        const int c = 2 * cp + x;
+        const float eB = exp2_fast(blast[x]);
+        float kh[8], vc[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const float bt = b[rr][x] + pre[x];
+          qhv[rr][x] = unpack2(qq[rr], T())[x] * exp2_fast(bt);
+          kiv[rr][x] = unpack2(kk[rr], T())[x] * exp2_fast(-bt);
+          kh[rr] = kiv[rr][x] * eB;
+          vc[rr] = unpack2(vv[rr], T())[x];
+        }
+        store8<T>(&sm.khT[c][8 * rg], kh);
+        store8<T>(&sm.vT[c][8 * rg], vc);
+        if (rg == 7) sm.decay[c] = eB;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int t = 8 * rg + rr;
+        st_pair<T>(&sm.qh[t][2 * cp], qhv[rr][0], qhv[rr][1]);
+        st_pair<T>(&sm.kg[t][2 * cp], kiv[rr][0], kiv[rr][1]);
+      }
+    } else {
+      float qgv[8][2], kgv[8][2], qhv[8][2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int c = 2 * cp + x;
+        const float eRi = exp2_fast(Ri[x]);
+        const float eKh = exp2_fast(blast[x] - Ri[x]);
+        float kh[8], vc[8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const float d = b[rr][x] + pre[x] - Ri[x];
+          qgv[rr][x] = unpack2(qq[rr], T())[x] * exp2_fast(d);
+          kgv[rr][x] = unpack2(kk[rr], T())[x] * exp2_fast(-d);
+          qhv[rr][x] = qgv[rr][x] * eRi;
+          kh[rr] = kgv[rr][x] * eKh;
+          vc[rr] = unpack2(vv[rr], T())[x];
+        }
+        store8<T>(&sm.khT[c][8 * rg], kh);
+        store8<T>(&sm.vT[c][8 * rg], vc);
+        if (rg < 6) {
+          sm.vij[rg][c] = exp2_fast(Rpi[x] - Rpj[x]);
+        } else if (rg == 7) {
+          sm.decay[c] = exp2_fast(blast[x]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int t = 8 * rg + rr;
+        st_pair<T>(&sm.qg[t][2 * cp], qgv[rr][0], qgv[rr][1]);
+        st_pair<T>(&sm.kg[t][2 * cp], kgv[rr][0], kgv[rr][1]);
+        st_pair<T>(&sm.qh[t][2 * cp], qhv[rr][0], qhv[rr][1]);
+      }
     }
     lds_barrier();  // (B) operands ready
 
-    // ---- intra scores: transposed blocks A^T[s][t], masked, stored as A[t][s]
-    for (int blk = wave; blk < 10; blk += NW) {
-      const int i = blk_i(blk), j = blk_j(blk);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- intra scores: transposed blocks A^T[s][t], masked, stored as A[t][s].
+    // All fragments of a phase are read before its first product so that the
+    // LDS latency is paid once per phase, not once per product.
+    {
+      const T* qsrc = fast ? &sm.qh[0][0] : &sm.qg[0][0];
 #pragma unroll
-      for (int p = 0; p < KS; ++p) {
-        F af = ld8<T>(&sm.kg[16 * j + r16][32 * p + 8 * g]);
-        F bf = ld8<T>(&sm.qg[16 * i + r16][32 * p + 8 * g]);
-        if (j < i) bf = scale8(bf, &sm.vij[pair_of(i, j)][32 * p + 8 * g]);
-        mma(acc, af, bf);
-      }
-      if (i == j) {
+      for (int n = 0; n < NB; ++n) {
+        const int blk = wave + n * NW;
+        if (blk < 10) {
+          const int i = blk_i(blk), j = blk_j(blk);
+          F af[KS], bf[KS];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r > r16) acc[r] = 0.f;
+          for (int p = 0; p < KS; ++p) {
+            af[p] = ld8<T>(&sm.kg[16 * j + r16][32 * p + 8 * g]);
+            bf[p] = ld8<T>(qsrc + (16 * i + r16) * DKP + 32 * p + 8 * g);
+          }
+          if (!fast && j < i) {
+#pragma unroll
+            for (int p = 0; p < KS; ++p)
+              bf[p] = scale8(bf[p], &sm.vij[pair_of(i, j)][32 * p + 8 * g]);
+          }
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < KS; ++p) mma(acc, af[p], bf[p]);
+          if (i == j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * g + r > r16) acc[r] = 0.f;
+          }
+          st4<T>(&sm.a[16 * i + r16][16 * j + 4 * g], acc);
+        }
       }
-      st4<T>(&sm.a[16 * i + r16][16 * j + 4 * g], acc);
     }
+
+    // phases are kept apart so that each one's fragments are not live at once
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- inter: O^T[n][t] = sum_c S[c][n] qh[t][c], with the state entering the chunk
     f32x4 O[4];
+    {
+      F qf[4][KS];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      O[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int p = 0; p < KS; ++p) {
-        F af = pack_acc<T>(S[2 * p], S[2 * p + 1]);
-        F bf = ld4x2<T>(&sm.qh[16 * qb + r16][32 * p + 4 * g]);
-        mma(O[qb], af, bf);
+        for (int p = 0; p < KS; ++p) qf[qb][p] = ld4x2<T>(&sm.qh[16 * qb + r16][32 * p + 4 * g]);
+      F sf[KS];
+#pragma unroll
+      for (int p = 0; p < KS; ++p) sf[p] = pack_acc<T>(S[2 * p], S[2 * p + 1]);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        O[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < KS; ++p) mma(O[qb], sf[p], qf[qb][p]);
       }
+      // issue order: every LDS read of the phase, then the products
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS * (sizeof(T) == 2 ? 1 : 8), 0);
     }
 
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- state update: S = diag(2^{b_last}) S + khT V
+    F vf[2];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int p = 0; p < 2; ++p) vf[p] = ld8<T>(&sm.vT[ncol + r16][32 * p + 8 * g]);
+    {
+      F kf[NCB][2];
+      f32x4 dec[NCB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[cb][r] *= sm.decay[16 * cb + 4 * g + r];
+      for (int cb = 0; cb < NCB; ++cb) {
+        dec[cb] = *reinterpret_cast<const f32x4*>(&sm.decay[16 * cb + 4 * g]);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        F af = ld8<T>(&sm.khT[16 * cb + r16][32 * p + 8 * g]);
-        F bf = ld8<T>(&sm.vT[ncol + r16][32 * p + 8 * g]);
-        mma(S[cb], af, bf);
+        for (int p = 0; p < 2; ++p) kf[cb][p] = ld8<T>(&sm.khT[16 * cb + r16][32 * p + 8 * g]);
       }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        S[cb] *= dec[cb];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) mma(S[cb], kf[cb][p], vf[p]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * NCB + 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCB * (sizeof(T) == 2 ? 1 : 8), 0);
     }
     lds_barrier();  // (C) scores ready
 
     // ---- intra: O^T[n][t] += sum_s vT[n][s] A[t][s]
+    {
+      F af[4][2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+      for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int p = 0; p <= qb / 2; ++p) {
-        F af = ld8<T>(&sm.vT[ncol + r16][32 * p + 8 * g]);
-        F bf = ld8<T>(&sm.a[16 * qb + r16][32 * p + 8 * g]);
-        mma(O[qb], af, bf);
-      }
+        for (int p = 0; p <= qb / 2; ++p) af[qb][p] = ld8<T>(&sm.a[16 * qb + r16][32 * p + 8 * g]);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int p = 0; p <= qb / 2; ++p) mma(O[qb], vf[p], af[qb][p]);
     }
 
     // ---- store O[t][ncol + 4g .. +3]
@@ -418,6 +502,452 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) hT[s_base + (16 * cb + 4 * g + r) * DK + ncol + r16] = S[cb][r];
+  }
+}
+
+// ------------------------------------------------------------------ pass 3, bf16
+// Wave-specialised form of the output pass.  One chunk's work splits into a
+// vector-ALU half (loads, cumulative sums, exponentials, the gated operand
+// tiles) and a matrix half (scores and products reading those tiles).  The
+// work-group holds two kinds of waves:
+//   producers (DK/32 waves) load and gate chunk c+1 into one half of a double
+//     buffer while
+//   consumers (DK/32 waves, 32 value columns each, holding the state) run the
+//     products of chunk c from the other half.
+// Per chunk c, two barriers:
+//   phase 1  consumers: load v(c+1); scores(c) -> a, inter(c), state update(c)
+//            producers: load q, k, log-gates(c+2); gate(c+1) -> x[(c+1)&1]
+//   ---- barrier A
+//   phase 2  consumers: intra(c) from a, store O(c), v(c+1)^T -> x[(c+1)&1]
+//            producers: take the loads of c+2
+//   ---- barrier B
+// (v needs no gating, so each consumer moves its own value columns.)
+// A producer wave owns 32 channels of all 64 rows; a lane takes rows
+// 4rq..4rq+3 and 8 channels, with 16-byte loads, and the 16 lanes of one
+// 16-lane row hold the 16 row quads of the same channels.  The chunk's
+// cumulative sums are then a scan inside the wave (in-thread over 4 rows,
+// across the row quads by in-row lane shifts), so gating needs no exchange
+// between waves.  Each
+// producer wave picks the single-reference or the sub-block form for its own
+// channels; the sub-block tables hold 1 for single-reference channels, so the
+// two forms mix freely within a chunk.  Tiles whose contraction runs over
+// tokens ([channel][token]) are unpadded with their 16-byte granules permuted
+// by row (see swz), which keeps the row-strided fragment reads free of bank
+// conflicts.
+
+template <int DK>
+struct PipeBuf {
+  static constexpr int DKP = DK + 8;
+  bf16 qs[kC][DKP];             // fast: q_t 2^{b_t}; sub-block: q_t 2^{b_t - R_i}
+  bf16 ks[kC][DKP];             // fast: k_s 2^{-b_s}; sub-block: k_s 2^{R_j - b_s}
+  bf16 khT[DK * kC];            // (k_s 2^{b_last - b_s})^T, swizzled
+  bf16 vT[DK * kC];             // v^T, swizzled
+  alignas(16) float decay[DK];  // 2^{b_last}
+  alignas(16) float eR[4][DK];  // sub-block chunks only: 2^{R_i}
+  alignas(16) float vij[6][DK]; // sub-block chunks only: 2^{R_i - R_j}
+  int fastw[4];                 // per producer wave: 1 if its channels take one reference
+};
+template <int DK>
+struct PipeSmem {
+  PipeBuf<DK> x[2];
+  bf16 a[kC][kC + 8];            // masked intra scores A[t][s]
+};
+
+// Cross-lane moves inside 16-lane rows (DPP): shift down by N lanes with zero
+// fill, and broadcast of row lane N to the whole row.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+
+// element offset of (row, col) in a [rows][64] tile: granule col/8 permuted by row
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * kC + ((((col >> 3) ^ row ^ (row >> 3)) & 7) << 3) + (col & 7);
+}
+
+template <int DK>
+__global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
+    bf16* __restrict__ o, float* __restrict__ hT, int T_len, int cps, int G) {
+  constexpr int NCB = DK / 16;             // 16-row blocks of the state
+  constexpr int KS = DK / 32;              // contraction steps over channels
+  constexpr int NWC = DK / 32;             // consumer waves (= producer waves)
+  constexpr int NB = (10 + NWC - 1) / NWC; // score blocks per consumer wave, at most
+  constexpr int OCT = DK / 8;              // 8-channel octets per row
+  typedef bf16x8 F;
+  __shared__ PipeSmem<DK> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool consumer = wave < NWC;
+  const int seg = blockIdx.x, bh = blockIdx.y;
+  const size_t off = (size_t)bh * T_len * DK;
+  const int nc = (T_len + kC - 1) / kC;
+  const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);
+  const size_t s_base = (size_t)bh * DK * DK;
+
+  for (int e = tid; e < 512; e += 4 * DK) {
+    const int z = e >> 8, t = (e >> 4) & 15, s = e & 15;
+    sm.a[32 * z + t][32 * z + 16 + s] = to_t<bf16>(0.f);
+  }
+
+  if (consumer) {
+    // ---------------------------------------------------------- consumer
+    const int cw = wave;  // value columns 32cw .. 32cw+31, as two 16-column blocks
+    const float* s0 = seg == 0 ? (h0 ? h0 + s_base : nullptr)
+                               : ws_state + ((size_t)bh * (G - 1) + seg - 1) * DK * DK;
+    f32x4 S[2][NCB];  // S[nt][cb]: rows 16cb + 4g + r, column 32cw + 16nt + r16
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[nt][cb][r] = s0 ? s0[(16 * cb + 4 * g + r) * DK + 32 * cw + 16 * nt + r16] : 0.f;
+
+    // v of a chunk: lane takes rows 4vr..4vr+3, columns 32cw + 8vo .. +7
+    const int vo = lane & 3, vr = lane >> 2;
+    const u32 vv2 = (u32)((4 * vr * DK + 32 * cw + 8 * vo) * 2);
+    u32x4 vl[4];
+    auto load_v = [&](int ch) {
+      const size_t e0 = off + (size_t)ch * kC * DK;
+      const Buf cv(v + e0, (u32)(T_len - ch * kC) * DK * 2);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) vl[rr] = cv.ld128(vv2 + rr * DK * 2);
+    };
+    auto store_vT = [&](PipeBuf<DK>& X) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32 e[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const u32 w = vl[rr][c >> 1];
+          e[rr] = (c & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        *reinterpret_cast<U2*>(&X.vT[swz(32 * cw + 8 * vo + c, 4 * vr)]) =
+            U2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+      }
+    };
+
+    // alongside the producers' prologue (chunk c_begin gated, c_begin+1 taken)
+    load_v(c_begin);
+    store_vT(sm.x[c_begin & 1]);
+    lds_barrier();
+    for (int ch = c_begin; ch < c_end; ++ch) {
+      PipeBuf<DK>& X = sm.x[ch & 1];
+      const bool has_next = ch + 1 < c_end;
+      if (has_next) load_v(ch + 1);
+      int fw = 1;
+#pragma unroll
+      for (int w = 0; w < NWC; ++w) fw &= X.fastw[w];
+      const bool fast = __builtin_amdgcn_readfirstlane(fw) != 0;
+      // ---- phase 1: scores -> a
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int blk = cw + n * NWC;
+        if (blk < 10) {
+          const int i = blk_i(blk), j = blk_j(blk);
+          F af[KS], bf[KS];
+#pragma unroll
+          for (int p = 0; p < KS; ++p) {
+            af[p] = ld8<bf16>(&X.ks[16 * j + r16][32 * p + 8 * g]);
+            bf[p] = ld8<bf16>(&X.qs[16 * i + r16][32 * p + 8 * g]);
+          }
+          if (!fast && j < i) {
+#pragma unroll
+            for (int p = 0; p < KS; ++p) bf[p] = scale8(bf[p], &X.vij[pair_of(i, j)][32 * p + 8 * g]);
+          }
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < KS; ++p) mma(acc, af[p], bf[p]);
+          if (i == j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * g + r > r16) acc[r] = 0.f;
+          }
+          st4<bf16>(&sm.a[16 * i + r16][16 * j + 4 * g], acc);
+        }
+      }
+      // ---- phase 1: inter, O^T[n][t] = sum_c S[c][n] qs[t][c] (state entering the chunk)
+      f32x4 O[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        F qf[2][KS];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int p = 0; p < KS; ++p)
+            qf[u][p] = ld4x2<bf16>(&X.qs[16 * (2 * h + u) + r16][32 * p + 4 * g]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int qb = 2 * h + u;
+            O[nt][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (fast) {
+#pragma unroll
+              for (int p = 0; p < KS; ++p)
+                mma(O[nt][qb], pack_acc<bf16>(S[nt][2 * p], S[nt][2 * p + 1]), qf[u][p]);
+            } else {
+              // sub-block form: query block i sees the state rows scaled by 2^{R_i}
+#pragma unroll
+              for (int p = 0; p < KS; ++p) {
+                const f32x4 e0 = *reinterpret_cast<const f32x4*>(&X.eR[qb][32 * p + 4 * g]);
+                const f32x4 e1 = *reinterpret_cast<const f32x4*>(&X.eR[qb][32 * p + 16 + 4 * g]);
+                mma(O[nt][qb], pack_acc<bf16>(S[nt][2 * p] * e0, S[nt][2 * p + 1] * e1), qf[u][p]);
+              }
+            }
+          }
+      }
+      // ---- phase 1: state update, S = diag(2^{b_last}) S + khT V
+      F vf[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          vf[nt][p] = ld8<bf16>(&X.vT[swz(32 * cw + 16 * nt + r16, 32 * p + 8 * g)]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        F kf[NCB / 2][2];
+#pragma unroll
+        for (int u = 0; u < NCB / 2; ++u)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            kf[u][p] = ld8<bf16>(&X.khT[swz(16 * (h * NCB / 2 + u) + r16, 32 * p + 8 * g)]);
+#pragma unroll
+        for (int u = 0; u < NCB / 2; ++u) {
+          const int cb = h * NCB / 2 + u;
+          const f32x4 dec = *reinterpret_cast<const f32x4*>(&X.decay[16 * cb + 4 * g]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            S[nt][cb] *= dec;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) mma(S[nt][cb], kf[u][p], vf[nt][p]);
+          }
+        }
+      }
+      lds_barrier();  // (A) scores visible
+      // ---- phase 2: intra, O^T[n][t] += sum_s vT[n][s] A[t][s]
+      {
+        F af[4][2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int p = 0; p <= qb / 2; ++p) af[qb][p] = ld8<bf16>(&sm.a[16 * qb + r16][32 * p + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+            for (int p = 0; p <= qb / 2; ++p) mma(O[nt][qb], vf[nt][p], af[qb][p]);
+      }
+      bf16* oc_ = o + off + (size_t)ch * kC * DK;  // chunk base (uniform)
+      const int rows = T_len - ch * kC;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          if (16 * qb + r16 < rows)
+            st4<bf16>(oc_ + (u32)((16 * qb + r16) * DK + 32 * cw + 16 * nt + 4 * g), O[nt][qb]);
+      if (has_next) store_vT(sm.x[(ch + 1) & 1]);
+      lds_barrier();  // (B) chunk done
+    }
+    if (hT && seg == G - 1) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            hT[s_base + (16 * cb + 4 * g + r) * DK + 32 * cw + 16 * nt + r16] = S[nt][cb][r];
+    }
+  } else {
+    // ---------------------------------------------------------- producer
+    const int pw = wave - NWC;                // channels 32pw .. 32pw+31
+    const int ol = lane >> 4, rq = lane & 15;  // channels ch0 .. ch0+7, rows 4rq .. 4rq+3
+    const int ch0 = 32 * pw + 8 * ol;
+    const int i_sub = rq >> 2;                // 16-row sub-block of the rows
+    // per-thread byte offsets inside a chunk, fixed for the whole kernel: the
+    // chunk moves the (scalar) buffer base instead, so no address register is
+    // rewritten while a load that reads it may still be queued
+    const u32 vo2 = (u32)((4 * rq * DK + ch0) * 2), vo4 = (u32)((4 * rq * DK + ch0) * 4);
+
+    u32x4 nq[4], nk[4], nla[4][2];  // loads in flight
+    u32x4 hq[4], hk[4], hla[4][2];  // chunk held for gating
+    // loads of one chunk, one row of the quad at a time (issued spread over the
+    // gating work, so a wave never blocks on a full memory queue for long)
+    struct Src { Buf q, k, la; };
+    auto src_of = [&](int ch) {
+      const size_t e0 = off + (size_t)ch * kC * DK;
+      const u32 rem = (u32)(T_len - ch * kC) * DK;  // elements from the chunk start to the end
+      return Src{Buf(q + e0, rem * 2), Buf(k + e0, rem * 2), Buf(la + e0, rem * 4)};
+    };
+    auto issue_row = [&](const Src& sr, int rr) {
+      nq[rr] = sr.q.ld128(vo2 + rr * DK * 2);
+      nk[rr] = sr.k.ld128(vo2 + rr * DK * 2);
+      nla[rr][0] = sr.la.ld128(vo4 + rr * DK * 4);
+      nla[rr][1] = sr.la.ld128(vo4 + rr * DK * 4 + 16);
+    };
+    auto issue = [&](int ch) {
+      const Src sr = src_of(ch);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) issue_row(sr, rr);
+    };
+    auto take = [&]() {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        hq[rr] = nq[rr];
+        hk[rr] = nk[rr];
+        hla[rr][0] = nla[rr][0];
+        hla[rr][1] = nla[rr][1];
+      }
+    };
+    auto gate = [&](PipeBuf<DK>& X, const Src& sr) {
+      issue_row(sr, 0);
+      // b: inclusive log2 cumsum from the chunk start (in-thread over 4 rows,
+      // then a scan over the 16 row quads inside the 16-lane row)
+      float b[4][8], inc[8], blast[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float run = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          run += f_at(hla[rr][c >> 2], c & 3) * kLog2e;
+          b[rr][c] = run;
+        }
+        inc[c] = run;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) inc[c] += row_shr<1>(inc[c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) inc[c] += row_shr<2>(inc[c]);
+      issue_row(sr, 1);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) inc[c] += row_shr<4>(inc[c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) inc[c] += row_shr<8>(inc[c]);
+      float bmin = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float ex = inc[c] - b[3][c];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) b[rr][c] += ex;
+        blast[c] = row_bcast<15>(inc[c]);  // the last row quad holds the chunk total
+        bmin = c ? fminf(bmin, blast[c]) : blast[c];
+      }
+      const bool fast = !__any(bmin < -kFastLog2);  // uniform over the wave
+      if (lane == 0) X.fastw[pw] = fast ? 1 : 0;
+      if (rq == 0) {
+        *reinterpret_cast<f32x4*>(&X.decay[ch0]) =
+            f32x4{exp2_fast(blast[0]), exp2_fast(blast[1]), exp2_fast(blast[2]), exp2_fast(blast[3])};
+        *reinterpret_cast<f32x4*>(&X.decay[ch0 + 4]) =
+            f32x4{exp2_fast(blast[4]), exp2_fast(blast[5]), exp2_fast(blast[6]), exp2_fast(blast[7])};
+      }
+      // references: none (fast) or b at row 16i+7 for sub-block i
+      float Ri[8];
+      if (fast) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) Ri[c] = 0.f;
+        // the sub-block tables read 1 for these channels
+        if (rq < 10) {
+          float* dst = rq < 4 ? &X.eR[rq][ch0] : &X.vij[rq - 4][ch0];
+          *reinterpret_cast<f32x4*>(dst) = f32x4{1.f, 1.f, 1.f, 1.f};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{1.f, 1.f, 1.f, 1.f};
+        }
+      } else {
+        float R[4][8];  // row 16i+7 is the last row of row quad 4i+1
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          R[0][c] = row_bcast<1>(b[3][c]);
+          R[1][c] = row_bcast<5>(b[3][c]);
+          R[2][c] = row_bcast<9>(b[3][c]);
+          R[3][c] = row_bcast<13>(b[3][c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          Ri[c] = i_sub == 0 ? R[0][c] : i_sub == 1 ? R[1][c] : i_sub == 2 ? R[2][c] : R[3][c];
+        if (rq < 4) {
+          const int i = rq;
+          float e[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            e[c] = exp2_fast(i == 0 ? R[0][c] : i == 1 ? R[1][c] : i == 2 ? R[2][c] : R[3][c]);
+          *reinterpret_cast<f32x4*>(&X.eR[i][ch0]) = f32x4{e[0], e[1], e[2], e[3]};
+          *reinterpret_cast<f32x4*>(&X.eR[i][ch0 + 4]) = f32x4{e[4], e[5], e[6], e[7]};
+        } else if (rq < 10) {
+          const int pr = rq - 4, pi = pair_i(pr), pj = pair_j(pr);
+          float e[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float a0 = pi == 1 ? R[1][c] : pi == 2 ? R[2][c] : R[3][c];
+            const float a1 = pj == 0 ? R[0][c] : pj == 1 ? R[1][c] : R[2][c];
+            e[c] = exp2_fast(a0 - a1);
+          }
+          *reinterpret_cast<f32x4*>(&X.vij[pr][ch0]) = f32x4{e[0], e[1], e[2], e[3]};
+          *reinterpret_cast<f32x4*>(&X.vij[pr][ch0 + 4]) = f32x4{e[4], e[5], e[6], e[7]};
+        }
+      }
+      issue_row(sr, 2);
+      // gated tiles, two rows at a time, rounded to bf16 pairs as they are made
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        if (hp == 1) issue_row(sr, 3);
+        u32 qw[2][4], kw[2][4];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float eKh = exp2_fast(blast[c] - Ri[c]);
+          float qx[2], kx[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int rr = 2 * hp + u;
+            const float d = b[rr][c] - Ri[c];
+            qx[u] = bf_at(hq[rr], c) * exp2_fast(d);
+            kx[u] = bf_at(hk[rr], c) * exp2_fast(-d);
+            if (c & 1) {
+              qw[u][c >> 1] |= pack_bf2(0.f, qx[u]) & 0xffff0000u;
+              kw[u][c >> 1] |= pack_bf2(0.f, kx[u]) & 0xffff0000u;
+            } else {
+              qw[u][c >> 1] = pack_bf2(qx[u], 0.f) & 0xffffu;
+              kw[u][c >> 1] = pack_bf2(kx[u], 0.f) & 0xffffu;
+            }
+          }
+          *reinterpret_cast<u32*>(&X.khT[swz(ch0 + c, 4 * rq + 2 * hp)]) =
+              pack_bf2(kx[0] * eKh, kx[1] * eKh);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int row = 4 * rq + 2 * hp + u;
+          *reinterpret_cast<u32x4*>(&X.qs[row][ch0]) = u32x4{qw[u][0], qw[u][1], qw[u][2], qw[u][3]};
+          *reinterpret_cast<u32x4*>(&X.ks[row][ch0]) = u32x4{kw[u][0], kw[u][1], kw[u][2], kw[u][3]};
+        }
+      }
+    };
+
+    // ---- prologue: chunk c_begin gated, c_begin+1 taken
+    issue(c_begin);
+    take();
+    gate(sm.x[c_begin & 1], src_of(min(c_begin + 1, c_end - 1)));
+    take();
+    lds_barrier();
+    // Loads are issued at the top of an iteration and taken at its end, so no
+    // load is in flight across the loop edge (a register copy there would have
+    // to wait for it).  Past the end, the last chunk is loaded again, unused.
+    for (int ch = c_begin; ch < c_end; ++ch) {
+      const Src nx = src_of(min(ch + 2, c_end - 1));
+      if (ch + 1 < c_end) {
+        gate(sm.x[(ch + 1) & 1], nx);
+      } else {
+        issue(min(ch + 2, c_end - 1));
+      }
+      lds_barrier();  // (A)
+      take();
+      lds_barrier();  // (B)
+    }
   }
 }
 
@@ -443,8 +973,14 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, h0, ws_state, (T*)o, hT, s.T, pl.cps, pl.G);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((gla_output_ws<DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, la, h0, ws_state, (bf16*)o, hT, s.T, pl.cps,
+                       pl.G);
+  } else {
+    hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,
+                       (const T*)k, (const T*)v, la, h0, ws_state, (T*)o, hT, s.T, pl.cps, pl.G);
+  }
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
 def run_and_check(B, H, T, d, w, M, dtype, seed=0, gate_mean=2.0, scale=None, mix=1.0, h0=False,
-                  qk_mult=1.0, zero_gate=False):
+                  qk_mult=1.0, zero_gate=False, steep_chunks=False):
     print(f"[case] B{B} H{H} T{T} d{d} w{w} M{M} {dtype} gate{gate_mean} mix{mix} h0{h0}", flush=True)
     inp = make_inputs(B, H, T, d, d, M, dtype=dtype, seed=seed, gate_mean=gate_mean, with_h0=h0)
     dt = DT[dtype]
@@ -35,6 +35,13 @@ def run_and_check(B, H, T, d, w, M, dtype, seed=0, gate_mean=2.0, scale=None, mi
         inp["k"] = (inp["k"].float() * qk_mult).to(dt)
     if zero_gate:
         inp["log_alpha"] = torch.zeros_like(inp["log_alpha"])
+    if steep_chunks:
+        # every third 64-token chunk decays 8x faster (about -94 per chunk in
+        # natural log), so chunks of both gate ranges follow one another
+        la = inp["log_alpha"].clone()
+        for c0 in range(64, T, 192):
+            la[:, :, c0:c0 + 64] *= 8.0
+        inp["log_alpha"] = la
     s = 1.0 / math.sqrt(d) if scale is None else scale
     x = to_dev(inp)
     out = lz.hybrid_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], w,
@@ -87,6 +94,14 @@ def test_alpha_one_fp32():
 def test_extreme_gates(dtype):
     # log alpha = logsigmoid(N(-3, 1)): about -200 per chunk in natural log
     run_and_check(1, 2, 256, 64, 64, 4, dtype, gate_mean=-3.0)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_mixed_gate_ranges(dtype, d):
+    # chunks with moderate and with steep decay alternate inside one sequence,
+    # with and without an initial state
+    run_and_check(1, 2, 1000, d, 64, 4, dtype, steep_chunks=True)
+    run_and_check(2, 1, 450, d, 128, 4, dtype, steep_chunks=True, h0=True)
 
 
 def test_initial_state_and_mix():
