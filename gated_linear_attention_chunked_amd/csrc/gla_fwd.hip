@@ -34,7 +34,8 @@
 namespace lz {
 namespace {
 
-constexpr int kC = 64;  // chunk length
+constexpr int kC = 64;       // chunk length
+constexpr int kMaxSeg = 16;  // segments per head, at most
 
 __host__ __device__ constexpr int blk_i(int b) { return b == 0 ? 0 : b < 3 ? 1 : b < 6 ? 2 : 3; }
 __host__ __device__ constexpr int blk_j(int b) { return b - blk_i(b) * (blk_i(b) + 1) / 2; }
@@ -54,7 +55,7 @@ Plan make_plan(const Shape& s) {
   p.nc = (s.T + kC - 1) / kC;
   const long long bh = (long long)s.B * s.H;
   int g = (int)((256 + bh - 1) / (bh > 0 ? bh : 1));
-  g = g < 1 ? 1 : (g > 16 ? 16 : g);
+  g = g < 1 ? 1 : (g > kMaxSeg ? kMaxSeg : g);
   if (g > p.nc) g = p.nc > 0 ? p.nc : 1;
   p.cps = p.nc > 0 ? (p.nc + g - 1) / g : 1;
   p.G = p.nc > 0 ? (p.nc + p.cps - 1) / p.cps : 1;
@@ -225,20 +226,34 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
 }
 
 // ------------------------------------------------------------------ pass 2
-// S_in(g+1) = 2^{Gamma_g} S_in(g) + S_loc(g), written over S_loc(g).
+// S_in(g+1) = 2^{Gamma_g} S_in(g) + S_loc(g), written over S_loc(g).  One
+// thread per 4 consecutive state entries (one row); every segment's slot is
+// loaded before the short recurrence runs, so the loads overlap.
 __global__ __launch_bounds__(256) void gla_carry_pass(const float* __restrict__ h0,
                                                      float* __restrict__ ws_state,
                                                      const float* __restrict__ ws_gamma, int DK,
                                                      int G) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   const size_t n = (size_t)DK * DK;
-  for (size_t e = threadIdx.x + (size_t)blockIdx.y * 256; e < n; e += 256 * gridDim.y) {
-    const int c = (int)(e / DK);
-    float S = h0 ? h0[(size_t)bh * n + e] : 0.f;
-    for (int s = 0; s < G - 1; ++s) {
-      float* slot = ws_state + ((size_t)bh * (G - 1) + s) * n;
-      S = exp2_fast(ws_gamma[((size_t)bh * (G - 1) + s) * DK + c]) * S + slot[e];
-      slot[e] = S;
+  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const int c = (int)(e / DK);
+  f32x4 loc[kMaxSeg - 1];
+  float gam[kMaxSeg - 1];
+#pragma unroll
+  for (int s = 0; s < kMaxSeg - 1; ++s) {
+    if (s < G - 1) {
+      const size_t slot = (size_t)bh * (G - 1) + s;
+      loc[s] = *reinterpret_cast<const f32x4*>(ws_state + slot * n + e);
+      gam[s] = ws_gamma[slot * DK + c];
+    }
+  }
+  f32x4 S = h0 ? *reinterpret_cast<const f32x4*>(h0 + (size_t)bh * n + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSeg - 1; ++s) {
+    if (s < G - 1) {
+      S = exp2_fast(gam[s]) * S + loc[s];
+      *reinterpret_cast<f32x4*>(ws_state + ((size_t)bh * (G - 1) + s) * n + e) = S;
     }
   }
 }
@@ -968,8 +983,8 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
                        (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gla_carry_pass, dim3(BH, 4), dim3(256), 0, st, h0, ws_state, ws_gamma,
-                       DK, pl.G);
+    hipLaunchKernelGGL(gla_carry_pass, dim3((DK * DK / 4 + 255) / 256, BH), dim3(256), 0, st, h0,
+                       ws_state, ws_gamma, DK, pl.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
