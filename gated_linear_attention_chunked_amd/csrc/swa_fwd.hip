@@ -215,10 +215,296 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
   }
 }
 
+// ------------------------------------------------------------- streaming form
+// When w <= 64*NPREV + 1, every key a 64-query tile needs lies in the tile's own
+// chunk or the NPREV chunks before it.  A work-group of 8 waves then walks a run
+// of query tiles of one head in order, two tiles (128 queries, one 16-query
+// block per wave) per step, and keeps the chunks those tiles need in an LDS ring
+// of NS = NPREV + 2 slots (K row-major, V transposed), so each key/value row is
+// staged once per work-group.  The next two chunks' K and V and the next
+// queries are loaded into registers while the current step computes (loads
+// issued at the top of an iteration and consumed at its end); two barriers per
+// step.
+template <typename T, int D, int NS>
+struct RingSmem {
+  static constexpr int DP = D + 8;
+  static constexpr int VP = NS * kKT + 8;
+  T k[NS][kKT][DP];
+  T vT[D][VP];
+  T mk[16][DP];
+  T mvT[D][32 + 8];
+};
+
+template <typename T, int D, int NS>
+__global__ __launch_bounds__(512, 1) void swa_fwd_ring(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ mk, const T* __restrict__ mv, T* __restrict__ o,
+    T* __restrict__ o_swa, float* __restrict__ lse, int T_len, int H, int W, int M,
+    float scale_log2, float out_scale, int accumulate, int cps) {
+  constexpr int KS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int NPREV = NS - 2;
+  constexpr int GR = D * (int)sizeof(T) / 16;  // 16-byte granules per row
+  constexpr int KPT = 2 * kKT * GR / 512;      // K granules per thread (two chunks)
+  constexpr int RV = D / 32;                   // V rows per thread (8 channels each)
+  constexpr int VG = (int)sizeof(T) / 2;       // 16-byte granules per 8 channels
+  constexpr int DP = RingSmem<T, D, NS>::DP, VP = RingSmem<T, D, NS>::VP;
+  typedef typename Frag<T>::type F;
+  __shared__ RingSmem<T, D, NS> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nseg = gridDim.x;
+  const int logical = xcd_remap(blockIdx.y * nseg + blockIdx.x, nseg * gridDim.y);
+  const int bh = logical / nseg, h = bh % H, seg = logical % nseg;
+  const int nc = (T_len + kKT - 1) / kKT;
+  const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);  // cps is even
+  const int half = wave >> 2, wq = wave & 3;  // this wave's tile of the step, block in it
+  const size_t base = (size_t)bh * T_len * D;
+  const u32 nbytes = (u32)((size_t)T_len * D * sizeof(T));
+  const Buf bq(q + base, nbytes), bk(k + base, nbytes), bv(v + base, nbytes);
+
+  // staging of the two chunks ch0, ch0+1 (threads 0..255 take ch0, the rest ch0+1):
+  //   K granule e = (tid & 255) + 256 j -> row e / GR, granule e % GR;
+  //   V rows RV*vr .. +RV-1, channels 8vo .. 8vo+7
+  const int sc = tid >> 8, st = tid & 255;
+  const int vo = st % (D / 8), vr = st / (D / 8);
+  u32x4 pk[KPT], pv[RV][VG];
+  auto load_kv = [&](int ch0) {
+    const int ch = ch0 + sc;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = st + 256 * j;
+      pk[j] = bk.ld128((u32)((ch * kKT + e / GR) * D * sizeof(T) + (e % GR) * 16));
+    }
+#pragma unroll
+    for (int rr = 0; rr < RV; ++rr)
+#pragma unroll
+      for (int u = 0; u < VG; ++u)
+        pv[rr][u] = bv.ld128((u32)(((ch * kKT + RV * vr + rr) * D + 8 * vo) * sizeof(T) + 16 * u));
+  };
+  auto store_kv = [&](int ch0) {
+    const int ch = ch0 + sc;
+    const int slot = ch % NS;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = st + 256 * j;
+      *reinterpret_cast<u32x4*>(&sm.k[slot][e / GR][(e % GR) * (16 / sizeof(T))]) = pk[j];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      T* dst = &sm.vT[8 * vo + c][slot * kKT + RV * vr];
+      if constexpr (sizeof(T) == 2) {
+        u32 e[RV];
+#pragma unroll
+        for (int rr = 0; rr < RV; ++rr) {
+          const u32 w = pv[rr][0][c >> 1];
+          e[rr] = (c & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        if constexpr (RV == 4) {
+          *reinterpret_cast<U2*>(dst) = U2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        } else {
+          *reinterpret_cast<u32*>(dst) = e[0] | (e[1] << 16);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < RV; ++rr) {
+          const u32 w = pv[rr][c >> 2][c & 3];
+          reinterpret_cast<u32*>(dst)[rr] = w;
+        }
+      }
+    }
+  };
+  // query fragments of the lane's query (B operand, contiguous channel map);
+  // rows past the end read zero and are never stored
+  F qf[KS], qn[KS];
+  auto load_q = [&](int ch, F* dst) {
+    const u32 row = (u32)(ch * kKT + 16 * wq + r16);
+#pragma unroll
+    for (int p = 0; p < KS; ++p) {
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 x = bq.ld128((row * D + 32 * p + 8 * g) * 2);
+        dst[p] = __builtin_bit_cast(bf16x8, x);
+      } else {
+        const u32x4 x0 = bq.ld128((row * D + 32 * p + 8 * g) * 4);
+        const u32x4 x1 = bq.ld128((row * D + 32 * p + 8 * g) * 4 + 16);
+        F f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f[i] = as_f(x0[i]); f[4 + i] = as_f(x1[i]); }
+        dst[p] = f;
+      }
+    }
+  };
+
+  // ---- prologue: meta slots, the chunks before the first tile and its own chunk
+  if (M > 0) {
+    const Buf bmk(mk + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
+    const Buf bmv(mv + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
+    stage_rows(&sm.mk[0][0], DP, bmk, 0, D, 16, tid, 512);
+    stage_cols(&sm.mvT[0][0], 32 + 8, bmv, 0, D, 32, tid, 512);
+  }
+  // chunks c_begin-NPREV .. c_begin+1, two at a time (out-of-range rows read 0)
+  for (int ch = c_begin - NPREV; ch <= c_begin + 1; ch += 2) {
+    const bool mine = ch + sc >= 0 && ch + sc <= c_begin + 1;
+    if (mine) load_kv(ch);
+    if (mine) store_kv(ch);
+  }
+  load_q(c_begin + half, qf);
+  lds_barrier();
+
+  for (int cs = c_begin; cs < c_end; cs += 2) {
+    const bool has_next = cs + 2 < c_end;
+    if (has_next) {
+      load_kv(cs + 2);
+      load_q(cs + 2 + half, qn);
+    }
+    const int ch = cs + half;  // this wave's query tile
+    const int t0 = ch * kKT;
+    const int tq0 = t0 + 16 * wq, tq = tq0 + r16;
+    const bool stores = ch < c_end && tq < T_len;
+    // the branch output this step adds to, read now so the load overlaps the step
+    typedef typename Pair<T>::type Raw2;
+    Raw2 oacc[NT][2];
+    if (accumulate && stores) {
+      const T* src = o + base + (size_t)tq * D + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        oacc[nt][0] = *reinterpret_cast<const Raw2*>(src + 16 * nt);
+        oacc[nt][1] = *reinterpret_cast<const Raw2*>(src + 16 * nt + 2);
+      }
+    }
+    // The whole window of this wave's 16 queries is at most 4*(NPREV+1) key
+    // blocks plus the meta block, so the softmax is taken exactly: every logit
+    // tile first (independent product chains), one max, one exponential pass,
+    // then every P V product -- no running rescale between key blocks.
+    constexpr int NKB = 4 * (NPREV + 1);
+    f32x4 Pm = {0.f, 0.f, 0.f, 0.f}, P[NKB];
+    bool act[NKB];  // uniform over the wave
+    if (M > 0) {
+#pragma unroll
+      for (int p = 0; p < KS; ++p) mma(Pm, ld8<T>(&sm.mk[r16][32 * p + 8 * g]), qf[p]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pm[r] = (4 * g + r < M) ? Pm[r] * scale_log2 : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+      const int kc = ch - NPREV + (j >> 2);
+      const int s_lo = kc * kKT + 16 * (j & 3);
+      act[j] = kc >= 0 && (s_lo + 15 >= tq0 - W + 1) && (s_lo <= tq0 + 15) && (s_lo < T_len);
+      P[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (act[j]) {
+        const int slot = kc % NS;
+#pragma unroll
+        for (int p = 0; p < KS; ++p)
+          mma(P[j], ld8<T>(&sm.k[slot][16 * (j & 3) + r16][32 * p + 8 * g]), qf[p]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = s_lo + 4 * g + r;
+          const bool ok = (s <= tq) && (s > tq - W);
+          P[j][r] = ok ? P[j][r] * scale_log2 : -INFINITY;
+        }
+      }
+    }
+    float mt = kNegBig;
+    if (M > 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, Pm[r]);
+#pragma unroll
+    for (int j = 0; j < NKB; ++j)
+      if (act[j])
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, P[j][r]);
+    mt = wave_max16(mt);
+    float l_run = 0.f;
+    if (M > 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Pm[r] = exp2_fast(Pm[r] - mt);
+        l_run += Pm[r];
+      }
+#pragma unroll
+    for (int j = 0; j < NKB; ++j)
+      if (act[j])
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          P[j][r] = exp2_fast(P[j][r] - mt);
+          l_run += P[j][r];
+        }
+    f32x4 O[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (M > 0) {
+      const F bf = pack_acc<T>(Pm, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld4x2<T>(&sm.mvT[16 * nt + r16][4 * g]), bf);
+    }
+#pragma unroll
+    for (int jp = 0; jp < NKB / 2; ++jp) {
+      if (act[2 * jp] || act[2 * jp + 1]) {
+        const int kc = ch - NPREV + (jp >> 1);
+        const F bf = pack_acc<T>(P[2 * jp], P[2 * jp + 1]);
+        const T* vs = &sm.vT[0][(kc % NS) * kKT + 32 * (jp & 1) + 4 * g];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld4x2<T>(vs + (16 * nt + r16) * VP), bf);
+      }
+    }
+    const float m_run = mt;
+
+    // ---- normalise and store
+    const float l_tot = wave_sum16(l_run);
+    const float inv = 1.f / l_tot;
+    if (stores) {
+      const size_t rowo = base + (size_t)tq * D;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const size_t off = rowo + 16 * nt + 4 * g;
+        const f32x4 val = O[nt] * inv;
+        if (o_swa) st4<T>(o_swa + off, val);
+        f32x4 out = val * out_scale;
+        if (accumulate) {
+          const f32x2 a = unpack2(oacc[nt][0], T()), b = unpack2(oacc[nt][1], T());
+          out += f32x4{a[0], a[1], b[0], b[1]};
+        }
+        st4<T>(o + off, out);
+      }
+      if (lse && g == 0) lse[(size_t)bh * T_len + tq] = (m_run + log2_fast(l_tot)) * kLn2;
+    }
+
+    lds_barrier();  // every read of the two oldest ring slots is done
+    if (has_next) {
+      store_kv(cs + 2);
+#pragma unroll
+      for (int p = 0; p < KS; ++p) qf[p] = qn[p];
+    }
+    lds_barrier();  // the next two chunks are in the ring
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v,
                         const void* mk, const void* mv, void* o, float out_scale, int acc,
                         void* o_swa, float* lse, hipStream_t st) {
+  if (s.window <= 2 * kKT + 1) {
+    // streaming form: runs of query tiles, enough work-groups to fill the chip
+    const int nc = (s.T + kKT - 1) / kKT;
+    const long long bh = (long long)s.B * s.H;
+    int g = (int)((256 + bh - 1) / bh);
+    g = g < 1 ? 1 : (g > nc ? nc : g);
+    int cps = (nc + g - 1) / g;
+    cps += cps & 1;  // whole steps of two tiles
+    const int G = (nc + cps - 1) / cps;
+    const float sl = s.scale * kLog2e;
+    if (s.window <= kKT + 1) {
+      hipLaunchKernelGGL((swa_fwd_ring<T, D, 3>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
+                         (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
+                         lse, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+    } else {
+      hipLaunchKernelGGL((swa_fwd_ring<T, D, 4>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
+                         (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
+                         lse, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+    }
+    return hipGetLastError();
+  }
   dim3 grid((s.T + kQT - 1) / kQT, s.B * s.H);
   hipLaunchKernelGGL((swa_fwd_kernel<T, D, D>), grid, dim3(256), 0, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa, lse, s.T, s.H,
