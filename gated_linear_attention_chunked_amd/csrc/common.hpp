@@ -192,6 +192,35 @@ __device__ __forceinline__ int xcd_remap(int L, int n) {
   return xcd * base + min(xcd, rem) + idx;
 }
 
+// LDS tile layouts.  A "granule" is 8 consecutive elements (one matrix-core
+// fragment: 16 bytes of bf16, 32 of fp32).  Tiles are stored unpadded with the
+// granules of each row permuted by a row-dependent XOR, chosen so that the
+// fragment reads (16 consecutive rows, one granule column) and the staging
+// writes of every kernel hit distinct banks.
+template <int GR>  // granules per row
+__device__ __forceinline__ int swz_gran(int row, int gran) {
+  if constexpr (GR == 4) {
+    return gran ^ ((row ^ (row >> 2)) & 3);
+  } else if constexpr (GR == 8) {
+    return (gran ^ row ^ (row >> 3)) & 7;
+  } else if constexpr (GR == 16) {
+    return gran ^ ((row ^ (row >> 2)) & 15);
+  } else {
+    return gran ^ ((row ^ (row >> 3)) & 15);
+  }
+}
+// element offset of (row, col) in a swizzled tile of GR granules per row
+template <int GR>
+__device__ __forceinline__ int swz_at(int row, int col) {
+  return row * (8 * GR) + swz_gran<GR>(row, col >> 3) * 8 + (col & 7);
+}
+// Position of element c of a 32-element group in "split" order: quads
+// 4g..4g+3 and 16+4g..16+4g+3 sit next to each other, so the granule at
+// position 8g holds exactly lane group g's split-map fragment.
+__host__ __device__ constexpr int split_pos(int c) {
+  return (c & ~31) | (((c & 15) >> 2) << 3) | ((c & 16) >> 2) | (c & 3);
+}
+
 __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

@@ -225,14 +225,16 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
 // queries are loaded into registers while the current step computes (loads
 // issued at the top of an iteration and consumed at its end); two barriers per
 // step.
+// LDS: K rows and V^T rows in swizzled granule layouts; V^T tokens (and the
+// meta V^T slots) in split order, so each P V operand is one granule read.
 template <typename T, int D, int NS>
 struct RingSmem {
-  static constexpr int DP = D + 8;
-  static constexpr int VP = NS * kKT + 8;
-  T k[NS][kKT][DP];
-  T vT[D][VP];
-  T mk[16][DP];
-  T mvT[D][32 + 8];
+  static constexpr int GK = D / 8;    // granules per K row
+  static constexpr int VW = 4 * kKT;  // V^T row length (tokens), a power-of-two granule count
+  T k[NS * kKT * D];
+  T vT[D * VW];
+  T mk[16 * D];
+  T mvT[D * 32];
 };
 
 template <typename T, int D, int NS>
@@ -248,7 +250,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
   constexpr int KPT = 2 * kKT * GR / 512;      // K granules per thread (two chunks)
   constexpr int RV = D / 32;                   // V rows per thread (8 channels each)
   constexpr int VG = (int)sizeof(T) / 2;       // 16-byte granules per 8 channels
-  constexpr int DP = RingSmem<T, D, NS>::DP, VP = RingSmem<T, D, NS>::VP;
+  constexpr int GK = RingSmem<T, D, NS>::GK, VW = RingSmem<T, D, NS>::VW;
+  static_assert(NS <= 4, "ring slots fit the V^T row");
   typedef typename Frag<T>::type F;
   __shared__ RingSmem<T, D, NS> sm;
 
@@ -289,11 +292,12 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int e = st + 256 * j;
-      *reinterpret_cast<u32x4*>(&sm.k[slot][e / GR][(e % GR) * (16 / sizeof(T))]) = pk[j];
+      const int row = e / GR, col = (e % GR) * (16 / (int)sizeof(T));
+      *reinterpret_cast<u32x4*>(&sm.k[slot * kKT * D + swz_at<GK>(row, col)]) = pk[j];
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      T* dst = &sm.vT[8 * vo + c][slot * kKT + RV * vr];
+      T* dst = &sm.vT[swz_at<VW / 8>(8 * vo + c, slot * kKT + split_pos(RV * vr))];
       if constexpr (sizeof(T) == 2) {
         u32 e[RV];
 #pragma unroll
@@ -338,10 +342,17 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
 
   // ---- prologue: meta slots, the chunks before the first tile and its own chunk
   if (M > 0) {
-    const Buf bmk(mk + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
-    const Buf bmv(mv + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
-    stage_rows(&sm.mk[0][0], DP, bmk, 0, D, 16, tid, 512);
-    stage_cols(&sm.mvT[0][0], 32 + 8, bmv, 0, D, 32, tid, 512);
+    // meta K rows (slots >= M read zero) and meta V^T in split order
+    const T* mkh = mk + (size_t)h * M * D;
+    const T* mvh = mv + (size_t)h * M * D;
+    for (int e = tid; e < 16 * D; e += 512) {
+      const int r = e / D, c = e % D;
+      sm.mk[swz_at<GK>(r, c)] = r < M ? mkh[r * D + c] : to_t<T>(0.f);
+    }
+    for (int e = tid; e < 32 * D; e += 512) {
+      const int c = e / 32, t = e % 32;
+      sm.mvT[swz_at<4>(c, split_pos(t))] = t < M ? mvh[t * D + c] : to_t<T>(0.f);
+    }
   }
   // chunks c_begin-NPREV .. c_begin+1, two at a time (out-of-range rows read 0)
   for (int ch = c_begin - NPREV; ch <= c_begin + 1; ch += 2) {
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     bool act[NKB];  // uniform over the wave
     if (M > 0) {
 #pragma unroll
-      for (int p = 0; p < KS; ++p) mma(Pm, ld8<T>(&sm.mk[r16][32 * p + 8 * g]), qf[p]);
+      for (int p = 0; p < KS; ++p) mma(Pm, ld8<T>(&sm.mk[swz_at<GK>(r16, 32 * p + 8 * g)]), qf[p]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Pm[r] = (4 * g + r < M) ? Pm[r] * scale_log2 : -INFINITY;
     }
@@ -396,7 +407,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
         const int slot = kc % NS;
 #pragma unroll
         for (int p = 0; p < KS; ++p)
-          mma(P[j], ld8<T>(&sm.k[slot][16 * (j & 3) + r16][32 * p + 8 * g]), qf[p]);
+          mma(P[j], ld8<T>(&sm.k[slot * kKT * D + swz_at<GK>(16 * (j & 3) + r16, 32 * p + 8 * g)]),
+              qf[p]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = s_lo + 4 * g + r;
@@ -436,16 +448,16 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     if (M > 0) {
       const F bf = pack_acc<T>(Pm, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld4x2<T>(&sm.mvT[16 * nt + r16][4 * g]), bf);
+      for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld8<T>(&sm.mvT[swz_at<4>(16 * nt + r16, 8 * g)]), bf);
     }
 #pragma unroll
     for (int jp = 0; jp < NKB / 2; ++jp) {
       if (act[2 * jp] || act[2 * jp + 1]) {
         const int kc = ch - NPREV + (jp >> 1);
         const F bf = pack_acc<T>(P[2 * jp], P[2 * jp + 1]);
-        const T* vs = &sm.vT[0][(kc % NS) * kKT + 32 * (jp & 1) + 4 * g];
+        const int pos = (kc % NS) * kKT + 32 * (jp & 1) + 8 * g;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld4x2<T>(vs + (16 * nt + r16) * VP), bf);
+        for (int nt = 0; nt < NT; ++nt) mma(O[nt], ld8<T>(&sm.vT[swz_at<VW / 8>(16 * nt + r16, pos)]), bf);
       }
     }
     const float m_run = mt;
