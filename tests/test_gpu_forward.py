@@ -81,9 +81,21 @@ def test_fp32_ragged_lengths(T):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T,w,M", [(300, 128, 4), (200, 1, 0), (129, 7, 16), (70, 500, 0),
-                                   (257, 64, 3)])
+                                   (257, 64, 3), (400, 65, 4), (400, 129, 4), (400, 130, 2)])
 def test_bf16_shapes(d, T, w, M):
     run_and_check(2, 2, T, d, w, M, "bf16", seed=T + w)
+
+
+@pytest.mark.parametrize("T", [1000, 900])
+def test_window_runs_of_tiles(T):
+    # 64 heads: several query-tile steps per work-group of the streaming window
+    # kernel, with an odd chunk count in the last run for T = 900
+    run_and_check(4, 16, T, 64, 100, 4, "bf16", seed=T)
+
+
+def test_fp32_window_boundaries():
+    run_and_check(1, 2, 300, 64, 129, 3, "f32", seed=5)
+    run_and_check(1, 2, 300, 64, 65, 3, "f32", seed=6)
 
 
 def test_alpha_one_fp32():
