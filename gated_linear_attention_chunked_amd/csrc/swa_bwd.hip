@@ -319,19 +319,48 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
 }
 
 // ----------------------------------------------------------- 3. meta reduce
-__global__ __launch_bounds__(256) void swa_meta_reduce(const float* __restrict__ metap,
-                                                       float* __restrict__ dmk,
-                                                       float* __restrict__ dmv, int B, int H,
-                                                       int ntiles, int M) {
+// Meta gradients: sum of the per-(sequence, query tile) partials, in a fixed
+// order (deterministic).  A block takes 64 consecutive entries of one head;
+// its 16 thread groups sum interleaved sixteenths of the partials (coalesced,
+// up to 16 loads in flight per thread), then a fixed tree adds the 16 sums.
+constexpr int kMetaGroups = 16;
+__global__ __launch_bounds__(64 * kMetaGroups) void swa_meta_reduce(
+    const float* __restrict__ metap, float* __restrict__ dmk, float* __restrict__ dmv, int B,
+    int H, int ntiles, int M) {
   const int h = blockIdx.x;
   const int n = M * kD;
-  for (int e = threadIdx.x; e < 2 * n; e += blockDim.x) {
-    float s = 0.f;
-    for (int b = 0; b < B; ++b)
-      for (int tl = 0; tl < ntiles; ++tl)
-        s += metap[(((size_t)(b * H + h)) * ntiles + tl) * 2 * n + e];
-    if (e < n) dmk[(size_t)h * n + e] = s;
-    else dmv[(size_t)h * n + e - n] = s;
+  const int i = threadIdx.x & 63;
+  const int e = blockIdx.y * 64 + i;
+  const int grp = threadIdx.x >> 6;
+  const int np = B * ntiles;  // partials of this head: p = b * ntiles + tile
+  float s = 0.f;
+  if (e < 2 * n) {
+    auto at = [&](int p) {
+      const int b = p / ntiles, tl = p - b * ntiles;
+      return metap[(((size_t)(b * H + h)) * ntiles + tl) * 2 * n + e];
+    };
+    constexpr int G = kMetaGroups;
+    int p = grp;
+    for (; p + 15 * G < np; p += 16 * G) {
+      float x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = at(p + G * u);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += x[u];
+    }
+    for (; p < np; p += G) s += at(p);
+  }
+  __shared__ float part[kMetaGroups][64];
+  part[grp][i] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = kMetaGroups / 2; w >= 1; w >>= 1) {
+    if (grp < w) part[grp][i] += part[grp + w][i];
+    __syncthreads();
+  }
+  if (grp == 0 && e < 2 * n) {
+    if (e < n) dmk[(size_t)h * n + e] = part[0][i];
+    else dmv[(size_t)h * n + e - n] = part[0][i];
   }
 }
 
@@ -362,8 +391,9 @@ hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const vo
                        s.window, s.scale, s.mix);
   }
   if (s.n_meta > 0 && s.H > 0)
-    hipLaunchKernelGGL(swa_meta_reduce, dim3(s.H), dim3(256), 0, st, metap, dmk, dmv, s.B, s.H,
-                       nqt, s.n_meta);
+    hipLaunchKernelGGL(swa_meta_reduce, dim3(s.H, (2 * s.n_meta * kD + 63) / 64),
+                       dim3(64 * kMetaGroups), 0, st,
+                       metap, dmk, dmv, s.B, s.H, nqt, s.n_meta);
   return hipGetLastError();
 }
 
