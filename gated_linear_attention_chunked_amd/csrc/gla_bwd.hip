@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_state_scan(
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gla_bwd_dstate_scan(
     const T* __restrict__ q, const T* __restrict__ dO, const float* __restrict__ la,
-    T* __restrict__ dS_all, int T_len) {
+    T* __restrict__ dS_all, T* __restrict__ dST_all, int T_len) {
   __shared__ __attribute__((aligned(16))) float bt[kC][kD + 4];
   __shared__ __attribute__((aligned(16))) float tot[4][kD];
   __shared__ __attribute__((aligned(16))) T qhT[kD][kTP];
@@ -152,10 +152,13 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_dstate_scan(
   for (int cb = 0; cb < kD / 16; ++cb) dS[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int ch = nc - 1; ch >= 0; --ch) {
     T* dst = dS_all + ((size_t)bh * nc + ch) * kD * kD;
+    T* dstT = dST_all + ((size_t)bh * nc + ch) * kD * kD;
 #pragma unroll
-    for (int cb = 0; cb < kD / 16; ++cb)
+    for (int cb = 0; cb < kD / 16; ++cb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * kD + 16 * wave + r16] = to_t<T>(dS[cb][r]);
+      st4<T>(dstT + (16 * wave + r16) * kD + 16 * cb + 4 * g, dS[cb]);
+    }
     stage_cols<T>(&qhT[0][0], kTP, bq, ch * kC, kD, kC, tid, kThreads);
     stage_cols<T>(&dOT[0][0], kTP, bdo, ch * kC, kD, kC, tid, kThreads);
     gate_table(bt, tot, bla, ch * kC, tid);
@@ -175,337 +178,430 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_dstate_scan(
   }
 }
 
-// Shared per-chunk quantities: midpoints R_i = b[16i+7], pair factors 2^{R_i - R_j}.
-struct ChunkRefs {
-  float R[4][kD];
-  float vij[6][kD];
+// ------------------------------------------------------- 3. per-chunk grads
+// DPP moves within rows of 16 lanes (zero where the source leaves the row).
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {  // lane i <- lane i - N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_shl(float x) {  // lane i <- lane i + N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_bcast(float x) {  // every lane <- lane N of its row
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ u32 dpp_swap1(u32 x) {  // exchange with the neighbouring lane
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);
+}
+// bf16 pairs: low halves of (a, b), high halves of (a, b)
+__device__ __forceinline__ u32 lo2(u32 a, u32 b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ u32 hi2(u32 a, u32 b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ __forceinline__ bf16x8 as_bf8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
+
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 ld64v(const Buf& b, u32 off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
+}
+
+constexpr int kTile = kC * kD;
+// element offset of (row, col) in a swizzled 64 x 64 bf16 tile
+__device__ __forceinline__ int at(int row, int col) { return swz_at<8>(row, col); }
+
+struct BwdSmem {
+  bf16 qg[kTile];   // q~ rows [t][c] = q_t 2^{b_t - R_i}, i = block of t
+  bf16 kg[kTile];   // k~ rows [s][c] = k_s 2^{R_j - b_s}, j = block of s
+  bf16 qgT[kTile];  // q~ transposed [c][split_pos(t)]
+  bf16 kgT[kTile];  // k~ transposed [c][split_pos(s)]
+  bf16 dor[kTile];  // dO rows [t][j]
+  bf16 doT[kTile];  // dO transposed [j][split_pos(t)]
+  bf16 vr[kTile];   // v rows [s][j]
+  float tot[4][kD];  // per-block gate totals
+  float R[4][kD];    // sub-block references R_i = b[16i + 7]
+  float bl[kD];      // chunk total b_last
+  float eR[4][kD];   // 2^{R_i}
+  float elR[4][kD];  // 2^{b_last - R_i}
+  float vij[6][kD];  // 2^{R_i - R_j}, i > j, index pair_of(i, j)
+  float sx[4][kD];   // per-block totals of the suffix items of dlog_alpha
+  float sy[4][kD];   // per-block totals of the prefix items
+  float st[kD];      // state term 2^{b_last} sum_j dS_{c+1}[c][j] S_c[c][j]
 };
 
-__device__ __forceinline__ void chunk_refs(ChunkRefs& cr, float (*bt)[kD + 4], int tid) {
-  const int c = tid % kD, qtr = tid / kD;
-  cr.R[qtr][c] = bt[16 * qtr + 7][c];
-  // pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) -> indices 0..5; quarter qtr computes qtr and qtr+4
-  const int pi[6] = {1, 2, 2, 3, 3, 3}, pj[6] = {0, 0, 1, 0, 1, 2};
+// factor 2^{R_i - R_j} for query block i, key block j (1 on the diagonal, 0 above)
+__device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, int c) {
+  return i > j ? sm.vij[pair_of(i, j)][c] : (i == j ? 1.f : 0.f);
+}
+
+// One work-group per (chunk, head): dq, dk, dv and dlog_alpha of the GLA
+// branch, from the chunk's inputs and the states S_c, dS_{c+1} (and dS_{c+1}^T)
+// written by the two scans.  Wave w owns token block w in both roles (query for
+// dq, key for dk and dv), so the work of the two halves balances.  Lane
+// (r16, g) owns token t = 16w + r16 and channels 16ct + 4g + r (ct, r < 4):
+// the accumulator layout of every output tile, in which the gate cumsum and
+// the dlog_alpha scans are also kept.
+__global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
+    const bf16* __restrict__ dS_all, const bf16* __restrict__ dST_all, bf16* __restrict__ dq,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dla, int T_len) {
+  __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ch = blockIdx.x, bh = blockIdx.y;
+  const int nc = gridDim.x, t0 = ch * kC;
+  const size_t off = (size_t)bh * T_len * kD;
+  const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
+  const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
+  const Buf bla(la + off, 2 * nb);
+  const size_t soff = ((size_t)bh * nc + ch) * kTile;
+  const u32 sb = (u32)(kTile * sizeof(bf16));
+  const Buf bS(S_all + soff, sb), bdS(dS_all + soff, sb), bdST(dST_all + soff, sb);
+  const int t = 16 * w + r16;
+  const bool live = t0 + t < T_len;
+  const u32 rowe = (u32)(t0 + t) * kD;  // element offset of this lane's token row
+
+  // ---- 0. every global read of the work-group, issued up front
+  u32x4 la4[4];
+  u32x2 q2[4], k2[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const u32 e = rowe + 16 * ct + 4 * g;
+    la4[ct] = bla.ld128(e * 4);
+    q2[ct] = ld64v(bq, e * 2);
+    k2[ct] = ld64v(bk, e * 2);
+  }
+  // dO / v staging: piece p -> token (p & 1) | 2 (p >> 4), granule (p >> 1) & 7,
+  // so neighbouring lanes hold neighbouring tokens of the same granule
+  u32x4 dog[2], vg[2];
+  int pt[2], po[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int p = qtr + 4 * h;
-    if (p < 6) cr.vij[p][c] = exp2_fast(bt[16 * pi[p] + 7][c] - bt[16 * pj[p] + 7][c]);
+    const int p = tid + kThreads * h;
+    pt[h] = (p & 1) | ((p >> 4) << 1);
+    po[h] = (p >> 1) & 7;
+    const u32 e = (u32)(t0 + pt[h]) * kD + 8 * po[h];
+    dog[h] = bdo.ld128(e * 2);
+    vg[h] = bv.ld128(e * 2);
   }
-}
-
-// factor 2^{R_i - R_j} for query block i and key block j (1 on the diagonal, 0 above)
-__device__ __forceinline__ float pair_factor(const ChunkRefs& cr, int i, int j, int c) {
-  return i > j ? cr.vij[pair_of(i, j)][c] : (i == j ? 1.f : 0.f);
-}
-
-// ---------------------------------------------------------------------- 3. dq
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gla_bwd_dq(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ la, const T* __restrict__ dO, const T* __restrict__ S_all,
-    const T* __restrict__ dS_all, T* __restrict__ dq, float* __restrict__ dla, int T_len) {
-  typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T sdo[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T sv[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T sS[kD][kDP];
-  __shared__ __attribute__((aligned(16))) T sq[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T kgT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T sk[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T sdS[kD][kDP];
-  __shared__ __attribute__((aligned(16))) float bt[kC][kD + 4];
-  __shared__ __attribute__((aligned(16))) float dbt[kC][kD + 4];
-  __shared__ __attribute__((aligned(16))) float tot[4][kD];
-  __shared__ __attribute__((aligned(16))) ChunkRefs cr;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int r16 = lane & 15, g = lane >> 4;
-  const int c = tid % kD, qtr = tid / kD;
-  const int ch = blockIdx.x, bh = blockIdx.y;
-  const int nc = gridDim.x, t0 = ch * kC;
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
-  const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
-  const Buf bla(la + off, (u32)((size_t)T_len * kD * 4));
-  const Buf bS(S_all + ((size_t)bh * nc + ch) * kD * kD, (u32)(kD * kD * sizeof(T)));
-  const Buf bdS(dS_all + ((size_t)bh * nc + ch) * kD * kD, (u32)(kD * kD * sizeof(T)));
-  stage_rows<T>(&sk[0][0], kDP, bk, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sdS[0][0], kDP, bdS, 0, kD, kD, tid, kThreads);
-  stage_rows<T>(&sdo[0][0], kDP, bdo, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sv[0][0], kDP, bv, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sq[0][0], kDP, bq, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sS[0][0], kDP, bS, 0, kD, kD, tid, kThreads);
-  stage_cols<T>(&kgT[0][0], kTP, bk, t0, kD, kC, tid, kThreads);
-  gate_table(bt, tot, bla, t0, tid);
-  lds_barrier();
-  // kg^T[c][s] = k_s 2^{R_j - b_s}, j = block of s (= qtr for this thread's rows)
-  scale_run16<T>(&kgT[c][16 * qtr], 1.f, &bt[16 * qtr][c], -1.f, bt[16 * qtr + 7][c]);
-  chunk_refs(cr, bt, tid);
-  lds_barrier();
-
-  const int w = wave;  // query block
-  f32x4 dAT[4];        // dA^T[s = 16j + 4g + r][t = 16w + r16], strictly s < t
-  float dAtt = 0.f;    // diagonal dA[t][t] of this lane's query
+  // state fragments: rows 16ct + r16, columns 32p + 8g..
+  auto frag_off = [&](int ct, int p) { return (u32)((16 * ct + r16) * kD + 32 * p + 8 * g) * 2; };
+  u32x4 Sf[4][2], dSf[4][2], dSTf[4][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    dAT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (j <= w) {
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-        mma(dAT[j], ld8<T>(&sv[16 * j + r16][32 * p + 8 * g]), ld8<T>(&sdo[16 * w + r16][32 * p + 8 * g]));
-      if (j == w) {
-        // lane (col r16, group r16/4) holds the diagonal at element r16 % 4
-        dAtt = __shfl(dAT[j][r16 & 3], 16 * (r16 >> 2) + r16);
+    for (int p = 0; p < 2; ++p) Sf[ct][p] = bS.ld128(frag_off(ct, p));
+
+  // ---- 1. dO and v tiles; gate cumsum within each 16-token block
+  {
+    const int odd = tid & 1;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r >= r16) dAT[j][r] = 0.f;
-      }
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4*>(&sm.dor[at(pt[h], 8 * po[h])]) = dog[h];
+      *reinterpret_cast<u32x4*>(&sm.vr[at(pt[h], 8 * po[h])]) = vg[h];
+      const u32 w0 = dog[h][0], w1 = dog[h][1], w2 = dog[h][2], w3 = dog[h][3];
+      const u32 r0 = dpp_swap1(odd ? w0 : w2), r1 = dpp_swap1(odd ? w1 : w3);
+      const u32 f0 = odd ? r0 : w0, f1 = odd ? r1 : w1;  // words of the even token
+      const u32 s0 = odd ? w2 : r0, s1 = odd ? w3 : r1;  // words of the odd token
+      const int j0 = 8 * po[h] + 4 * odd, tc = split_pos(pt[h] & ~1);
+      *reinterpret_cast<u32*>(&sm.doT[at(j0 + 0, tc)]) = lo2(f0, s0);
+      *reinterpret_cast<u32*>(&sm.doT[at(j0 + 1, tc)]) = hi2(f0, s0);
+      *reinterpret_cast<u32*>(&sm.doT[at(j0 + 2, tc)]) = lo2(f1, s1);
+      *reinterpret_cast<u32*>(&sm.doT[at(j0 + 3, tc)]) = hi2(f1, s1);
     }
   }
-  const int t = 16 * w + r16;
+  float b[4][4];
 #pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) {
-    f32x4 inter = {0.f, 0.f, 0.f, 0.f}, intra = {0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      mma(inter, ld8<T>(&sS[16 * ct + r16][32 * p + 8 * g]), ld8<T>(&sdo[16 * w + r16][32 * p + 8 * g]));
-    const int cl = 16 * ct + r16;  // A-fragment row (channel)
+    for (int r = 0; r < 4; ++r) b[ct][r] = f_at(la4[ct], r) * kLog2e;
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      if (2 * pp <= w) {
-        F af = ld4x2<T>(&kgT[cl][32 * pp + 4 * g]);
-        const float f0 = pair_factor(cr, w, 2 * pp, cl), f1 = pair_factor(cr, w, 2 * pp + 1, cl);
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          af[e] = to_t<T>(to_f(af[e]) * f0);
-          af[e + 4] = to_t<T>(to_f(af[e + 4]) * f1);
-        }
-        mma(intra, af, pack_acc<T>(dAT[2 * pp], dAT[2 * pp + 1]));
-      }
-    }
-    // lane holds rows c = 16ct + 4g + r of dq^T at column t
-    const int c0 = 16 * ct + 4 * g;
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[t][c0]);
-    const f32x4 R4 = *reinterpret_cast<const f32x4*>(&cr.R[w][c0]);
-    const f32x4 q4 = ld4f<T>(&sq[t][c0]);
-    const f32x4 k4 = ld4f<T>(&sk[t][c0]);
-    f32x4 dqv, db;
+    for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<1>(b[ct][r]);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<2>(b[ct][r]);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<4>(b[ct][r]);
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<8>(b[ct][r]);
+  if (r16 == 15)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      *reinterpret_cast<f32x4*>(&sm.tot[w][16 * ct + 4 * g]) = f32x4{b[ct][0], b[ct][1], b[ct][2], b[ct][3]};
+  lds_barrier();
+
+  // ---- 2. chunk-wide cumsum, references
+  float Rw[4][4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    f32x4 pre = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < w; ++j) pre += *reinterpret_cast<const f32x4*>(&sm.tot[j][16 * ct + 4 * g]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float off_diag = exp2_fast(b4[r] - R4[r]) * (exp2_fast(R4[r]) * inter[r] + intra[r]);
-      dqv[r] = off_diag + dAtt * k4[r];
-      db[r] = q4[r] * off_diag;
+      b[ct][r] += pre[r];
+      Rw[ct][r] = dpp_bcast<7>(b[ct][r]);
     }
-    if (t0 + t < T_len) st4<T>(dq + off + (size_t)(t0 + t) * kD + c0, dqv);
-    *reinterpret_cast<f32x4*>(&dbt[t][c0]) = db;
-  }
-  lds_barrier();
-  // ---- dlog_alpha, q side: in-chunk suffix sums plus the state term
-  {
-    float st = 0.f;
-    for (int j = 0; j < kD; ++j) st += to_f(sdS[c][j]) * to_f(sS[c][j]);
-    st *= exp2_fast(bt[kC - 1][c]);
-    float loc[16];
-    float run = 0.f;
-#pragma unroll
-    for (int rr = 15; rr >= 0; --rr) {
-      run += dbt[16 * qtr + rr][c];
-      loc[rr] = run;
-    }
-    tot[qtr][c] = run;
-    lds_barrier();
-    float post = st;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) post += (j > qtr) ? tot[j][c] : 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int tt = t0 + 16 * qtr + rr;
-      if (tt < T_len) dla[off + (size_t)tt * kD + c] = loc[rr] + post;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ 4. dk, dv
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gla_bwd_dkdv(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ la, const T* __restrict__ dO, const T* __restrict__ dS_all,
-    T* __restrict__ dk, T* __restrict__ dv, float* __restrict__ dla, int T_len) {
-  typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T sdo[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T dOT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T sv[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T qg[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T qgT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T kg[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T sk[kC][kDP];
-  __shared__ __attribute__((aligned(16))) T sdS[kD][kDP];
-  __shared__ __attribute__((aligned(16))) T dST[kD][kDP];
-  __shared__ __attribute__((aligned(16))) float bt[kC][kD + 4];
-  __shared__ __attribute__((aligned(16))) T sq[kC][kDP];
-  __shared__ __attribute__((aligned(16))) float dbs[kC][kD + 4];  // k dk^intra, t > s
-  __shared__ __attribute__((aligned(16))) float dbp[kC][kD + 4];  // k dk^inter
-  __shared__ __attribute__((aligned(16))) float tot[4][kD];
-  __shared__ __attribute__((aligned(16))) float tot2[4][kD];
-  __shared__ __attribute__((aligned(16))) float elR[4][kD];  // 2^{b_last - R_j}
-  __shared__ __attribute__((aligned(16))) ChunkRefs cr;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int r16 = lane & 15, g = lane >> 4;
-  const int c = tid % kD, qtr = tid / kD;
-  const int ch = blockIdx.x, bh = blockIdx.y;
-  const int nc = gridDim.x, t0 = ch * kC;
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
-  const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
-  const Buf bla(la + off, (u32)((size_t)T_len * kD * 4));
-  const Buf bdS(dS_all + ((size_t)bh * nc + ch) * kD * kD, (u32)(kD * kD * sizeof(T)));
-  stage_rows<T>(&sdo[0][0], kDP, bdo, t0, kD, kC, tid, kThreads);
-  stage_cols<T>(&dOT[0][0], kTP, bdo, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sv[0][0], kDP, bv, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&qg[0][0], kDP, bq, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sq[0][0], kDP, bq, t0, kD, kC, tid, kThreads);
-  stage_cols<T>(&qgT[0][0], kTP, bq, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&kg[0][0], kDP, bk, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sk[0][0], kDP, bk, t0, kD, kC, tid, kThreads);
-  stage_rows<T>(&sdS[0][0], kDP, bdS, 0, kD, kD, tid, kThreads);
-  stage_cols<T>(&dST[0][0], kDP, bdS, 0, kD, kD, tid, kThreads);
-  gate_table(bt, tot, bla, t0, tid);
-  lds_barrier();
-  {
-    const float Rq = bt[16 * qtr + 7][c];
-    const float blast = bt[kC - 1][c];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int t = 16 * qtr + rr;
-      const float d = bt[t][c] - Rq;
-      qg[t][c] = to_t<T>(to_f(qg[t][c]) * exp2_fast(d));
-      kg[t][c] = to_t<T>(to_f(kg[t][c]) * exp2_fast(-d));
-    }
-    scale_run16<T>(&qgT[c][16 * qtr], 1.f, &bt[16 * qtr][c], 1.f, Rq);
-    elR[qtr][c] = exp2_fast(blast - Rq);
-    chunk_refs(cr, bt, tid);
+    if (r16 == 7)
+      *reinterpret_cast<f32x4*>(&sm.R[w][16 * ct + 4 * g]) = f32x4{b[ct][0], b[ct][1], b[ct][2], b[ct][3]};
+    if (w == 3 && r16 == 15)
+      *reinterpret_cast<f32x4*>(&sm.bl[16 * ct + 4 * g]) = f32x4{b[ct][0], b[ct][1], b[ct][2], b[ct][3]};
   }
   lds_barrier();
 
-  const int w = wave;  // key block
-  f32x4 dA[4], Ab[4];  // [t = 16i + 4g + r][s = 16w + r16]; dA strictly t > s
-  float dAss = 0.f;    // diagonal dA[s][s] of this lane's key
+  // ---- 3. factor tables; gated q, k tiles (rows and transposes)
+  {
+    const int c = tid & 63, x = tid >> 6;
+    const float Rx = sm.R[x][c], blc = sm.bl[c];
+    sm.eR[x][c] = exp2_fast(Rx);
+    sm.elR[x][c] = exp2_fast(blc - Rx);
+    // pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): thread group x makes pairs x and x + 4
+    const int pi[6] = {1, 2, 2, 3, 3, 3}, pj[6] = {0, 0, 1, 0, 1, 2};
+    sm.vij[x][c] = exp2_fast(sm.R[pi[x]][c] - sm.R[pj[x]][c]);
+    if (x < 2) sm.vij[x + 4][c] = exp2_fast(sm.R[pi[x + 4]][c] - sm.R[pj[x + 4]][c]);
+  }
+  {
+    const int odd = r16 & 1, te = split_pos(t & ~1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Ab[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i >= w) {
+    for (int ct = 0; ct < 4; ++ct) {
+      const int c0 = 16 * ct + 4 * g;
+      const u32 qa = q2[ct][0], qb = q2[ct][1], ka = k2[ct][0], kb = k2[ct][1];
+      float fq[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        mma(dA[i], ld8<T>(&sdo[16 * i + r16][32 * p + 8 * g]), ld8<T>(&sv[16 * w + r16][32 * p + 8 * g]));
-        F af = ld8<T>(&qg[16 * i + r16][32 * p + 8 * g]);
-        if (i > w) {
-          const float* f = &cr.vij[pair_of(i, w)][32 * p + 8 * g];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) af[e] = to_t<T>(to_f(af[e]) * f[e]);
-        }
-        mma(Ab[i], af, ld8<T>(&kg[16 * w + r16][32 * p + 8 * g]));
-      }
-      if (i == w) {
-        dAss = __shfl(dA[i][r16 & 3], 16 * (r16 >> 2) + r16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (4 * g + r <= r16) dA[i][r] = 0.f;
-          if (4 * g + r < r16) Ab[i][r] = 0.f;
-        }
-      }
+      for (int r = 0; r < 4; ++r) fq[r] = b[ct][r] - Rw[ct][r];
+      const u32 Q0 = pack_bf2(bf_lo(qa) * exp2_fast(fq[0]), bf_hi(qa) * exp2_fast(fq[1]));
+      const u32 Q1 = pack_bf2(bf_lo(qb) * exp2_fast(fq[2]), bf_hi(qb) * exp2_fast(fq[3]));
+      const u32 K0 = pack_bf2(bf_lo(ka) * exp2_fast(-fq[0]), bf_hi(ka) * exp2_fast(-fq[1]));
+      const u32 K1 = pack_bf2(bf_lo(kb) * exp2_fast(-fq[2]), bf_hi(kb) * exp2_fast(-fq[3]));
+      *reinterpret_cast<u32x2*>(&sm.qg[at(t, c0)]) = u32x2{Q0, Q1};
+      *reinterpret_cast<u32x2*>(&sm.kg[at(t, c0)]) = u32x2{K0, K1};
+      // neighbouring lanes hold tokens t, t+1: the even lane writes channels
+      // c0, c0+1 and the odd lane c0+2, c0+3 as (token, token+1) pairs
+      const u32 rq = dpp_swap1(odd ? Q0 : Q1), rk = dpp_swap1(odd ? K0 : K1);
+      const u32 fQ = odd ? rq : Q0, sQ = odd ? Q1 : rq;
+      const u32 fK = odd ? rk : K0, sK = odd ? K1 : rk;
+      const int cp = c0 + 2 * odd;
+      *reinterpret_cast<u32*>(&sm.qgT[at(cp, te)]) = lo2(fQ, sQ);
+      *reinterpret_cast<u32*>(&sm.qgT[at(cp + 1, te)]) = hi2(fQ, sQ);
+      *reinterpret_cast<u32*>(&sm.kgT[at(cp, te)]) = lo2(fK, sK);
+      *reinterpret_cast<u32*>(&sm.kgT[at(cp + 1, te)]) = hi2(fK, sK);
     }
   }
-  const int s = 16 * w + r16;  // this lane's key (column of the accumulators)
-  // ---- dk^T[c][s]
+  // the dS_{c+1} fragments are needed only from the dk part on
 #pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) {
-    f32x4 intra = {0.f, 0.f, 0.f, 0.f}, inter = {0.f, 0.f, 0.f, 0.f};
-    const int cl = 16 * ct + r16;
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      if (2 * pp + 1 >= w) {
-        F af = ld4x2<T>(&qgT[cl][32 * pp + 4 * g]);
-        const float f0 = pair_factor(cr, 2 * pp, w, cl), f1 = pair_factor(cr, 2 * pp + 1, w, cl);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          af[e] = to_t<T>(to_f(af[e]) * f0);
-          af[e + 4] = to_t<T>(to_f(af[e + 4]) * f1);
-        }
-        mma(intra, af, pack_acc<T>(dA[2 * pp], dA[2 * pp + 1]));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      mma(inter, ld8<T>(&sdS[cl][32 * p + 8 * g]), ld8<T>(&sv[16 * w + r16][32 * p + 8 * g]));
-    const int c0 = 16 * ct + 4 * g;
-    const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[s][c0]);
-    const f32x4 R4 = *reinterpret_cast<const f32x4*>(&cr.R[w][c0]);
-    const f32x4 k4 = ld4f<T>(&sk[s][c0]);
-    const f32x4 q4 = ld4f<T>(&sq[s][c0]);
-    f32x4 dkv, bs, bp;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float bl = bt[kC - 1][c0 + r];
-      const float di = exp2_fast(R4[r] - b4[r]) * intra[r];
-      const float de = exp2_fast(bl - b4[r]) * inter[r];
-      dkv[r] = di + de + dAss * q4[r];
-      bs[r] = k4[r] * di;
-      bp[r] = k4[r] * de;
-    }
-    if (t0 + s < T_len) st4<T>(dk + off + (size_t)(t0 + s) * kD + c0, dkv);
-    *reinterpret_cast<f32x4*>(&dbs[s][c0]) = bs;
-    *reinterpret_cast<f32x4*>(&dbp[s][c0]) = bp;
-  }
-  // ---- dv^T[j][s]
-#pragma unroll
-  for (int jt = 0; jt < kD / 16; ++jt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int jl = 16 * jt + r16;
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
-      if (2 * pp + 1 >= w) mma(acc, ld4x2<T>(&dOT[jl][32 * pp + 4 * g]), pack_acc<T>(Ab[2 * pp], Ab[2 * pp + 1]));
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      F bf = ld8<T>(&kg[16 * w + r16][32 * p + 8 * g]);
-      const float* f = &elR[w][32 * p + 8 * g];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bf[e] = to_t<T>(to_f(bf[e]) * f[e]);
-      mma(acc, ld8<T>(&dST[jl][32 * p + 8 * g]), bf);
+      dSf[ct][p] = bdS.ld128(frag_off(ct, p));
+      dSTf[ct][p] = bdST.ld128(frag_off(ct, p));
     }
-    if (t0 + s < T_len) st4<T>(dv + off + (size_t)(t0 + s) * kD + 16 * jt + 4 * g, acc);
-  }
   lds_barrier();
-  // ---- dlog_alpha, k side: minus the suffix sums of dbs, plus the exclusive
-  // prefix sums of dbp, added to the q-side terms already in dlog_alpha
+
+  float X[4][4], Y[4][4];  // dlog_alpha items: suffix-summed X, prefix-summed Y
+  // ---- 4. dq: wave w is query block w
   {
-    float suf[16], pre[16];
-    float rs = 0.f, rp = 0.f;
+    bf16x8 dof[2];
 #pragma unroll
-    for (int rr = 15; rr >= 0; --rr) {
-      rs += dbs[16 * qtr + rr][c];
-      suf[rr] = rs;
-    }
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      pre[rr] = rp;
-      rp += dbp[16 * qtr + rr][c];
-    }
-    tot[qtr][c] = rs;
-    tot2[qtr][c] = rp;
-    lds_barrier();
-    float after = 0.f, before = 0.f;
+    for (int p = 0; p < 2; ++p) dof[p] = ld8<bf16>(&sm.dor[at(t, 32 * p + 8 * g)]);
+    f32x4 dAT[4];  // dA^T[s = 16j + 4g + r][t], strictly s < t
+    float dAtt = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      after += (j > qtr) ? tot[j][c] : 0.f;
-      before += (j < qtr) ? tot2[j][c] : 0.f;
-    }
+      dAT[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (j <= w) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int t = t0 + 16 * qtr + rr;
-      if (t < T_len) {
-        float* p = dla + off + (size_t)t * kD + c;
-        *p = *p - (suf[rr] + after) + (pre[rr] + before);
+        for (int p = 0; p < 2; ++p) mma(dAT[j], ld8<bf16>(&sm.vr[at(16 * j + r16, 32 * p + 8 * g)]), dof[p]);
+        if (j == w) {
+          dAtt = __shfl(dAT[j][r16 & 3], 16 * (r16 >> 2) + r16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * g + r >= r16) dAT[j][r] = 0.f;
+        }
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 inter = {0.f, 0.f, 0.f, 0.f}, intra = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) mma(inter, as_bf8(Sf[ct][p]), dof[p]);
+      const int cl = 16 * ct + r16;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        if (2 * pp <= w) {
+          bf16x8 af = ld8<bf16>(&sm.kgT[at(cl, 32 * pp + 8 * g)]);
+          const float f0 = pair_factor(sm, w, 2 * pp, cl), f1 = pair_factor(sm, w, 2 * pp + 1, cl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            af[e] = (bf16)((float)af[e] * f0);
+            af[e + 4] = (bf16)((float)af[e + 4] * f1);
+          }
+          mma(intra, af, pack_acc<bf16>(dAT[2 * pp], dAT[2 * pp + 1]));
+        }
+      }
+      const int c0 = 16 * ct + 4 * g;
+      const f32x4 eR4 = *reinterpret_cast<const f32x4*>(&sm.eR[w][c0]);
+      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.R[w][c0]);
+      const u32 qa = q2[ct][0], qb = q2[ct][1], ka = k2[ct][0], kb = k2[ct][1];
+      const float qv[4] = {bf_lo(qa), bf_hi(qa), bf_lo(qb), bf_hi(qb)};
+      const float kv[4] = {bf_lo(ka), bf_hi(ka), bf_lo(kb), bf_hi(kb)};
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float od = exp2_fast(b[ct][r] - R4[r]) * (eR4[r] * inter[r] + intra[r]);
+        o[r] = od + dAtt * kv[r];
+        X[ct][r] = qv[r] * od;
+      }
+      if (live)
+        *reinterpret_cast<u32x2*>(dq + off + rowe + c0) = u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+    }
+  }
+  // state term (wave 0; S_c is not needed after this)
+  if (w == 0) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      float pc = 0.f;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pc += bf_at(Sf[ct][p], e) * bf_at(dSf[ct][p], e);
+      pc += __shfl_xor(pc, 16);
+      pc += __shfl_xor(pc, 32);
+      if (g == 0) sm.st[16 * ct + r16] = pc * exp2_fast(sm.bl[16 * ct + r16]);
+    }
+  }
+  // ---- 5. dk, dv: wave w is key block w
+  {
+    bf16x8 vf[2], kf[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      vf[p] = ld8<bf16>(&sm.vr[at(t, 32 * p + 8 * g)]);
+      kf[p] = ld8<bf16>(&sm.kg[at(t, 32 * p + 8 * g)]);
+    }
+    f32x4 dA[4], Ab[4];  // [t = 16i + 4g + r][s]; dA strictly t > s, A with t >= s
+    float dAss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Ab[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i >= w) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          mma(dA[i], ld8<bf16>(&sm.dor[at(16 * i + r16, 32 * p + 8 * g)]), vf[p]);
+          bf16x8 af = ld8<bf16>(&sm.qg[at(16 * i + r16, 32 * p + 8 * g)]);
+          if (i > w) {
+            const float* f = &sm.vij[pair_of(i, w)][32 * p + 8 * g];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) af[e] = (bf16)((float)af[e] * f[e]);
+          }
+          mma(Ab[i], af, kf[p]);
+        }
+        if (i == w) {
+          dAss = __shfl(dA[i][r16 & 3], 16 * (r16 >> 2) + r16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (4 * g + r <= r16) dA[i][r] = 0.f;
+            if (4 * g + r < r16) Ab[i][r] = 0.f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 intra = {0.f, 0.f, 0.f, 0.f}, inter = {0.f, 0.f, 0.f, 0.f};
+      const int cl = 16 * ct + r16;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        if (2 * pp + 1 >= w) {
+          bf16x8 af = ld8<bf16>(&sm.qgT[at(cl, 32 * pp + 8 * g)]);
+          const float f0 = pair_factor(sm, 2 * pp, w, cl), f1 = pair_factor(sm, 2 * pp + 1, w, cl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            af[e] = (bf16)((float)af[e] * f0);
+            af[e + 4] = (bf16)((float)af[e + 4] * f1);
+          }
+          mma(intra, af, pack_acc<bf16>(dA[2 * pp], dA[2 * pp + 1]));
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) mma(inter, as_bf8(dSf[ct][p]), vf[p]);
+      const int c0 = 16 * ct + 4 * g;
+      const f32x4 bl4 = *reinterpret_cast<const f32x4*>(&sm.bl[c0]);
+      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.R[w][c0]);
+      const u32 qa = q2[ct][0], qb = q2[ct][1], ka = k2[ct][0], kb = k2[ct][1];
+      const float qv[4] = {bf_lo(qa), bf_hi(qa), bf_lo(qb), bf_hi(qb)};
+      const float kv[4] = {bf_lo(ka), bf_hi(ka), bf_lo(kb), bf_hi(kb)};
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float di = exp2_fast(R4[r] - b[ct][r]) * intra[r];
+        const float de = exp2_fast(bl4[r] - b[ct][r]) * inter[r];
+        o[r] = di + de + dAss * qv[r];
+        X[ct][r] -= kv[r] * di;
+        Y[ct][r] = kv[r] * de;
+      }
+      if (live)
+        *reinterpret_cast<u32x2*>(dk + off + rowe + c0) = u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+    }
+    // K^_s = k~_s 2^{b_last - R_w}
+    bf16x8 kh[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float* f = &sm.elR[w][32 * p + 8 * g];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kh[p][e] = (bf16)((float)kf[p][e] * f[e]);
+    }
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int jl = 16 * jt + r16;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        if (2 * pp + 1 >= w)
+          mma(acc, ld8<bf16>(&sm.doT[at(jl, 32 * pp + 8 * g)]), pack_acc<bf16>(Ab[2 * pp], Ab[2 * pp + 1]));
+#pragma unroll
+      for (int p = 0; p < 2; ++p) mma(acc, as_bf8(dSTf[jt][p]), kh[p]);
+      if (live)
+        *reinterpret_cast<u32x2*>(dv + off + rowe + 16 * jt + 4 * g) =
+            u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+    }
+  }
+  // ---- 6. dlog_alpha: suffix sums of X and exclusive prefix sums of Y over
+  // the chunk, plus the state term
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float xs = X[ct][r], yi = Y[ct][r];
+      xs += dpp_shl<1>(xs);
+      yi += dpp_shr<1>(yi);
+      xs += dpp_shl<2>(xs);
+      yi += dpp_shr<2>(yi);
+      xs += dpp_shl<4>(xs);
+      yi += dpp_shr<4>(yi);
+      xs += dpp_shl<8>(xs);
+      yi += dpp_shr<8>(yi);
+      X[ct][r] = xs;
+      Y[ct][r] = yi - Y[ct][r];  // exclusive
+      if (r16 == 0) sm.sx[w][16 * ct + 4 * g + r] = xs;
+      if (r16 == 15) sm.sy[w][16 * ct + 4 * g + r] = yi;
+    }
+  lds_barrier();
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c0 = 16 * ct + 4 * g;
+    f32x4 add = *reinterpret_cast<const f32x4*>(&sm.st[c0]);
+    for (int j = w + 1; j < 4; ++j) add += *reinterpret_cast<const f32x4*>(&sm.sx[j][c0]);
+    for (int j = 0; j < w; ++j) add += *reinterpret_cast<const f32x4*>(&sm.sy[j][c0]);
+    f32x4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = X[ct][r] + Y[ct][r] + add[r];
+    if (live) *reinterpret_cast<f32x4*>(dla + off + rowe + c0) = o;
   }
 }
 
@@ -514,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_dkdv(
 size_t gla_bwd_workspace_bytes(const Shape& s) {
   const size_t nc = (size_t)(s.T + kC - 1) / kC;
   const size_t bh = (size_t)s.B * s.H;
-  return 2 * bh * nc * kD * kD * sizeof(bf16);
+  return 3 * bh * nc * kD * kD * sizeof(bf16);
 }
 
 hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const void* v,
@@ -526,16 +622,14 @@ hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const vo
   if (nc == 0 || BH == 0) return hipSuccess;
   T* S_all = (T*)ws;
   T* dS_all = S_all + (size_t)BH * nc * kD * kD;
+  T* dST_all = dS_all + (size_t)BH * nc * kD * kD;
   hipLaunchKernelGGL(gla_bwd_state_scan<T>, dim3(BH), dim3(kThreads), 0, st, (const T*)k,
                      (const T*)v, la, h0, S_all, s.T);
   hipLaunchKernelGGL(gla_bwd_dstate_scan<T>, dim3(BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)dO, la, dS_all, s.T);
-  hipLaunchKernelGGL(gla_bwd_dq<T>, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q, (const T*)k,
-                     (const T*)v, la, (const T*)dO, (const T*)S_all, (const T*)dS_all, (T*)dq,
-                     dla, s.T);
-  hipLaunchKernelGGL(gla_bwd_dkdv<T>, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, (const T*)dS_all, (T*)dk, (T*)dv,
-                     dla, s.T);
+                     (const T*)dO, la, dS_all, dST_all, s.T);
+  hipLaunchKernelGGL(gla_bwd_chunk, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
+                     (const T*)k, (const T*)v, la, (const T*)dO, (const T*)S_all,
+                     (const T*)dS_all, (const T*)dST_all, (T*)dq, (T*)dk, (T*)dv, dla, s.T);
   return hipGetLastError();
 }
 
