@@ -21,12 +21,11 @@
 // is never formed).
 //
 // Kernels:
-//   1. state scan    (per head, forward)  S_c for every chunk  -> workspace
-//   2. dstate scan   (per head, reverse)  dS_{c+1} per chunk   -> workspace
-//   3. dq            (per head x chunk)   dq, and the q-side and state terms of
-//                                          dlog_alpha
-//   4. dk, dv        (per head x chunk)   dk, dv, and the k-side terms
-// Intra-chunk factors use the forward's 16-token sub-block midpoints R_i.
+//   1. scans (one launch): per head, the state scan forward writes S_c for every
+//      chunk and the reverse scan writes dS_{c+1} (and its transpose)
+//   2. per chunk: dq, dk, dv and dlog_alpha from the chunk's inputs and the two
+//      states of its boundaries
+// Intra-chunk factors use 16-token sub-block midpoints R_i as references.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,150 +34,12 @@ namespace {
 
 constexpr int kC = 64;
 constexpr int kD = 64;          // head size supported by the backward
-constexpr int kDP = kD + 8;     // padded row (elements)
-constexpr int kTP = kC + 8;     // padded token row
 constexpr int kThreads = 256;
+constexpr float kFastLog2 = 64.f;  // single-reference bound on the chunk decay (log2)
 
 __host__ __device__ constexpr int pair_of(int i, int j) { return i * (i - 1) / 2 + j; }
 
-// b[t][c] = log2-gate cumsum over rows 0..t of the chunk (rows past T add 0).
-// Thread (c, quarter) scans 16 rows; quarter totals are exchanged through tot.
-__device__ __forceinline__ void gate_table(float (*bt)[kD + 4], float (*tot)[kD], const Buf& bla,
-                                           int t0, int tid) {
-  const int c = tid % kD, qtr = tid / kD;
-  float loc[16];
-  float run = 0.f;
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const u32 off = (u32)(((t0 + 16 * qtr + rr) * kD + c) * 4);
-    run += __builtin_bit_cast(float, bla.ld32(off)) * kLog2e;
-    loc[rr] = run;
-  }
-  tot[qtr][c] = run;
-  lds_barrier();
-  float pre = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) pre += (j < qtr) ? tot[j][c] : 0.f;
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) bt[16 * qtr + rr][c] = loc[rr] + pre;
-}
-
-template <typename T>
-__device__ __forceinline__ void scale_run16(T* p, float f0, const float* bcol, float sgn,
-                                            float ref) {
-  // p[0..15] *= 2^{sgn * (b[t] - ref)} (b read with stride kD + 4)
-  typedef typename Frag<T>::type F;
-  F a = *reinterpret_cast<F*>(p), b = *reinterpret_cast<F*>(p + 8);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = to_t<T>(to_f(a[e]) * exp2_fast(sgn * (bcol[e * (kD + 4)] - ref)) * f0);
-    b[e] = to_t<T>(to_f(b[e]) * exp2_fast(sgn * (bcol[(e + 8) * (kD + 4)] - ref)) * f0);
-  }
-  *reinterpret_cast<F*>(p) = a;
-  *reinterpret_cast<F*>(p + 8) = b;
-}
-
-// ---------------------------------------------------------------- 1. states
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gla_bwd_state_scan(
-    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ la,
-    const float* __restrict__ h0, T* __restrict__ S_all, int T_len) {
-  typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) float bt[kC][kD + 4];
-  __shared__ __attribute__((aligned(16))) float tot[4][kD];
-  __shared__ __attribute__((aligned(16))) T khT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T vT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) float decay[kD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int r16 = lane & 15, g = lane >> 4;
-  const int c = tid % kD, qtr = tid / kD;
-  const int bh = blockIdx.x;
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
-  const Buf bk(k + off, nb), bv(v + off, nb), bla(la + off, (u32)((size_t)T_len * kD * 4));
-  const int nc = (T_len + kC - 1) / kC;
-  f32x4 S[kD / 16];
-#pragma unroll
-  for (int cb = 0; cb < kD / 16; ++cb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[cb][r] = h0 ? h0[(size_t)bh * kD * kD + (16 * cb + 4 * g + r) * kD + 16 * wave + r16] : 0.f;
-  for (int ch = 0; ch < nc; ++ch) {
-    T* dst = S_all + ((size_t)bh * nc + ch) * kD * kD;
-#pragma unroll
-    for (int cb = 0; cb < kD / 16; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * kD + 16 * wave + r16] = to_t<T>(S[cb][r]);
-    stage_cols<T>(&khT[0][0], kTP, bk, ch * kC, kD, kC, tid, kThreads);
-    stage_cols<T>(&vT[0][0], kTP, bv, ch * kC, kD, kC, tid, kThreads);
-    gate_table(bt, tot, bla, ch * kC, tid);
-    lds_barrier();
-    const float blast = bt[kC - 1][c];
-    scale_run16<T>(&khT[c][16 * qtr], 1.f, &bt[16 * qtr][c], -1.f, blast);
-    if (qtr == 0) decay[c] = exp2_fast(blast);
-    lds_barrier();
-#pragma unroll
-    for (int cb = 0; cb < kD / 16; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[cb][r] *= decay[16 * cb + 4 * g + r];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        mma(S[cb], ld8<T>(&khT[16 * cb + r16][32 * p + 8 * g]), ld8<T>(&vT[16 * wave + r16][32 * p + 8 * g]));
-    }
-    lds_barrier();
-  }
-}
-
-// --------------------------------------------------------------- 2. dstates
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gla_bwd_dstate_scan(
-    const T* __restrict__ q, const T* __restrict__ dO, const float* __restrict__ la,
-    T* __restrict__ dS_all, T* __restrict__ dST_all, int T_len) {
-  __shared__ __attribute__((aligned(16))) float bt[kC][kD + 4];
-  __shared__ __attribute__((aligned(16))) float tot[4][kD];
-  __shared__ __attribute__((aligned(16))) T qhT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T dOT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) float decay[kD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int r16 = lane & 15, g = lane >> 4;
-  const int c = tid % kD, qtr = tid / kD;
-  const int bh = blockIdx.x;
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
-  const Buf bq(q + off, nb), bdo(dO + off, nb), bla(la + off, (u32)((size_t)T_len * kD * 4));
-  const int nc = (T_len + kC - 1) / kC;
-  f32x4 dS[kD / 16];  // dS[16cb + 4g + r][16 wave + r16]
-#pragma unroll
-  for (int cb = 0; cb < kD / 16; ++cb) dS[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int ch = nc - 1; ch >= 0; --ch) {
-    T* dst = dS_all + ((size_t)bh * nc + ch) * kD * kD;
-    T* dstT = dST_all + ((size_t)bh * nc + ch) * kD * kD;
-#pragma unroll
-    for (int cb = 0; cb < kD / 16; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * kD + 16 * wave + r16] = to_t<T>(dS[cb][r]);
-      st4<T>(dstT + (16 * wave + r16) * kD + 16 * cb + 4 * g, dS[cb]);
-    }
-    stage_cols<T>(&qhT[0][0], kTP, bq, ch * kC, kD, kC, tid, kThreads);
-    stage_cols<T>(&dOT[0][0], kTP, bdo, ch * kC, kD, kC, tid, kThreads);
-    gate_table(bt, tot, bla, ch * kC, tid);
-    lds_barrier();
-    scale_run16<T>(&qhT[c][16 * qtr], 1.f, &bt[16 * qtr][c], 1.f, 0.f);
-    if (qtr == 0) decay[c] = exp2_fast(bt[kC - 1][c]);
-    lds_barrier();
-#pragma unroll
-    for (int cb = 0; cb < kD / 16; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dS[cb][r] *= decay[16 * cb + 4 * g + r];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        mma(dS[cb], ld8<T>(&qhT[16 * cb + r16][32 * p + 8 * g]), ld8<T>(&dOT[16 * wave + r16][32 * p + 8 * g]));
-    }
-    lds_barrier();
-  }
-}
-
-// ------------------------------------------------------- 3. per-chunk grads
+// ------------------------------------------------------------------ helpers
 // DPP moves within rows of 16 lanes (zero where the source leaves the row).
 template <int N>
 __device__ __forceinline__ float dpp_shr(float x) {  // lane i <- lane i - N
@@ -209,6 +70,188 @@ constexpr int kTile = kC * kD;
 // element offset of (row, col) in a swizzled 64 x 64 bf16 tile
 __device__ __forceinline__ int at(int row, int col) { return swz_at<8>(row, col); }
 
+
+// Fragment-major layout of the per-chunk states in the workspace: the 16-byte
+// fragment (rows 16a + r, columns 32p + 8g..8g+7) of lane 16g + r sits at
+// element ((2a + p) * 64 + 16g + r) * 8, so a wave reads one as 1 KiB in a row.
+__device__ __forceinline__ int frag_major(int row, int col) {
+  return (((row >> 4) * 2 + (col >> 5)) * 64 + ((col >> 3) & 3) * 16 + (row & 15)) * 8 + (col & 7);
+}
+
+// -------------------------------------------------------------- 1-2. scans
+// Work-groups 0..BH-1 run the state scan of one head forward (writing S_c, the
+// state entering chunk c); work-groups BH..2BH-1 run the reverse scan (writing
+// dS_{c+1} and its transpose, the state gradient leaving chunk c):
+//   S_{c+1} = D_c S_c + K^_c^T V_c,   dS_c = D_c dS_{c+1} + Q^_c^T dO_c,
+// D_c = diag(2^{b_last}), K^_s = k_s 2^{b_last - b_s}, Q^_t = q_t 2^{b_t}.
+// The next chunk's inputs are loaded while this one is processed; lane (r16, g)
+// of wave w owns token 16w + r16, channels 16ct + 4g + r, as in the grad kernel.
+struct ScanSmem {
+  bf16 xT[2][kTile];  // gated k (or q) transposed [c][t]
+  bf16 yT[2][kTile];  // v (or dO) transposed [j][t]
+  float tot[2][4][kD];
+};
+
+__global__ __launch_bounds__(kThreads) void gla_bwd_scans(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
+    bf16* __restrict__ S_all, bf16* __restrict__ dS_all, bf16* __restrict__ dST_all, int BH,
+    int T_len) {
+  __shared__ __attribute__((aligned(16))) ScanSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool rev = (int)blockIdx.x >= BH;
+  const int bh = rev ? blockIdx.x - BH : blockIdx.x;
+  const size_t off = (size_t)bh * T_len * kD;
+  const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
+  const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb), bla(la + off, 2 * nb);
+  const int nc = (T_len + kC - 1) / kC;
+  const int t = 16 * w + r16;
+
+  // a1[jb]: [j = 16jb + 4g + r][c = 16w + r16] (state transposed); a2[jb] (reverse
+  // scan only): [c = 16w + 4g + r][j = 16jb + r16]
+  f32x4 a1[4], a2[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a2[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (!rev && h0) {
+    const float* hp = h0 + (size_t)bh * kD * kD + (size_t)t * kD + 4 * g;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) a1[jb] = *reinterpret_cast<const f32x4*>(hp + 16 * jb);
+  }
+  // Two input sets, each reloaded (two chunks ahead) right after its last use,
+  // so no in-flight load is carried across the loop's back edge.
+  struct In {
+    u32x4 la[4];
+    u32x2 x[4], y[4];
+  };
+  auto load = [&](In& d, int ch) {
+    const u32 rowe = (u32)(ch * kC + t) * kD;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const u32 e = rowe + 16 * ct + 4 * g;
+      d.la[ct] = bla.ld128(e * 4);
+      d.x[ct] = ld64v(bx, e * 2);
+      d.y[ct] = ld64v(by, e * 2);
+    }
+  };
+  const int odd = r16 & 1, te = t & ~1;
+  auto chunk_at = [&](int n) { return rev ? nc - 1 - n : n; };
+  auto step = [&](In& d, int n) {
+    const int ch = chunk_at(n), buf = n & 1;
+    // the state at the chunk boundary, before this chunk's update
+    {
+      const size_t so = ((size_t)bh * nc + ch) * kTile;
+      bf16* dst = (rev ? dS_all : S_all) + so;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        *reinterpret_cast<u32x2*>(dst + frag_major(t, 16 * jb + 4 * g)) =
+            u32x2{pack_bf2(a1[jb][0], a1[jb][1]), pack_bf2(a1[jb][2], a1[jb][3])};
+      if (rev)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+          *reinterpret_cast<u32x2*>(dST_all + so + frag_major(16 * jb + r16, 16 * w + 4 * g)) =
+              u32x2{pack_bf2(a2[jb][0], a2[jb][1]), pack_bf2(a2[jb][2], a2[jb][3])};
+    }
+    // gate cumsum within the 16-token block, then across blocks
+    float b[4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[ct][r] = f_at(d.la[ct], r) * kLog2e;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<1>(b[ct][r]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<2>(b[ct][r]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<4>(b[ct][r]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<8>(b[ct][r]);
+    if (r16 == 15)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        *reinterpret_cast<f32x4*>(&sm.tot[buf][w][16 * ct + 4 * g]) =
+            f32x4{b[ct][0], b[ct][1], b[ct][2], b[ct][3]};
+    lds_barrier();
+    // gated x and raw y, transposed: the even lane of a token pair writes
+    // channels c0, c0+1 and the odd lane c0+2, c0+3
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int c0 = 16 * ct + 4 * g;
+      f32x4 pre = {0.f, 0.f, 0.f, 0.f}, bl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 tj = *reinterpret_cast<const f32x4*>(&sm.tot[buf][j][c0]);
+        bl += tj;
+        if (j < w) pre += tj;
+      }
+      float f[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float bb = b[ct][r] + pre[r];
+        f[r] = exp2_fast(rev ? bb : bl[r] - bb);
+      }
+      const u32 xa = d.x[ct][0], xb = d.x[ct][1];
+      const u32 X0 = pack_bf2(bf_lo(xa) * f[0], bf_hi(xa) * f[1]);
+      const u32 X1 = pack_bf2(bf_lo(xb) * f[2], bf_hi(xb) * f[3]);
+      const u32 Y0 = d.y[ct][0], Y1 = d.y[ct][1];
+      const u32 rx = dpp_swap1(odd ? X0 : X1), ry = dpp_swap1(odd ? Y0 : Y1);
+      const u32 fX = odd ? rx : X0, sX = odd ? X1 : rx;
+      const u32 fY = odd ? ry : Y0, sY = odd ? Y1 : ry;
+      const int cp = c0 + 2 * odd;
+      *reinterpret_cast<u32*>(&sm.xT[buf][at(cp, te)]) = lo2(fX, sX);
+      *reinterpret_cast<u32*>(&sm.xT[buf][at(cp + 1, te)]) = hi2(fX, sX);
+      *reinterpret_cast<u32*>(&sm.yT[buf][at(cp, te)]) = lo2(fY, sY);
+      *reinterpret_cast<u32*>(&sm.yT[buf][at(cp + 1, te)]) = hi2(fY, sY);
+    }
+    if (n + 2 < nc) load(d, chunk_at(n + 2));
+    lds_barrier();
+    // decay, then add this chunk's outer products
+    float d1 = 0.f;
+    f32x4 d2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d1 += sm.tot[buf][j][t];
+      if (rev) d2 += *reinterpret_cast<const f32x4*>(&sm.tot[buf][j][16 * w + 4 * g]);
+    }
+    d1 = exp2_fast(d1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d2[r] = exp2_fast(d2[r]);
+    bf16x8 xf[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) xf[p] = ld8<bf16>(&sm.xT[buf][at(t, 32 * p + 8 * g)]);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      a1[jb] *= d1;
+      if (rev) a2[jb] *= d2;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const bf16x8 yf = ld8<bf16>(&sm.yT[buf][at(16 * jb + r16, 32 * p + 8 * g)]);
+        mma(a1[jb], yf, xf[p]);
+        if (rev) mma(a2[jb], xf[p], yf);
+      }
+    }
+  };
+  In A, B;
+  load(A, chunk_at(0));
+  if (nc > 1) load(B, chunk_at(1));
+  for (int n = 0; n < nc; n += 2) {
+    step(A, n);
+    if (n + 1 < nc) step(B, n + 1);
+  }
+}
+
+// ------------------------------------------------------- 2. per-chunk grads
 struct BwdSmem {
   bf16 qg[kTile];   // q~ rows [t][c] = q_t 2^{b_t - R_i}, i = block of t
   bf16 kg[kTile];   // k~ rows [s][c] = k_s 2^{R_j - b_s}, j = block of s
@@ -218,7 +261,8 @@ struct BwdSmem {
   bf16 doT[kTile];  // dO transposed [j][split_pos(t)]
   bf16 vr[kTile];   // v rows [s][j]
   float tot[4][kD];  // per-block gate totals
-  float R[4][kD];    // sub-block references R_i = b[16i + 7]
+  float R[4][kD];    // sub-block midpoints b[16i + 7]
+  float Ru[4][kD];   // references in use: the midpoints, or 0 on the single-reference path
   float bl[kD];      // chunk total b_last
   float eR[4][kD];   // 2^{R_i}
   float elR[4][kD];  // 2^{b_last - R_i}
@@ -284,8 +328,8 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     dog[h] = bdo.ld128(e * 2);
     vg[h] = bv.ld128(e * 2);
   }
-  // state fragments: rows 16ct + r16, columns 32p + 8g..
-  auto frag_off = [&](int ct, int p) { return (u32)((16 * ct + r16) * kD + 32 * p + 8 * g) * 2; };
+  // state fragments (fragment-major): rows 16ct + r16, columns 32p + 8g..
+  auto frag_off = [&](int ct, int p) { return (u32)(((2 * ct + p) * 64 + lane) * 16); };
   u32x4 Sf[4][2], dSf[4][2], dSTf[4][2];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
@@ -356,15 +400,27 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   lds_barrier();
 
   // ---- 3. factor tables; gated q, k tiles (rows and transposes)
+  // A chunk whose decay 2^{b_last} stays above 2^-kFastLog2 in every channel
+  // uses one reference, the chunk start (R_i = 0): k~ grows by at most
+  // 2^kFastLog2, far inside bf16 range, and no pair factors are needed.  Every
+  // wave tests the same 64 values, so the choice is uniform over the group.
+  const bool fast = !__any(sm.bl[lane] < -kFastLog2);
+  if (fast) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Rw[ct][r] = 0.f;
+  }
   {
     const int c = tid & 63, x = tid >> 6;
-    const float Rx = sm.R[x][c], blc = sm.bl[c];
+    const float Rx = fast ? 0.f : sm.R[x][c], blc = sm.bl[c];
+    sm.Ru[x][c] = Rx;
     sm.eR[x][c] = exp2_fast(Rx);
     sm.elR[x][c] = exp2_fast(blc - Rx);
     // pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): thread group x makes pairs x and x + 4
     const int pi[6] = {1, 2, 2, 3, 3, 3}, pj[6] = {0, 0, 1, 0, 1, 2};
-    sm.vij[x][c] = exp2_fast(sm.R[pi[x]][c] - sm.R[pj[x]][c]);
-    if (x < 2) sm.vij[x + 4][c] = exp2_fast(sm.R[pi[x + 4]][c] - sm.R[pj[x + 4]][c]);
+    sm.vij[x][c] = fast ? 1.f : exp2_fast(sm.R[pi[x]][c] - sm.R[pj[x]][c]);
+    if (x < 2) sm.vij[x + 4][c] = fast ? 1.f : exp2_fast(sm.R[pi[x + 4]][c] - sm.R[pj[x + 4]][c]);
   }
   {
     const int odd = r16 & 1, te = split_pos(t & ~1);
@@ -435,18 +491,20 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
       for (int pp = 0; pp < 2; ++pp) {
         if (2 * pp <= w) {
           bf16x8 af = ld8<bf16>(&sm.kgT[at(cl, 32 * pp + 8 * g)]);
-          const float f0 = pair_factor(sm, w, 2 * pp, cl), f1 = pair_factor(sm, w, 2 * pp + 1, cl);
+          if (!fast) {
+            const float f0 = pair_factor(sm, w, 2 * pp, cl), f1 = pair_factor(sm, w, 2 * pp + 1, cl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            af[e] = (bf16)((float)af[e] * f0);
-            af[e + 4] = (bf16)((float)af[e + 4] * f1);
+            for (int e = 0; e < 4; ++e) {
+              af[e] = (bf16)((float)af[e] * f0);
+              af[e + 4] = (bf16)((float)af[e + 4] * f1);
+            }
           }
           mma(intra, af, pack_acc<bf16>(dAT[2 * pp], dAT[2 * pp + 1]));
         }
       }
       const int c0 = 16 * ct + 4 * g;
       const f32x4 eR4 = *reinterpret_cast<const f32x4*>(&sm.eR[w][c0]);
-      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.R[w][c0]);
+      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.Ru[w][c0]);
       const u32 qa = q2[ct][0], qb = q2[ct][1], ka = k2[ct][0], kb = k2[ct][1];
       const float qv[4] = {bf_lo(qa), bf_hi(qa), bf_lo(qb), bf_hi(qb)};
       const float kv[4] = {bf_lo(ka), bf_hi(ka), bf_lo(kb), bf_hi(kb)};
@@ -494,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
         for (int p = 0; p < 2; ++p) {
           mma(dA[i], ld8<bf16>(&sm.dor[at(16 * i + r16, 32 * p + 8 * g)]), vf[p]);
           bf16x8 af = ld8<bf16>(&sm.qg[at(16 * i + r16, 32 * p + 8 * g)]);
-          if (i > w) {
+          if (i > w && !fast) {
             const float* f = &sm.vij[pair_of(i, w)][32 * p + 8 * g];
 #pragma unroll
             for (int e = 0; e < 8; ++e) af[e] = (bf16)((float)af[e] * f[e]);
@@ -519,11 +577,13 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
       for (int pp = 0; pp < 2; ++pp) {
         if (2 * pp + 1 >= w) {
           bf16x8 af = ld8<bf16>(&sm.qgT[at(cl, 32 * pp + 8 * g)]);
-          const float f0 = pair_factor(sm, 2 * pp, w, cl), f1 = pair_factor(sm, 2 * pp + 1, w, cl);
+          if (!fast) {
+            const float f0 = pair_factor(sm, 2 * pp, w, cl), f1 = pair_factor(sm, 2 * pp + 1, w, cl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            af[e] = (bf16)((float)af[e] * f0);
-            af[e + 4] = (bf16)((float)af[e + 4] * f1);
+            for (int e = 0; e < 4; ++e) {
+              af[e] = (bf16)((float)af[e] * f0);
+              af[e + 4] = (bf16)((float)af[e + 4] * f1);
+            }
           }
           mma(intra, af, pack_acc<bf16>(dA[2 * pp], dA[2 * pp + 1]));
         }
@@ -532,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
       for (int p = 0; p < 2; ++p) mma(inter, as_bf8(dSf[ct][p]), vf[p]);
       const int c0 = 16 * ct + 4 * g;
       const f32x4 bl4 = *reinterpret_cast<const f32x4*>(&sm.bl[c0]);
-      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.R[w][c0]);
+      const f32x4 R4 = *reinterpret_cast<const f32x4*>(&sm.Ru[w][c0]);
       const u32 qa = q2[ct][0], qb = q2[ct][1], ka = k2[ct][0], kb = k2[ct][1];
       const float qv[4] = {bf_lo(qa), bf_hi(qa), bf_lo(qb), bf_hi(qb)};
       const float kv[4] = {bf_lo(ka), bf_hi(ka), bf_lo(kb), bf_hi(kb)};
@@ -623,10 +683,9 @@ hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const vo
   T* S_all = (T*)ws;
   T* dS_all = S_all + (size_t)BH * nc * kD * kD;
   T* dST_all = dS_all + (size_t)BH * nc * kD * kD;
-  hipLaunchKernelGGL(gla_bwd_state_scan<T>, dim3(BH), dim3(kThreads), 0, st, (const T*)k,
-                     (const T*)v, la, h0, S_all, s.T);
-  hipLaunchKernelGGL(gla_bwd_dstate_scan<T>, dim3(BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)dO, la, dS_all, dST_all, s.T);
+  hipLaunchKernelGGL(gla_bwd_scans, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
+                     (const T*)k, (const T*)v, la, (const T*)dO, h0, S_all, dS_all, dST_all, BH,
+                     s.T);
   hipLaunchKernelGGL(gla_bwd_chunk, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, la, (const T*)dO, (const T*)S_all,
                      (const T*)dS_all, (const T*)dST_all, (T*)dq, (T*)dk, (T*)dv, dla, s.T);

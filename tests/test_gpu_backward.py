@@ -41,11 +41,19 @@ def ref_grads(inp, w, s, mix, h0=None):
                                   h0=None if h0 is None else h0.double().numpy())
 
 
-def check(B, H, T, w, M, seed=0, mix=1.0, gate_mean=2.0, with_h0=False):
+def check(B, H, T, w, M, seed=0, mix=1.0, gate_mean=2.0, with_h0=False, steep_chunks=False):
     d = 64
-    print(f"[case] bwd B{B} H{H} T{T} w{w} M{M} mix{mix} gate{gate_mean} h0{with_h0}", flush=True)
+    print(f"[case] bwd B{B} H{H} T{T} w{w} M{M} mix{mix} gate{gate_mean} h0{with_h0} "
+          f"steep{steep_chunks}", flush=True)
     inp = make_inputs(B, H, T, d, d, M, dtype="bf16", seed=seed, gate_mean=gate_mean,
                       with_grad_out=True, with_h0=with_h0)
+    if steep_chunks:
+        # every third 64-token chunk decays 8x faster (about -94 per chunk in
+        # natural log): chunks on both sides of the single-reference bound
+        la = inp["log_alpha"].clone()
+        for c0 in range(64, T, 192):
+            la[:, :, c0:c0 + 64] *= 8.0
+        inp["log_alpha"] = la
     h0 = inp.pop("h0", None)
     s = 1.0 / math.sqrt(d)
     g = run_grads(inp, w, s, mix, h0)
@@ -68,6 +76,11 @@ def test_backward_h0_and_mix():
 
 def test_backward_extreme_gates():
     check(1, 2, 192, 64, 4, seed=4, gate_mean=-3.0)
+
+
+def test_backward_mixed_gate_ranges():
+    check(2, 2, 450, 64, 4, seed=5, steep_chunks=True)
+    check(1, 2, 320, 100, 4, seed=6, gate_mean=0.3, with_h0=True)
 
 
 def test_backward_deterministic():
