@@ -277,8 +277,8 @@ __device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, in
   return i > j ? sm.vij[pair_of(i, j)][c] : (i == j ? 1.f : 0.f);
 }
 
-// One work-group per (chunk, head): dq, dk, dv and dlog_alpha of the GLA
-// branch, from the chunk's inputs and the states S_c, dS_{c+1} (and dS_{c+1}^T)
+// One work-group per (chunk, head): dq, dk, dv (added to what dq, dk, dv hold)
+// and dlog_alpha of the GLA branch, from the chunk's inputs and the states S_c, dS_{c+1} (and dS_{c+1}^T)
 // written by the two scans.  Wave w owns token block w in both roles (query for
 // dq, key for dk and dv), so the work of the two halves balances.  Lane
 // (r16, g) owns token t = 16w + r16 and channels 16ct + 4g + r (ct, r < 4):
@@ -460,8 +460,13 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   lds_barrier();
 
   float X[4][4], Y[4][4];  // dlog_alpha items: suffix-summed X, prefix-summed Y
+  // the window branch's gradients, to which this branch's are added
+  const Buf bgq(dq + off, nb), bgk(dk + off, nb), bgv(dv + off, nb);
   // ---- 4. dq: wave w is query block w
   {
+    u32x2 dqw[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) dqw[ct] = ld64v(bgq, (rowe + 16 * ct + 4 * g) * 2);
     bf16x8 dof[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) dof[p] = ld8<bf16>(&sm.dor[at(t, 32 * p + 8 * g)]);
@@ -515,8 +520,12 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
         o[r] = od + dAtt * kv[r];
         X[ct][r] = qv[r] * od;
       }
-      if (live)
-        *reinterpret_cast<u32x2*>(dq + off + rowe + c0) = u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+      if (live) {
+        const u32x2 prev = dqw[ct];
+        const u32 pa = prev[0], pb = prev[1];
+        *reinterpret_cast<u32x2*>(dq + off + rowe + c0) =
+            u32x2{pack_bf2(o[0] + bf_lo(pa), o[1] + bf_hi(pa)), pack_bf2(o[2] + bf_lo(pb), o[3] + bf_hi(pb))};
+      }
     }
   }
   // state term (wave 0; S_c is not needed after this)
@@ -535,6 +544,12 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   }
   // ---- 5. dk, dv: wave w is key block w
   {
+    u32x2 dkw[4], dvw[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      dkw[ct] = ld64v(bgk, (rowe + 16 * ct + 4 * g) * 2);
+      dvw[ct] = ld64v(bgv, (rowe + 16 * ct + 4 * g) * 2);
+    }
     bf16x8 vf[2], kf[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -605,8 +620,12 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
         X[ct][r] -= kv[r] * di;
         Y[ct][r] = kv[r] * de;
       }
-      if (live)
-        *reinterpret_cast<u32x2*>(dk + off + rowe + c0) = u32x2{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+      if (live) {
+        const u32x2 prev = dkw[ct];
+        const u32 pa = prev[0], pb = prev[1];
+        *reinterpret_cast<u32x2*>(dk + off + rowe + c0) =
+            u32x2{pack_bf2(o[0] + bf_lo(pa), o[1] + bf_hi(pa)), pack_bf2(o[2] + bf_lo(pb), o[3] + bf_hi(pb))};
+      }
     }
     // K^_s = k~_s 2^{b_last - R_w}
     bf16x8 kh[2];
@@ -626,9 +645,13 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
           mma(acc, ld8<bf16>(&sm.doT[at(jl, 32 * pp + 8 * g)]), pack_acc<bf16>(Ab[2 * pp], Ab[2 * pp + 1]));
 #pragma unroll
       for (int p = 0; p < 2; ++p) mma(acc, as_bf8(dSTf[jt][p]), kh[p]);
-      if (live)
+      if (live) {
+        const u32x2 prev = dvw[jt];
+        const u32 pa = prev[0], pb = prev[1];
         *reinterpret_cast<u32x2*>(dv + off + rowe + 16 * jt + 4 * g) =
-            u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+            u32x2{pack_bf2(acc[0] + bf_lo(pa), acc[1] + bf_hi(pa)),
+                  pack_bf2(acc[2] + bf_lo(pb), acc[3] + bf_hi(pb))};
+      }
     }
   }
   // ---- 6. dlog_alpha: suffix sums of X and exclusive prefix sums of Y over

@@ -1,5 +1,5 @@
-// Hybrid backward orchestration: GLA branch then window branch, both adding
-// into the same dq, dk, dv (the window kernels read-modify-write them).
+// Hybrid backward orchestration: the window branch writes dq, dk, dv, then the
+// GLA branch adds its gradients to them (read-modify-write in its grad kernel).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,10 +46,10 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
     return hipGetLastError();
   }
   char* w = (char*)ws;
-  hipError_t e = launch_gla_bwd(s, q, k, v, la, h0, dO, dq, dk, dv, dla, w, st);
+  hipError_t e = launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
+                                w + align256(gla_bwd_workspace_bytes(s)), st);
   if (e != hipSuccess) return e;
-  return launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
-                        w + align256(gla_bwd_workspace_bytes(s)), st);
+  return launch_gla_bwd(s, q, k, v, la, h0, dO, dq, dk, dv, dla, w, st);
 }
 
 }  // namespace lz

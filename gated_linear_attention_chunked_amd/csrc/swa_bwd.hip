@@ -10,9 +10,10 @@
 // tile, so nothing of size T x T is ever formed.
 //
 // Kernels (deterministic, no float atomics):
-//   1. dq   per (head, 64-query tile): D_t, dq (added in place), and the tile's
-//           meta-gradient partial sums
-//   2. dkdv per (head, 64-key tile):   dk, dv (added in place)
+//   1. dq   per (head, 64-query tile): D_t, dq, and the tile's meta-gradient
+//           partial sums
+//   2. dkdv per (head, 64-key tile):   dk, dv
+// This branch runs first and writes dq, dk, dv; the GLA branch adds to them.
 //   3. meta reduction per head over (batch, tile) in a fixed order
 #include "common.hpp"
 #include "kernels.hpp"
@@ -208,13 +209,11 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
       }
     }
   }
-  // ---- dq[t][c] += scale * dq^T[c][t]
+  // ---- dq[t][c] = scale * dq^T[c][t]
   if (tq < T_len) {
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      T* ptr = dq + off + (size_t)tq * kD + 16 * ct + 4 * g;
-      st4<T>(ptr, ld4f<T>(ptr) + dqT[ct] * scale);
-    }
+    for (int ct = 0; ct < kD / 16; ++ct)
+      st4<T>(dq + off + (size_t)tq * kD + 16 * ct + 4 * g, dqT[ct] * scale);
   }
 }
 
@@ -310,10 +309,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
   if (sk < T_len) {
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct) {
-      T* pk = dk + off + (size_t)sk * kD + 16 * ct + 4 * g;
-      T* pv = dv + off + (size_t)sk * kD + 16 * ct + 4 * g;
-      st4<T>(pk, ld4f<T>(pk) + dkT[ct] * scale);
-      st4<T>(pv, ld4f<T>(pv) + dvT[ct] * mix);
+      st4<T>(dk + off + (size_t)sk * kD + 16 * ct + 4 * g, dkT[ct] * scale);
+      st4<T>(dv + off + (size_t)sk * kD + 16 * ct + 4 * g, dvT[ct] * mix);
     }
   }
 }
