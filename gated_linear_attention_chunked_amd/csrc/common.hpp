@@ -214,11 +214,46 @@ template <int GR>
 __device__ __forceinline__ int swz_at(int row, int col) {
   return row * (8 * GR) + swz_gran<GR>(row, col >> 3) * 8 + (col & 7);
 }
+// Tile with 64-element rows whose granules are permuted by (row >> 1) & 7.  A
+// fragment read (rows 16a..16a+15, one granule column) touches 16 distinct
+// bank groups, and the permutation does not depend on a, so a lane's offset
+// for rows 16a + r is 1024 a plus a per-lane base (an instruction immediate).
+__device__ __forceinline__ int swz64(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ (row >> 1)) & 7) << 3) + (col & 7);
+}
 // Position of element c of a 32-element group in "split" order: quads
 // 4g..4g+3 and 16+4g..16+4g+3 sit next to each other, so the granule at
 // position 8g holds exactly lane group g's split-map fragment.
 __host__ __device__ constexpr int split_pos(int c) {
   return (c & ~31) | (((c & 15) >> 2) << 3) | ((c & 16) >> 2) | (c & 3);
+}
+
+// ---- lane exchange and packing
+// DPP moves within rows of 16 lanes (zero where the source leaves the row).
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {  // lane i <- lane i - N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_shl(float x) {  // lane i <- lane i + N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
+}
+template <int N>
+__device__ __forceinline__ float dpp_bcast(float x) {  // every lane <- lane N of its row
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ u32 dpp_swap1(u32 x) {  // exchange with the neighbouring lane
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);
+}
+// bf16 pairs: low halves of (a, b), high halves of (a, b)
+__device__ __forceinline__ u32 lo2(u32 a, u32 b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ u32 hi2(u32 a, u32 b) { return (a >> 16) | (b & 0xffff0000u); }
+__device__ __forceinline__ bf16x8 as_bf8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
+
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+// 8 bytes through a buffer view (elements read out as with Buf::ld128)
+__device__ __forceinline__ u32x2 ld64v(const Buf& b, u32 off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
 }
 
 __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value

@@ -39,33 +39,6 @@ constexpr float kFastLog2 = 64.f;  // single-reference bound on the chunk decay 
 
 __host__ __device__ constexpr int pair_of(int i, int j) { return i * (i - 1) / 2 + j; }
 
-// ------------------------------------------------------------------ helpers
-// DPP moves within rows of 16 lanes (zero where the source leaves the row).
-template <int N>
-__device__ __forceinline__ float dpp_shr(float x) {  // lane i <- lane i - N
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xf, 0xf, true));
-}
-template <int N>
-__device__ __forceinline__ float dpp_shl(float x) {  // lane i <- lane i + N
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xf, 0xf, true));
-}
-template <int N>
-__device__ __forceinline__ float dpp_bcast(float x) {  // every lane <- lane N of its row
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
-}
-__device__ __forceinline__ u32 dpp_swap1(u32 x) {  // exchange with the neighbouring lane
-  return (u32)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);
-}
-// bf16 pairs: low halves of (a, b), high halves of (a, b)
-__device__ __forceinline__ u32 lo2(u32 a, u32 b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ u32 hi2(u32 a, u32 b) { return (a >> 16) | (b & 0xffff0000u); }
-__device__ __forceinline__ bf16x8 as_bf8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
-
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x2 ld64v(const Buf& b, u32 off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
-}
-
 constexpr int kTile = kC * kD;
 // element offset of (row, col) in a swizzled 64 x 64 bf16 tile
 __device__ __forceinline__ int at(int row, int col) { return swz_at<8>(row, col); }
@@ -696,9 +669,10 @@ size_t gla_bwd_workspace_bytes(const Shape& s) {
   return 3 * bh * nc * kD * kD * sizeof(bf16);
 }
 
-hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const void* v,
-                          const float* la, const float* h0, const void* dO, void* dq, void* dk,
-                          void* dv, float* dla, void* ws, hipStream_t st) {
+// Scans: S_c and dS_{c+1} (and its transpose) for every chunk, into ws.
+hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
+                                const float* la, const float* h0, const void* dO, void* ws,
+                                hipStream_t st) {
   typedef bf16 T;
   const int nc = (s.T + kC - 1) / kC;
   const int BH = s.B * s.H;
@@ -709,9 +683,23 @@ hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const vo
   hipLaunchKernelGGL(gla_bwd_scans, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, la, (const T*)dO, h0, S_all, dS_all, dST_all, BH,
                      s.T);
+  return hipGetLastError();
+}
+
+// Per-chunk gradients from the scans' states; adds into dq, dk, dv.
+hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
+                                const float* la, const void* dO, void* dq, void* dk, void* dv,
+                                float* dla, const void* ws, hipStream_t st) {
+  typedef bf16 T;
+  const int nc = (s.T + kC - 1) / kC;
+  const int BH = s.B * s.H;
+  if (nc == 0 || BH == 0) return hipSuccess;
+  const T* S_all = (const T*)ws;
+  const T* dS_all = S_all + (size_t)BH * nc * kD * kD;
+  const T* dST_all = dS_all + (size_t)BH * nc * kD * kD;
   hipLaunchKernelGGL(gla_bwd_chunk, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, (const T*)S_all,
-                     (const T*)dS_all, (const T*)dST_all, (T*)dq, (T*)dk, (T*)dv, dla, s.T);
+                     (const T*)k, (const T*)v, la, (const T*)dO, S_all, dS_all, dST_all, (T*)dq,
+                     (T*)dk, (T*)dv, dla, s.T);
   return hipGetLastError();
 }
 

@@ -7,9 +7,12 @@ namespace lz {
 
 size_t gla_bwd_workspace_bytes(const Shape& s);
 size_t swa_bwd_workspace_bytes(const Shape& s);
-hipError_t launch_gla_bwd(const Shape& s, const void* q, const void* k, const void* v,
-                          const float* la, const float* h0, const void* dO, void* dq, void* dk,
-                          void* dv, float* dla, void* ws, hipStream_t st);
+hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
+                                const float* la, const float* h0, const void* dO, void* ws,
+                                hipStream_t st);
+hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
+                                const float* la, const void* dO, void* dq, void* dk, void* dv,
+                                float* dla, const void* ws, hipStream_t st);
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv, float* dmk, float* dmv,
@@ -22,6 +25,7 @@ __global__ void zero_kernel(float* p, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
 }
+
 }  // namespace
 
 bool bwd_supported(const Shape& s) { return s.dtype == 1 && s.dk == 64 && s.dv == 64; }
@@ -46,10 +50,14 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
     return hipGetLastError();
   }
   char* w = (char*)ws;
-  hipError_t e = launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
-                                w + align256(gla_bwd_workspace_bytes(s)), st);
+  char* wswa = w + align256(gla_bwd_workspace_bytes(s));
+  // The window branch writes dq, dk, dv; the GLA grad kernel (after the scans
+  // that produce its states) adds its gradients to them.
+  hipError_t e = launch_gla_bwd_scans(s, q, k, v, la, h0, dO, w, st);
   if (e != hipSuccess) return e;
-  return launch_gla_bwd(s, q, k, v, la, h0, dO, dq, dk, dv, dla, w, st);
+  e = launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv, wswa, st);
+  if (e != hipSuccess) return e;
+  return launch_gla_bwd_grads(s, q, k, v, la, dO, dq, dk, dv, dla, w, st);
 }
 
 }  // namespace lz
