@@ -57,13 +57,27 @@ __device__ __forceinline__ int frag_major(int row, int col) {
 // dS_{c+1} and its transpose, the state gradient leaving chunk c):
 //   S_{c+1} = D_c S_c + K^_c^T V_c,   dS_c = D_c dS_{c+1} + Q^_c^T dO_c,
 // D_c = diag(2^{b_last}), K^_s = k_s 2^{b_last - b_s}, Q^_t = q_t 2^{b_t}.
-// The next chunk's inputs are loaded while this one is processed; lane (r16, g)
-// of wave w owns token 16w + r16, channels 16ct + 4g + r, as in the grad kernel.
+// Gating: wave w owns channels 16w..16w+15 and lane l token l of the chunk, so
+// the cumsum over the chunk is one 64-lane scan (row shifts, then the row
+// broadcasts of lanes 15 and 31) and b_last is lane 63's value.  The next
+// chunk's inputs are loaded two steps ahead into alternating register sets.
 struct ScanSmem {
   bf16 xT[2][kTile];  // gated k (or q) transposed [c][t]
   bf16 yT[2][kTile];  // v (or dO) transposed [j][t]
-  float tot[2][4][kD];
+  float dec[2][kD];   // 2^{b_last} per channel
 };
+
+// inclusive cumsum over the 64 lanes of a wave
+__device__ __forceinline__ float wave_scan64(float x) {
+  x += dpp_shr<1>(x);
+  x += dpp_shr<2>(x);
+  x += dpp_shr<4>(x);
+  x += dpp_shr<8>(x);
+  // lane 15 of row 0 into row 1, lane 47 of row 2 into row 3; then lane 31 into rows 2, 3
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
 
 __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -72,14 +86,15 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     int T_len) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-  const int r16 = lane & 15, g = lane >> 4;
+  const int r16 = lane & 15, g = lane >> 4, odd = lane & 1;
   const bool rev = (int)blockIdx.x >= BH;
   const int bh = rev ? blockIdx.x - BH : blockIdx.x;
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
   const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb), bla(la + off, 2 * nb);
   const int nc = (T_len + kC - 1) / kC;
-  const int t = 16 * w + r16;
+  const int cw = 16 * w;                  // this wave's first channel
+  const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
 
   // a1[jb]: [j = 16jb + 4g + r][c = 16w + r16] (state transposed); a2[jb] (reverse
   // scan only): [c = 16w + 4g + r][j = 16jb + r16]
@@ -90,134 +105,113 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     a2[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (!rev && h0) {
-    const float* hp = h0 + (size_t)bh * kD * kD + (size_t)t * kD + 4 * g;
+    const float* hp = h0 + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) a1[jb] = *reinterpret_cast<const f32x4*>(hp + 16 * jb);
   }
-  // Two input sets, each reloaded (two chunks ahead) right after its last use,
-  // so no in-flight load is carried across the loop's back edge.
+  // lane = token of the chunk; 16 channels from cw
   struct In {
     u32x4 la[4];
-    u32x2 x[4], y[4];
+    u32x4 x[2], y[2];
   };
   auto load = [&](In& d, int ch) {
-    const u32 rowe = (u32)(ch * kC + t) * kD;
+    const u32 e = (u32)(ch * kC + lane) * kD + cw;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const u32 e = rowe + 16 * ct + 4 * g;
-      d.la[ct] = bla.ld128(e * 4);
-      d.x[ct] = ld64v(bx, e * 2);
-      d.y[ct] = ld64v(by, e * 2);
+    for (int i = 0; i < 4; ++i) d.la[i] = bla.ld128((e + 4 * i) * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      d.x[i] = bx.ld128((e + 8 * i) * 2);
+      d.y[i] = by.ld128((e + 8 * i) * 2);
     }
   };
-  const int odd = r16 & 1, te = t & ~1;
+  const int te = lane & ~1;
+  // 16 channels of tokens (lane, lane ^ 1) as (even, odd) token pairs: the
+  // even lane writes channels cw..cw+7, the odd lane cw+8..cw+15
+  auto tstore = [&](bf16* dstT, const u32 (&X)[8]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const u32 R = dpp_swap1(odd ? X[m] : X[4 + m]);
+      const u32 fst = odd ? R : X[m], snd = odd ? X[4 + m] : R;
+      const int c = cw + 8 * odd + 2 * m;
+      *reinterpret_cast<u32*>(&dstT[swz64(c, te)]) = lo2(fst, snd);
+      *reinterpret_cast<u32*>(&dstT[swz64(c + 1, te)]) = hi2(fst, snd);
+    }
+  };
   auto chunk_at = [&](int n) { return rev ? nc - 1 - n : n; };
   auto step = [&](In& d, int n) {
     const int ch = chunk_at(n), buf = n & 1;
+    // gate cumsum over the chunk, per channel
+    float b[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) b[c] = wave_scan64(f_at(d.la[c >> 2], c & 3) * kLog2e);
+    float bl[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      bl[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b[c]), 63));
+    if (lane < 16) {
+      float dl = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) dl = lane == c ? bl[c] : dl;
+      sm.dec[buf][cw + lane] = exp2_fast(dl);
+    }
+    u32 X[8], Y[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const u32 xw = d.x[m >> 2][m & 3];
+      const float f0 = exp2_fast(rev ? b[2 * m] : bl[2 * m] - b[2 * m]);
+      const float f1 = exp2_fast(rev ? b[2 * m + 1] : bl[2 * m + 1] - b[2 * m + 1]);
+      X[m] = pack_bf2(bf_lo(xw) * f0, bf_hi(xw) * f1);
+      Y[m] = d.y[m >> 2][m & 3];
+    }
+    tstore(sm.xT[buf], X);
+    tstore(sm.yT[buf], Y);
+    // unconditional (clamped at the last chunk) so that the wait counts stay exact
+    load(d, chunk_at(min(n + 2, nc - 1)));
     // the state at the chunk boundary, before this chunk's update
+    // (all words packed before the first store, so no store's data register is
+    // rewritten while earlier stores are in flight)
     {
       const size_t so = ((size_t)bh * nc + ch) * kTile;
       bf16* dst = (rev ? dS_all : S_all) + so;
+      u32x2 w1[4], w2[4];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        w1[jb] = u32x2{pack_bf2(a1[jb][0], a1[jb][1]), pack_bf2(a1[jb][2], a1[jb][3])};
+        w2[jb] = u32x2{pack_bf2(a2[jb][0], a2[jb][1]), pack_bf2(a2[jb][2], a2[jb][3])};
+      }
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
-        *reinterpret_cast<u32x2*>(dst + frag_major(t, 16 * jb + 4 * g)) =
-            u32x2{pack_bf2(a1[jb][0], a1[jb][1]), pack_bf2(a1[jb][2], a1[jb][3])};
+        *reinterpret_cast<u32x2*>(dst + frag_major(cw + r16, 16 * jb + 4 * g)) = w1[jb];
       if (rev)
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
-          *reinterpret_cast<u32x2*>(dST_all + so + frag_major(16 * jb + r16, 16 * w + 4 * g)) =
-              u32x2{pack_bf2(a2[jb][0], a2[jb][1]), pack_bf2(a2[jb][2], a2[jb][3])};
+          *reinterpret_cast<u32x2*>(dST_all + so + frag_major(16 * jb + r16, cw + 4 * g)) = w2[jb];
     }
-    // gate cumsum within the 16-token block, then across blocks
-    float b[4][4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[ct][r] = f_at(d.la[ct], r) * kLog2e;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<1>(b[ct][r]);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<2>(b[ct][r]);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<4>(b[ct][r]);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) b[ct][r] += dpp_shr<8>(b[ct][r]);
-    if (r16 == 15)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        *reinterpret_cast<f32x4*>(&sm.tot[buf][w][16 * ct + 4 * g]) =
-            f32x4{b[ct][0], b[ct][1], b[ct][2], b[ct][3]};
-    lds_barrier();
-    // gated x and raw y, transposed: the even lane of a token pair writes
-    // channels c0, c0+1 and the odd lane c0+2, c0+3
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int c0 = 16 * ct + 4 * g;
-      f32x4 pre = {0.f, 0.f, 0.f, 0.f}, bl = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 tj = *reinterpret_cast<const f32x4*>(&sm.tot[buf][j][c0]);
-        bl += tj;
-        if (j < w) pre += tj;
-      }
-      float f[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float bb = b[ct][r] + pre[r];
-        f[r] = exp2_fast(rev ? bb : bl[r] - bb);
-      }
-      const u32 xa = d.x[ct][0], xb = d.x[ct][1];
-      const u32 X0 = pack_bf2(bf_lo(xa) * f[0], bf_hi(xa) * f[1]);
-      const u32 X1 = pack_bf2(bf_lo(xb) * f[2], bf_hi(xb) * f[3]);
-      const u32 Y0 = d.y[ct][0], Y1 = d.y[ct][1];
-      const u32 rx = dpp_swap1(odd ? X0 : X1), ry = dpp_swap1(odd ? Y0 : Y1);
-      const u32 fX = odd ? rx : X0, sX = odd ? X1 : rx;
-      const u32 fY = odd ? ry : Y0, sY = odd ? Y1 : ry;
-      const int cp = c0 + 2 * odd;
-      *reinterpret_cast<u32*>(&sm.xT[buf][at(cp, te)]) = lo2(fX, sX);
-      *reinterpret_cast<u32*>(&sm.xT[buf][at(cp + 1, te)]) = hi2(fX, sX);
-      *reinterpret_cast<u32*>(&sm.yT[buf][at(cp, te)]) = lo2(fY, sY);
-      *reinterpret_cast<u32*>(&sm.yT[buf][at(cp + 1, te)]) = hi2(fY, sY);
-    }
-    if (n + 2 < nc) load(d, chunk_at(n + 2));
     lds_barrier();
     // decay, then add this chunk's outer products
-    float d1 = 0.f;
-    f32x4 d2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      d1 += sm.tot[buf][j][t];
-      if (rev) d2 += *reinterpret_cast<const f32x4*>(&sm.tot[buf][j][16 * w + 4 * g]);
-    }
-    d1 = exp2_fast(d1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d2[r] = exp2_fast(d2[r]);
-    bf16x8 xf[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) xf[p] = ld8<bf16>(&sm.xT[buf][at(t, 32 * p + 8 * g)]);
+    const float d1 = sm.dec[buf][cw + r16];
+    const f32x4 d2 = *reinterpret_cast<const f32x4*>(&sm.dec[buf][cw + 4 * g]);
+    const bf16* xb = sm.xT[buf] + 1024 * w;
+    const bf16x8 xf0 = ld8<bf16>(xb + fb0), xf1 = ld8<bf16>(xb + fb1);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       a1[jb] *= d1;
       if (rev) a2[jb] *= d2;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const bf16x8 yf = ld8<bf16>(&sm.yT[buf][at(16 * jb + r16, 32 * p + 8 * g)]);
-        mma(a1[jb], yf, xf[p]);
-        if (rev) mma(a2[jb], xf[p], yf);
+      const bf16* yb = sm.yT[buf] + 1024 * jb;
+      const bf16x8 y0 = ld8<bf16>(yb + fb0), y1 = ld8<bf16>(yb + fb1);
+      mma(a1[jb], y0, xf0);
+      mma(a1[jb], y1, xf1);
+      if (rev) {
+        mma(a2[jb], xf0, y0);
+        mma(a2[jb], xf1, y1);
       }
     }
   };
   In A, B;
   load(A, chunk_at(0));
-  if (nc > 1) load(B, chunk_at(1));
+  __builtin_amdgcn_sched_barrier(0);  // keep set A's loads ahead of set B's
+  load(B, chunk_at(min(1, nc - 1)));
+  __builtin_amdgcn_sched_barrier(0);
   for (int n = 0; n < nc; n += 2) {
     step(A, n);
     if (n + 1 < nc) step(B, n + 1);
