@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and training lines")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
+    ap.add_argument("--train-only", action="store_true",
+                    help="only time the training step (forward + backward), for profiling")
     args = ap.parse_args()
     if args.copy_probe:
         import torch
@@ -149,6 +151,10 @@ def main():
     from gated_linear_attention_chunked_amd import _abi
     from workloads import WORKLOADS, make_inputs
 
+    if args.train_only:
+        print(json.dumps({"train": bench_train(lz, torch, torch.device("cuda:0"), args)}),
+              flush=True)
+        return
     name = "prefill_bf16_b2_h32_t4096_d128"
     wl = WORKLOADS[name]
     B, H, T, d, w, M, C = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta, wl.chunk
