@@ -151,9 +151,11 @@ __global__ void pos_increment_kernel(int64_t* pos, int B) {
 }
 
 template <typename T>
-__global__ void ring_fill_kernel(const T* __restrict__ x, T* __restrict__ ring, int T_len, int W,
-                                 int D) {
+__global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                 T* __restrict__ rk, T* __restrict__ rv, int T_len, int W, int D) {
   const int slot = blockIdx.x, bh = blockIdx.y;
+  const T* x = blockIdx.z ? v : k;  // z = 0: keys, z = 1: values
+  T* ring = blockIdx.z ? rv : rk;
   // the position p = slot (mod W) inside [T - W, T), if any
   long base = (long)T_len - W;
   long p = base + ((((long)slot - base) % W) + W) % W;
@@ -181,13 +183,9 @@ hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, con
 template <typename T>
 hipError_t ring_fill_typed(const Shape& s, const void* k, const void* v, void* rk, void* rv,
                            hipStream_t st) {
-  dim3 grid(s.window, s.B * s.H);
-  hipLaunchKernelGGL(ring_fill_kernel<T>, grid, dim3(64), 0, st, (const T*)k, (T*)rk, s.T,
-                     s.window, s.dk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ring_fill_kernel<T>, grid, dim3(64), 0, st, (const T*)v, (T*)rv, s.T,
-                     s.window, s.dv);
+  dim3 grid(s.window, s.B * s.H, 2);  // dk == dv
+  hipLaunchKernelGGL(ring_fill_kernel<T>, grid, dim3(64), 0, st, (const T*)k, (const T*)v,
+                     (T*)rk, (T*)rv, s.T, s.window, s.dk);
   return hipGetLastError();
 }
 

@@ -24,9 +24,12 @@ hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const vo
 
 // Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
 // accumulate != 0); o_swa and lse are optional extra outputs.
+// ring_k / ring_v (nullable): also fill the decode window cache (slot p mod w <- token p
+// for the last min(T, w) tokens, zero elsewhere).
 hipError_t launch_swa_fwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, void* o, float out_scale,
-                          int accumulate, void* o_swa, float* lse, hipStream_t st);
+                          int accumulate, void* o_swa, float* lse, void* ring_k, void* ring_v,
+                          hipStream_t st);
 
 // Window cache after a prefill (slot p mod w <- token p for the last min(T,w) tokens).
 hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* ring_k,

@@ -100,7 +100,8 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
   if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   if (!has_tokens(desc)) return LIZARD_OK;
   return hip_status(
-      lz::launch_swa_fwd(to_shape(desc), q, k, v, meta_k, meta_v, o, 1.0f, 0, nullptr, lse, stream));
+      lz::launch_swa_fwd(to_shape(desc), q, k, v, meta_k, meta_v, o, 1.0f, 0, nullptr, lse,
+                         nullptr, nullptr, stream));
 }
 
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
@@ -123,11 +124,12 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
     // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
     e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, ws, stream);
     if (e == hipSuccess)
-      e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, stream);
-  } else if (hT) {
-    e = lz::launch_state_copy(s, h0, hT, stream);
+      e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, ring_k,
+                             ring_v, stream);
+  } else {
+    if (hT) e = lz::launch_state_copy(s, h0, hT, stream);
+    if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, k, v, ring_k, ring_v, stream);
   }
-  if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, k, v, ring_k, ring_v, stream);
   return hip_status(e);
 }
 

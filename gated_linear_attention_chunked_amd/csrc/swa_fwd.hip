@@ -241,8 +241,8 @@ template <typename T, int D, int NS>
 __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ mk, const T* __restrict__ mv, T* __restrict__ o,
-    T* __restrict__ o_swa, float* __restrict__ lse, int T_len, int H, int W, int M,
-    float scale_log2, float out_scale, int accumulate, int cps) {
+    T* __restrict__ o_swa, float* __restrict__ lse, T* __restrict__ rk, T* __restrict__ rv,
+    int T_len, int H, int W, int M, float scale_log2, float out_scale, int accumulate, int cps) {
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int NPREV = NS - 2;
@@ -490,12 +490,34 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     }
     lds_barrier();  // the next two chunks are in the ring
   }
+  // window cache for decoding (rk, rv non-null): slot p mod W <- token p for the
+  // last min(T, W) tokens, zero for slots without a token (T < W); the head's
+  // segments share the slots, so no work-group's tail grows much
+  if (rk) {
+    constexpr int PER = 16 / (int)sizeof(T);  // elements per 16 bytes
+    constexpr int RG = D / PER;               // 16-byte pieces per row
+    const size_t rbase = (size_t)bh * W * D;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int s_lo = (int)((long long)W * seg / nseg), s_hi = (int)((long long)W * (seg + 1) / nseg);
+    for (int e = s_lo * RG + tid; e < s_hi * RG; e += 512) {
+      const int slot = e / RG, c = (e % RG) * PER;
+      const int p = slot < T_len % W ? T_len - T_len % W + slot : T_len - T_len % W - W + slot;
+      u32x4 xk = z, xv = z;
+      if (p >= 0) {
+        const u32 off = (u32)(((size_t)p * D + c) * sizeof(T));
+        xk = bk.ld128(off);
+        xv = bv.ld128(off);
+      }
+      *reinterpret_cast<u32x4*>(&rk[rbase + (size_t)slot * D + c]) = xk;
+      *reinterpret_cast<u32x4*>(&rv[rbase + (size_t)slot * D + c]) = xv;
+    }
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v,
                         const void* mk, const void* mv, void* o, float out_scale, int acc,
-                        void* o_swa, float* lse, hipStream_t st) {
+                        void* o_swa, float* lse, void* rk, void* rv, hipStream_t st) {
   if (s.window <= 2 * kKT + 1) {
     // streaming form: runs of query tiles, enough work-groups to fill the chip
     const int nc = (s.T + kKT - 1) / kKT;
@@ -509,11 +531,11 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
     if (s.window <= kKT + 1) {
       hipLaunchKernelGGL((swa_fwd_ring<T, D, 3>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
-                         lse, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
     } else {
       hipLaunchKernelGGL((swa_fwd_ring<T, D, 4>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
-                         lse, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
     }
     return hipGetLastError();
   }
@@ -521,20 +543,28 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
   hipLaunchKernelGGL((swa_fwd_kernel<T, D, D>), grid, dim3(256), 0, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa, lse, s.T, s.H,
                      s.window, s.n_meta, s.scale * kLog2e, out_scale, acc);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && rk) e = launch_ring_fill(s, k, v, rk, rv, st);
+  return e;
 }
 
 }  // namespace
 
 hipError_t launch_swa_fwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, void* o, float out_scale,
-                          int accumulate, void* o_swa, float* lse, hipStream_t st) {
-  if (s.T == 0 || s.B * s.H == 0) return hipSuccess;
+                          int accumulate, void* o_swa, float* lse, void* ring_k, void* ring_v,
+                          hipStream_t st) {
+  if (s.B * s.H == 0) return hipSuccess;
+  if (s.T == 0) return ring_k ? launch_ring_fill(s, k, v, ring_k, ring_v, st) : hipSuccess;
   if (s.dtype == 1) {
-    if (s.dk == 128) return launch_typed<bf16, 128>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse, st);
-    return launch_typed<bf16, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse, st);
+    if (s.dk == 128)
+      return launch_typed<bf16, 128>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
+                                     ring_k, ring_v, st);
+    return launch_typed<bf16, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
+                                  ring_k, ring_v, st);
   }
-  return launch_typed<float, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse, st);
+  return launch_typed<float, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
+                                 ring_k, ring_v, st);
 }
 
 }  // namespace lz
