@@ -11,9 +11,9 @@
 // chunks so that B*H*G work-groups fill the chip (G depends on B*H, not on T):
 //   1. state pass   (segments 0..G-2, parallel): the segment's own end state
 //                   from zero and its total log2 decay;
-//   2. carry pass   (per head): S_in(g+1) = 2^{Gamma_g} S_in(g) + S_loc(g);
-//   3. output pass  (all segments, parallel): the chunk recurrence below,
-//                   started from S_in(g).
+//   2. output pass  (all segments, parallel): S_in(g) from h0 and the earlier
+//                   segments, S_in(j+1) = 2^{Gamma_j} S_in(j) + S_loc(j), then
+//                   the chunk recurrence below started from S_in(g).
 // The state is associative over (decay, state) pairs, so this is the same
 // recurrence evaluated in another order.
 //
@@ -213,11 +213,12 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
       }
     }
   }
+  // stored column-major ([value column][key row]) so that the output pass reads
+  // four consecutive rows of one column as one 16-byte load
   float* dst = ws_state + ((size_t)bh * (G - 1) + seg) * DK * DK;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * cb + 4 * g + r) * DK + 16 * wave + r16] = S[cb][r];
+    *reinterpret_cast<f32x4*>(&dst[(16 * wave + r16) * DK + 16 * cb + 4 * g]) = S[cb];
   if (rg == 0) {
     float* gd = ws_gamma + ((size_t)bh * (G - 1) + seg) * DK;
     gd[2 * cp] = gsum[0];
@@ -226,39 +227,6 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
 }
 
 // ------------------------------------------------------------------ pass 2
-// S_in(g+1) = 2^{Gamma_g} S_in(g) + S_loc(g), written over S_loc(g).  One
-// thread per 4 consecutive state entries (one row); every segment's slot is
-// loaded before the short recurrence runs, so the loads overlap.
-__global__ __launch_bounds__(256) void gla_carry_pass(const float* __restrict__ h0,
-                                                     float* __restrict__ ws_state,
-                                                     const float* __restrict__ ws_gamma, int DK,
-                                                     int G) {
-  const int bh = blockIdx.y;
-  const size_t n = (size_t)DK * DK;
-  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= n) return;
-  const int c = (int)(e / DK);
-  f32x4 loc[kMaxSeg - 1];
-  float gam[kMaxSeg - 1];
-#pragma unroll
-  for (int s = 0; s < kMaxSeg - 1; ++s) {
-    if (s < G - 1) {
-      const size_t slot = (size_t)bh * (G - 1) + s;
-      loc[s] = *reinterpret_cast<const f32x4*>(ws_state + slot * n + e);
-      gam[s] = ws_gamma[slot * DK + c];
-    }
-  }
-  f32x4 S = h0 ? *reinterpret_cast<const f32x4*>(h0 + (size_t)bh * n + e) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < kMaxSeg - 1; ++s) {
-    if (s < G - 1) {
-      S = exp2_fast(gam[s]) * S + loc[s];
-      *reinterpret_cast<f32x4*>(ws_state + ((size_t)bh * (G - 1) + s) * n + e) = S;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ pass 3
 // A chunk whose per-channel decay 2^{b_last} stays above 2^-kFastLog2 in every
 // channel takes one reference for all its intra scores, the chunk start:
 // q_t 2^{b_t} (<= |q_t|) against k_s 2^{-b_s} (<= 2^kFastLog2 |k_s|), both far
@@ -271,7 +239,8 @@ template <typename T, int DK>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
-    T* __restrict__ o, float* __restrict__ hT, int T_len, int cps, int G) {
+    const float* __restrict__ ws_gamma, T* __restrict__ o, float* __restrict__ hT, int T_len,
+    int cps, int G) {
   constexpr int NCB = DK / 16;
   constexpr int KS = DK / 32;
   constexpr int NW = DK / 16;
@@ -294,14 +263,24 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
   const int ncol = 16 * wave;
   const size_t s_base = (size_t)bh * DK * DK;
 
-  // state slice S[16cb + 4g + r][ncol + r16]
-  const float* s0 = seg == 0 ? (h0 ? h0 + s_base : nullptr)
-                             : ws_state + ((size_t)bh * (G - 1) + seg - 1) * DK * DK;
+  // state slice S[16cb + 4g + r][ncol + r16] entering the segment: h0 carried
+  // through the earlier segments' local end states and decays
   f32x4 S[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[cb][r] = s0 ? s0[(16 * cb + 4 * g + r) * DK + ncol + r16] : 0.f;
+    for (int r = 0; r < 4; ++r) S[cb][r] = h0 ? h0[s_base + (16 * cb + 4 * g + r) * DK + ncol + r16] : 0.f;
+  for (int sg = 0; sg < seg; ++sg) {  // local states are column-major
+    const float* loc = ws_state + ((size_t)bh * (G - 1) + sg) * DK * DK;
+    const float* gm = ws_gamma + ((size_t)bh * (G - 1) + sg) * DK;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&loc[(ncol + r16) * DK + 16 * cb + 4 * g]);
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gm[16 * cb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[cb][r] = exp2_fast(g4[r]) * S[cb][r] + l4[r];
+    }
+  }
 
   // score blocks (0,1) and (2,3) lie above the diagonal; they are read by the
   // paired contraction steps and must stay zero
@@ -588,7 +567,8 @@ template <int DK>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
-    bf16* __restrict__ o, float* __restrict__ hT, int T_len, int cps, int G) {
+    const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT, int T_len,
+    int cps, int G) {
   constexpr int NCB = DK / 16;             // 16-row blocks of the state
   constexpr int KS = DK / 32;              // contraction steps over channels
   constexpr int NWC = DK / 32;             // consumer waves (= producer waves)
@@ -614,8 +594,8 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
   if (consumer) {
     // ---------------------------------------------------------- consumer
     const int cw = wave;  // value columns 32cw .. 32cw+31, as two 16-column blocks
-    const float* s0 = seg == 0 ? (h0 ? h0 + s_base : nullptr)
-                               : ws_state + ((size_t)bh * (G - 1) + seg - 1) * DK * DK;
+    // state entering the segment: h0 carried through the earlier segments'
+    // local end states and decays
     f32x4 S[2][NCB];  // S[nt][cb]: rows 16cb + 4g + r, column 32cw + 16nt + r16
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -623,7 +603,21 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[nt][cb][r] = s0 ? s0[(16 * cb + 4 * g + r) * DK + 32 * cw + 16 * nt + r16] : 0.f;
+          S[nt][cb][r] = h0 ? h0[s_base + (16 * cb + 4 * g + r) * DK + 32 * cw + 16 * nt + r16] : 0.f;
+    for (int sg = 0; sg < seg; ++sg) {  // local states are column-major
+      const float* loc = ws_state + ((size_t)bh * (G - 1) + sg) * DK * DK;
+      const float* gm = ws_gamma + ((size_t)bh * (G - 1) + sg) * DK;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gm[16 * cb + 4 * g]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&loc[(32 * cw + 16 * nt + r16) * DK + 16 * cb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[nt][cb][r] = exp2_fast(g4[r]) * S[nt][cb][r] + l4[r];
+        }
+      }
+    }
 
     // v of a chunk: lane takes rows 4vr..4vr+3, columns 32cw + 8vo .. +7
     const int vo = lane & 3, vr = lane >> 2;
@@ -983,18 +977,14 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
                        (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gla_carry_pass, dim3((DK * DK / 4 + 255) / 256, BH), dim3(256), 0, st, h0,
-                       ws_state, ws_gamma, DK, pl.G);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((gla_output_ws<DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, la, h0, ws_state, (bf16*)o, hT, s.T, pl.cps,
+                       (const bf16*)k, (const bf16*)v, la, h0, ws_state, ws_gamma, (bf16*)o, hT, s.T, pl.cps,
                        pl.G);
   } else {
     hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, la, h0, ws_state, (T*)o, hT, s.T, pl.cps, pl.G);
+                       (const T*)k, (const T*)v, la, h0, ws_state, ws_gamma, (T*)o, hT, s.T, pl.cps, pl.G);
   }
   return hipGetLastError();
 }
