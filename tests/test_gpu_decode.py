@@ -95,3 +95,29 @@ def test_full_size_decode_sampled_heads():
     wl = WORKLOADS["decode_bf16_b64_h32_d128"]
     prefill_then_decode(wl.B, wl.H, wl.T, 4, wl.dk, wl.window, wl.n_meta, wl.dtype,
                         heads=[(0, 0), (63, 31)])
+
+
+def test_decode_position_advance_many_heads():
+    # the position counter advances once per call however many heads a sequence
+    # has; a negative position decodes as 0 and still advances by one
+    B, H, d, w, M = 3, 32, 64, 8, 2
+    rng = torch.Generator().manual_seed(11)
+    state = torch.randn(B, H, d, d, generator=rng) * 0.1
+    rk = torch.randn(B, H, w, d, generator=rng) / 8
+    rv = torch.randn(B, H, w, d, generator=rng) / 8
+    mk, mv = torch.randn(H, M, d, generator=rng), torch.randn(H, M, d, generator=rng)
+    dec = make_decode_inputs(1, B, H, d, d, dtype="f32", seed=5)
+    x = [dec[n][0].cuda() for n in ("q", "k", "v", "log_alpha")]
+    outs = []
+    for p0 in ([-3, 7, 1000], [0, 7, 1000]):
+        g = [t.clone().cuda() for t in (state, rk, rv)]
+        pos = torch.tensor(p0, dtype=torch.int64, device="cuda")
+        o = lz.decode_step(*x, *g, pos, mk.cuda(), mv.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(pos.cpu(), torch.tensor(p0) + 1)
+        outs.append([o] + [t.clone() for t in g])
+        lz.decode_step(*x, *g, pos, mk.cuda(), mv.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(pos.cpu(), torch.tensor(p0) + 2)
+    for a, b in zip(*outs):  # one step from position -3 is one step from 0
+        assert torch.equal(a, b)
