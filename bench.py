@@ -227,6 +227,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["long_prefill"] = bench_long_prefill(lz, torch, dev, args, ms / (B * T))
         out["decode"] = bench_decode(lz, torch, dev)
         try:
             out["train"] = bench_train(lz, torch, dev, args)
@@ -235,6 +236,26 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_long_prefill(lz, torch, dev, args, ms_per_token_headline):
+    """Hybrid prefill of B=1, H=32, T=32768, d=128 (same value families); the time
+    per token against the headline workload's shows whether time is linear in T
+    (same B*H*T/8 work per token, 8x longer sequences)."""
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["prefill_bf16_b1_h32_t32768_d128"]
+    x = {n: t.to(dev) for n, t in make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.n_meta,
+                                              dtype=wl.dtype, seed=0).items()}
+
+    def step():
+        lz.hybrid_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"],
+                      wl.window)
+
+    ms = event_time_ms(step, max(5, args.steps // 5), max(5, args.warmup // 2))
+    per_tok = ms / (wl.B * wl.T)
+    return {"workload": "prefill_bf16_b1_h32_t32768_d128", "ms_per_call": ms,
+            "tokens_per_s": wl.B * wl.T / (ms / 1e3),
+            "time_per_token_vs_headline": per_tok / ms_per_token_headline}
 
 
 def bench_decode(lz, torch, dev):
