@@ -22,7 +22,7 @@
 //
 // Kernels:
 //   1. scans (one launch): per head, the state scan forward writes S_c for every
-//      chunk and the reverse scan writes dS_{c+1} (and its transpose)
+//      chunk and the reverse scan writes dS_{c+1}
 //   2. per chunk: dq, dk, dv and dlog_alpha from the chunk's inputs and the two
 //      states of its boundaries
 // Intra-chunk factors use 16-token sub-block midpoints R_i as references.
@@ -54,7 +54,7 @@ __device__ __forceinline__ int frag_major(int row, int col) {
 // -------------------------------------------------------------- 1-2. scans
 // Work-groups 0..BH-1 run the state scan of one head forward (writing S_c, the
 // state entering chunk c); work-groups BH..2BH-1 run the reverse scan (writing
-// dS_{c+1} and its transpose, the state gradient leaving chunk c):
+// dS_{c+1}, the state gradient leaving chunk c):
 //   S_{c+1} = D_c S_c + K^_c^T V_c,   dS_c = D_c dS_{c+1} + Q^_c^T dO_c,
 // D_c = diag(2^{b_last}), K^_s = k_s 2^{b_last - b_s}, Q^_t = q_t 2^{b_t}.
 // Gating: wave w owns channels 16w..16w+15 and lane l token l of the chunk, so
@@ -82,8 +82,7 @@ __device__ __forceinline__ float wave_scan64(float x) {
 __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
-    bf16* __restrict__ S_all, bf16* __restrict__ dS_all, bf16* __restrict__ dST_all, int BH,
-    int T_len) {
+    bf16* __restrict__ S_all, bf16* __restrict__ dS_all, int BH, int T_len) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4, odd = lane & 1;
@@ -96,14 +95,10 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   const int cw = 16 * w;                  // this wave's first channel
   const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
 
-  // a1[jb]: [j = 16jb + 4g + r][c = 16w + r16] (state transposed); a2[jb] (reverse
-  // scan only): [c = 16w + 4g + r][j = 16jb + r16]
-  f32x4 a1[4], a2[4];
+  // a1[jb]: [j = 16jb + 4g + r][c = 16w + r16] (the state, transposed)
+  f32x4 a1[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    a2[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int jb = 0; jb < 4; ++jb) a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (!rev && h0) {
     const float* hp = h0 + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
 #pragma unroll
@@ -173,38 +168,26 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     {
       const size_t so = ((size_t)bh * nc + ch) * kTile;
       bf16* dst = (rev ? dS_all : S_all) + so;
-      u32x2 w1[4], w2[4];
+      u32x2 w1[4];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
+      for (int jb = 0; jb < 4; ++jb)
         w1[jb] = u32x2{pack_bf2(a1[jb][0], a1[jb][1]), pack_bf2(a1[jb][2], a1[jb][3])};
-        w2[jb] = u32x2{pack_bf2(a2[jb][0], a2[jb][1]), pack_bf2(a2[jb][2], a2[jb][3])};
-      }
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
         *reinterpret_cast<u32x2*>(dst + frag_major(cw + r16, 16 * jb + 4 * g)) = w1[jb];
-      if (rev)
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-          *reinterpret_cast<u32x2*>(dST_all + so + frag_major(16 * jb + r16, cw + 4 * g)) = w2[jb];
     }
     lds_barrier();
     // decay, then add this chunk's outer products
     const float d1 = sm.dec[buf][cw + r16];
-    const f32x4 d2 = *reinterpret_cast<const f32x4*>(&sm.dec[buf][cw + 4 * g]);
     const bf16* xb = sm.xT[buf] + 1024 * w;
     const bf16x8 xf0 = ld8<bf16>(xb + fb0), xf1 = ld8<bf16>(xb + fb1);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       a1[jb] *= d1;
-      if (rev) a2[jb] *= d2;
       const bf16* yb = sm.yT[buf] + 1024 * jb;
       const bf16x8 y0 = ld8<bf16>(yb + fb0), y1 = ld8<bf16>(yb + fb1);
       mma(a1[jb], y0, xf0);
       mma(a1[jb], y1, xf1);
-      if (rev) {
-        mma(a2[jb], xf0, y0);
-        mma(a2[jb], xf1, y1);
-      }
     }
   };
   In A, B;
@@ -227,6 +210,7 @@ struct BwdSmem {
   bf16 dor[kTile];  // dO rows [t][j]
   bf16 doT[kTile];  // dO transposed [j][split_pos(t)]
   bf16 vr[kTile];   // v rows [s][j]
+  bf16 dST[kTile];  // dS_{c+1} transposed [j][c] (swz64 layout)
   float tot[4][kD];  // per-block gate totals
   float R[4][kD];    // sub-block midpoints b[16i + 7]
   float Ru[4][kD];   // references in use: the midpoints, or 0 on the single-reference path
@@ -245,8 +229,8 @@ __device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, in
 }
 
 // One work-group per (chunk, head): dq, dk, dv (added to what dq, dk, dv hold)
-// and dlog_alpha of the GLA branch, from the chunk's inputs and the states S_c, dS_{c+1} (and dS_{c+1}^T)
-// written by the two scans.  Wave w owns token block w in both roles (query for
+// and dlog_alpha of the GLA branch, from the chunk's inputs and the states S_c,
+// dS_{c+1} written by the two scans (dS_{c+1} is transposed here, in LDS).  Wave w owns token block w in both roles (query for
 // dq, key for dk and dv), so the work of the two halves balances.  Lane
 // (r16, g) owns token t = 16w + r16 and channels 16ct + 4g + r (ct, r < 4):
 // the accumulator layout of every output tile, in which the gate cumsum and
@@ -254,7 +238,7 @@ __device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, in
 __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
-    const bf16* __restrict__ dS_all, const bf16* __restrict__ dST_all, bf16* __restrict__ dq,
+    const bf16* __restrict__ dS_all, bf16* __restrict__ dq,
     bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dla, int T_len) {
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -267,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   const Buf bla(la + off, 2 * nb);
   const size_t soff = ((size_t)bh * nc + ch) * kTile;
   const u32 sb = (u32)(kTile * sizeof(bf16));
-  const Buf bS(S_all + soff, sb), bdS(dS_all + soff, sb), bdST(dST_all + soff, sb);
+  const Buf bS(S_all + soff, sb), bdS(dS_all + soff, sb);
   const int t = 16 * w + r16;
   const bool live = t0 + t < T_len;
   const u32 rowe = (u32)(t0 + t) * kD;  // element offset of this lane's token row
@@ -297,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   }
   // state fragments (fragment-major): rows 16ct + r16, columns 32p + 8g..
   auto frag_off = [&](int ct, int p) { return (u32)(((2 * ct + p) * 64 + lane) * 16); };
-  u32x4 Sf[4][2], dSf[4][2], dSTf[4][2];
+  u32x4 Sf[4][2], dSf[4][2];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -422,7 +406,6 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       dSf[ct][p] = bdS.ld128(frag_off(ct, p));
-      dSTf[ct][p] = bdST.ld128(frag_off(ct, p));
     }
   lds_barrier();
 
@@ -509,6 +492,28 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
       if (g == 0) sm.st[16 * ct + r16] = pc * exp2_fast(sm.bl[16 * ct + r16]);
     }
   }
+  // dS_{c+1} transposed into LDS for the dv inter product: neighbouring lanes
+  // hold rows c, c+1; the even lane writes (c, c+1) pairs of columns j0..j0+3,
+  // the odd lane of j0+4..j0+7
+  {
+    const int odd = r16 & 1;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const u32 W0 = dSf[ct][p][0], W1 = dSf[ct][p][1], W2 = dSf[ct][p][2], W3 = dSf[ct][p][3];
+        const int ce = 16 * ct + (r16 & ~1), j0 = 32 * p + 8 * g + 4 * odd;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const u32 lo = m ? W1 : W0, hi = m ? W3 : W2;
+          const u32 R = dpp_swap1(odd ? lo : hi);
+          const u32 fst = odd ? R : lo, snd = odd ? hi : R;
+          *reinterpret_cast<u32*>(&sm.dST[swz64(j0 + 2 * m, ce)]) = lo2(fst, snd);
+          *reinterpret_cast<u32*>(&sm.dST[swz64(j0 + 2 * m + 1, ce)]) = hi2(fst, snd);
+        }
+      }
+  }
+  lds_barrier();
   // ---- 5. dk, dv: wave w is key block w
   {
     u32x2 dkw[4], dvw[4];
@@ -611,7 +616,8 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
         if (2 * pp + 1 >= w)
           mma(acc, ld8<bf16>(&sm.doT[at(jl, 32 * pp + 8 * g)]), pack_acc<bf16>(Ab[2 * pp], Ab[2 * pp + 1]));
 #pragma unroll
-      for (int p = 0; p < 2; ++p) mma(acc, as_bf8(dSTf[jt][p]), kh[p]);
+      for (int p = 0; p < 2; ++p)
+        mma(acc, ld8<bf16>(&sm.dST[1024 * jt + swz64(r16, 32 * p + 8 * g)]), kh[p]);
       if (live) {
         const u32x2 prev = dvw[jt];
         const u32 pa = prev[0], pb = prev[1];
@@ -660,10 +666,10 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
 size_t gla_bwd_workspace_bytes(const Shape& s) {
   const size_t nc = (size_t)(s.T + kC - 1) / kC;
   const size_t bh = (size_t)s.B * s.H;
-  return 3 * bh * nc * kD * kD * sizeof(bf16);
+  return 2 * bh * nc * kD * kD * sizeof(bf16);
 }
 
-// Scans: S_c and dS_{c+1} (and its transpose) for every chunk, into ws.
+// Scans: S_c and dS_{c+1} for every chunk, into ws.
 hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
                                 const float* la, const float* h0, const void* dO, void* ws,
                                 hipStream_t st) {
@@ -673,9 +679,8 @@ hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, co
   if (nc == 0 || BH == 0) return hipSuccess;
   T* S_all = (T*)ws;
   T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  T* dST_all = dS_all + (size_t)BH * nc * kD * kD;
   hipLaunchKernelGGL(gla_bwd_scans, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, h0, S_all, dS_all, dST_all, BH,
+                     (const T*)k, (const T*)v, la, (const T*)dO, h0, S_all, dS_all, BH,
                      s.T);
   return hipGetLastError();
 }
@@ -690,9 +695,8 @@ hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, co
   if (nc == 0 || BH == 0) return hipSuccess;
   const T* S_all = (const T*)ws;
   const T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  const T* dST_all = dS_all + (size_t)BH * nc * kD * kD;
   hipLaunchKernelGGL(gla_bwd_chunk, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, S_all, dS_all, dST_all, (T*)dq,
+                     (const T*)k, (const T*)v, la, (const T*)dO, S_all, dS_all, (T*)dq,
                      (T*)dk, (T*)dv, dla, s.T);
   return hipGetLastError();
 }

@@ -128,9 +128,9 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
  * dlog_alpha [B,H,T,dk], dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all float32 except
  * dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as in the forward
  * (its own gradient is not produced).  ws must hold lizard_workspace_bytes(desc,
- * LIZARD_OP_HYBRID_BWD) bytes: three bf16 dk x dv matrices per 64-token chunk
- * and head (S_c, dS_{c+1} and its transpose) plus small per-token and per-tile
- * buffers, so it grows linearly with T.
+ * LIZARD_OP_HYBRID_BWD) bytes: two bf16 dk x dv matrices per 64-token chunk
+ * and head (S_c and dS_{c+1}) plus small per-token and per-tile buffers, so it
+ * grows linearly with T.
  * This version supports BF16 with dk = dv = 64 (LIZARD_E_UNSUPPORTED otherwise). */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
