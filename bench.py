@@ -299,8 +299,7 @@ def bench_decode(lz, torch, dev):
             "us_per_step": ms * 1e3 / steps, "tokens_per_s": B * steps / (ms / 1e3),
             "algorithmic_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "note": "algorithmic bytes equal the counter-measured bytes per step "
-                    "(profiles/decode_b64_h32_d128.md); the separate position-increment "
-                    "launch is included in the step time"}
+                    "(profiles/decode_b64_h32_d128.md)"}
 
 
 def bench_train(lz, torch, dev, args):

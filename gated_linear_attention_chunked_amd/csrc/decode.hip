@@ -20,7 +20,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ la, float* __restrict__ state, T* __restrict__ ring_k,
-    T* __restrict__ ring_v, const int64_t* __restrict__ pos, const T* __restrict__ mk,
+    T* __restrict__ ring_v, int64_t* __restrict__ pos, const T* __restrict__ mk,
     const T* __restrict__ mv, T* __restrict__ o, int H, int W, int M, float scale_log2,
     float mix) {
   constexpr int CQ = D / 4;        // threads per state row (4 columns each)
@@ -34,7 +34,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x, b = bh / H, h = bh % H;
-  const int64_t p = pos[b] < 0 ? 0 : pos[b];  // negative positions count as 0
+  // While the heads of sequence b run, pos[b] = position + (heads done) * 2^40
+  // (see the end of the kernel); the position is the low 40 bits, sign-extended.
+  const int64_t pv = (int64_t)((uint64_t)pos[b] << 24) >> 24;
+  const int64_t p = pv < 0 ? 0 : pv;  // negative positions count as 0
   const int slot = (int)(p % W);
   const int n = (int)((p + 1 < W) ? p + 1 : W);
   const int nk = n + M;
@@ -143,12 +146,17 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const f32x4 out = og + os * (mix / sum);
     st4<T>(o + (size_t)bh * D + 4 * cq, out);
   }
+  // This head is done (every thread read pos[b] before the first barrier): add
+  // 2^40; the last of the H heads of sequence b turns the H arrivals into the
+  // step, pos[b] + 1.  No head reads pos[b] after its own arrival.
+  if (tid == 0) {
+    const int64_t old = (int64_t)atomicAdd(reinterpret_cast<unsigned long long*>(&pos[b]), 1ull << 40);
+    if (((old - pv) >> 40) == H - 1)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&pos[b]),
+                (unsigned long long)(1 - ((int64_t)H << 40)));
+  }
 }
 
-__global__ void pos_increment_kernel(int64_t* pos, int B) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) pos[i] += 1;
-}
 
 template <typename T>
 __global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ v,
@@ -174,9 +182,6 @@ hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, con
                      (const T*)k, (const T*)v, la, state, (T*)ring_k, (T*)ring_v, pos,
                      (const T*)mk, (const T*)mv, (T*)o, s.H, s.window, s.n_meta,
                      s.scale * kLog2e, s.mix);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pos_increment_kernel, dim3((s.B + 255) / 256), dim3(256), 0, st, pos, s.B);
   return hipGetLastError();
 }
 
