@@ -168,6 +168,8 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
   if (desc->n_meta > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   // the window softmax keeps w + M logits in LDS
   if ((long long)desc->window + desc->n_meta > 16384) return LIZARD_E_UNSUPPORTED;
+  // the heads of a sequence count their completion in bits 40.. of pos[b]
+  if (desc->H >= (1 << 22)) return LIZARD_E_UNSUPPORTED;
   return hip_status(lz::launch_decode(to_shape(desc), q, k, v, log_alpha, state, ring_k, ring_v,
                                       pos, meta_k, meta_v, o, stream));
 }

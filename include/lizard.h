@@ -144,7 +144,10 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
  * pos [B] int64 (device): tokens already seen by each sequence.  The call
  * updates state in place, writes (k, v) to ring slot pos mod w, attends over the
  * min(pos+1, w) filled slots plus the M meta slots, writes o [B,H,dv] and then
- * increments every pos[b] by one. */
+ * increments every pos[b] by one.  |pos[b]| must stay below 2^39; while the
+ * call runs, pos[b] holds intermediate values (the heads of a sequence count
+ * their completion in its high bits), so it must not be read or written by
+ * other work until the call has finished. */
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
                                    const void* v, const float* log_alpha, float* state,
                                    void* ring_k, void* ring_v, int64_t* pos,
