@@ -17,7 +17,7 @@ namespace lz {
 namespace {
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(256, 8) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ la, float* __restrict__ state, T* __restrict__ ring_k,
     T* __restrict__ ring_v, int64_t* __restrict__ pos, const T* __restrict__ mk,
