@@ -79,19 +79,23 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
     float qv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] = sq[part * EPL + e];
+    // loads are unconditional (the slot row's value is replaced by the new key
+    // from LDS afterwards) so that several passes' loads are in flight at once
+#pragma unroll 3
     for (int base = 0; base < nk; base += 256 / LPR) {
       const int row = base + tid / LPR;
       float dot = 0.f;
       if (row < nk) {
-        if (row == slot) {
+        const T* kp = (row < n) ? ring_k + ((size_t)bh * W + row) * D
+                                : mk + ((size_t)h * M + (row - n)) * D;
+        float kv[EPL];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) dot += qv[e] * sk[part * EPL + e];
-        } else {
-          const T* kp = (row < n) ? ring_k + ((size_t)bh * W + row) * D
-                                  : mk + ((size_t)h * M + (row - n)) * D;
+        for (int e = 0; e < EPL; ++e) kv[e] = to_f(kp[part * EPL + e]);
+        if (row == slot)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) dot += qv[e] * to_f(kp[part * EPL + e]);
-        }
+          for (int e = 0; e < EPL; ++e) kv[e] = sk[part * EPL + e];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot += qv[e] * kv[e];
       }
 #pragma unroll
       for (int off = 1; off < LPR; off <<= 1) dot += __shfl_xor(dot, off);
@@ -123,11 +127,12 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
 
   // ---- o_swa = sum p_s val_s, with the same (row group, 4 columns) layout
   f32x4 ow = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int row = rg; row < nk; row += RG) {
-    f32x4 val;
-    if (row == slot) val = v4;
-    else if (row < n) val = ld4f<T>(ring_v + ((size_t)bh * W + row) * D + 4 * cq);
-    else val = ld4f<T>(mv + ((size_t)h * M + (row - n)) * D + 4 * cq);
+    const T* vp = (row < n) ? ring_v + ((size_t)bh * W + row) * D
+                            : mv + ((size_t)h * M + (row - n)) * D;
+    f32x4 val = ld4f<T>(vp + 4 * cq);
+    if (row == slot) val = v4;  // the new token, from LDS
     ow += val * logit[row];
   }
   __syncthreads();  // red (GLA partials) complete; reuse red for o_swa after reading
