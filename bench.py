@@ -200,6 +200,7 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     value = B * T / (ms / 1e3)
     flops = algorithmic_flops(B, H, T, d, C, w, M)
+    step_bytes = B * H * T * (3 * d * 2 + d * 4 + d * 2)  # q, k, v, log_alpha in; o out
 
     # ---- dominant part: the GLA branch, timed alone on the same stream
     gws_n = lz.workspace_bytes(desc, _abi.OP_GLA_FWD)
@@ -223,7 +224,15 @@ def main():
         "mfma": {"algorithmic_tflop_per_step": flops / 1e12,
                  "achieved_tflops": flops / (ms / 1e3) / 1e12,
                  "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
-                 "frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+                 "frac": flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 # the step is below the ridge: its ceiling is min(peak, HBM BW x FLOP/B)
+                 "roofline_ceiling_frac": min(1.0, flops / step_bytes * HBM_PEAK_GBS * 1e9
+                                              / (BF16_MFMA_PEAK_TFLOPS * 1e12)),
+                 "frac_of_ceiling": (flops / (ms / 1e3)) / min(BF16_MFMA_PEAK_TFLOPS * 1e12,
+                                                                flops / step_bytes * HBM_PEAK_GBS * 1e9)},
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved_GBs": step_bytes / (ms / 1e3) / 1e9,
+                     "frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"kernel": "GLA branch (lizard_gla_fwd: state and output passes)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
