@@ -1003,6 +1003,20 @@ hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const float* la,
+                            void* ws, int* G, int* cps, hipStream_t st) {
+  const Plan pl = make_plan(s);
+  *G = pl.G;
+  *cps = pl.cps;
+  if (s.T == 0 || pl.G < 2 || s.dtype != 1 || s.dk != 128) return hipSuccess;
+  const int BH = s.B * s.H;
+  float* ws_state = (float*)ws;
+  float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * 128 * 128;
+  hipLaunchKernelGGL((gla_state_pass<bf16, 128>), dim3(pl.G - 1, BH), dim3(512), 0, st,
+                     (const bf16*)k, (const bf16*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
+  return hipGetLastError();
+}
+
 hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const void* v,
                           const float* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st) {

@@ -22,6 +22,21 @@ hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const vo
                           const float* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st);
 
+// State pass of the GLA branch alone (bf16, dk = dv = 128): the local end states
+// and decays of segments 0..G-2 into ws (same layout as launch_gla_fwd's
+// workspace); G segments of cps 64-token chunks each.
+hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const float* la,
+                            void* ws, int* G, int* cps, hipStream_t st);
+
+// Both branches' outputs in one pass after launch_gla_state: o = o_gla + mix *
+// o_swa, hT (optional) and the decode window cache (optional).  Only for the
+// shapes hybrid_fused_ok accepts.
+bool hybrid_fused_ok(const Shape& s);
+hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* v,
+                               const float* la, const void* mk, const void* mv, const float* h0,
+                               void* o, float* hT, void* ring_k, void* ring_v, void* ws,
+                               hipStream_t st);
+
 // Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
 // accumulate != 0); o_swa and lse are optional extra outputs.
 // ring_k / ring_v (nullable): also fill the decode window cache (slot p mod w <- token p

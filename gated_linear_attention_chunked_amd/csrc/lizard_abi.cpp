@@ -120,7 +120,11 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   hipError_t e = hipSuccess;
-  if (desc->T > 0) {
+  if (desc->T > 0 && !lse && !o_swa && lz::hybrid_fused_ok(s)) {
+    // state pass, then both branches in one output pass (o written once)
+    e = lz::launch_hybrid_fused(s, q, k, v, log_alpha, meta_k, meta_v, h0, o, hT, ring_k, ring_v,
+                                ws, stream);
+  } else if (desc->T > 0) {
     // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
     e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, ws, stream);
     if (e == hipSuccess)

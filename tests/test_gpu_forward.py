@@ -57,6 +57,15 @@ def run_and_check(B, H, T, d, w, M, dtype, seed=0, gate_mean=2.0, scale=None, mi
     assert_close("hT", out["hT"], ref["hT"], dt)
     assert_close("ring_k", out["ring_k"], ref["ring_k"], dt, tol=0.0)
     assert_close("ring_v", out["ring_v"], ref["ring_v"], dt, tol=0.0)
+    # the inference call (nothing saved for the backward pass): for bf16 at
+    # d = 128 and w <= 129 both branches run in one output pass
+    inf = lz.hybrid_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], w,
+                        scale=s, mix=mix, h0=x.get("h0"), return_state=True, return_ring=True)
+    torch.cuda.synchronize()
+    assert_close("inference.o", inf["o"], ref["o"], dt)
+    assert_close("inference.hT", inf["hT"], ref["hT"], dt)
+    assert_close("inference.ring_k", inf["ring_k"], ref["ring_k"], dt, tol=0.0)
+    assert_close("inference.ring_v", inf["ring_v"], ref["ring_v"], dt, tol=0.0)
     # each branch alone through its own entry point
     o_gla, hT = lz.gla_fwd(x["q"], x["k"], x["v"], x["log_alpha"], h0=x.get("h0"),
                            return_state=True)
@@ -125,6 +134,23 @@ def test_sharp_softmax():
     # scale 1 on q,k ~ N(0,1): logits of order d, nearly one-hot rows
     run_and_check(1, 2, 200, 64, 64, 4, "f32", scale=1.0, qk_mult=8.0)
     run_and_check(1, 2, 200, 128, 128, 4, "bf16", scale=1.0, qk_mult=math.sqrt(128))
+
+
+# Single-pass hybrid (bf16, d = 128): one head per launch gives the most
+# segments (one per 64-token chunk up to 16), so ring prologues at segment
+# starts, ragged tails and windows up to the ring's 129 keys are all crossed.
+@pytest.mark.parametrize("B,H,T,w,M", [(1, 1, 1, 128, 4), (1, 1, 31, 128, 0), (1, 1, 32, 33, 1),
+                                       (1, 1, 33, 32, 16), (1, 1, 64, 31, 4), (1, 1, 95, 129, 4),
+                                       (1, 1, 200, 1, 0), (1, 1, 300, 64, 4), (1, 1, 383, 100, 16),
+                                       (2, 3, 520, 128, 4), (1, 1, 2200, 128, 4)])
+def test_single_pass_hybrid_shapes(B, H, T, w, M):
+    run_and_check(B, H, T, 128, w, M, "bf16", h0=True, mix=0.7)
+
+
+def test_single_pass_hybrid_steep_chunks():
+    # chunks of both gate ranges (single reference and sub-block) in one segment
+    run_and_check(1, 1, 1100, 128, 128, 4, "bf16", steep_chunks=True, h0=True)
+    run_and_check(1, 2, 700, 128, 129, 16, "bf16", gate_mean=-3.0)
 
 
 def test_outputs_fully_written_and_deterministic():
