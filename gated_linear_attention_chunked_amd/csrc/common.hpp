@@ -304,5 +304,37 @@ __device__ __forceinline__ float wave_sum16(float x) {
   x += __shfl_xor(x, 32);
   return x;
 }
+// The same two reductions with VALU lane swaps instead of LDS permutes.
+// v_permlane32_swap a, b exchanges the upper 32 lanes of a with the lower 32
+// lanes of b; v_permlane16_swap does the same for the odd 16-lane rows of a and
+// the even rows of b.  Started from a = b = x, lane l then holds
+// x[l mod 32] and x[32 + l mod 32] (respectively rows 2k and 2k+1), and every
+// lane ends with the identical value.  Written as asm with both registers
+// read and written: this compiler's builtins for these instructions lose the
+// second result when both results feed one expression.
+__device__ __forceinline__ void lane_swap32(u32& a, u32& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap16(u32& a, u32& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float swap_max16(float x) {
+  u32 a = __builtin_bit_cast(u32, x), b = a;
+  lane_swap32(a, b);
+  const float m = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  a = __builtin_bit_cast(u32, m);
+  b = a;
+  lane_swap16(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float swap_sum16(float x) {
+  u32 a = __builtin_bit_cast(u32, x), b = a;
+  lane_swap32(a, b);
+  const float m = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(u32, m);
+  b = a;
+  lane_swap16(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
 
 }  // namespace lz

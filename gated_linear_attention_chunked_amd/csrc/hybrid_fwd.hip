@@ -534,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, L[b][i]);
-      m = wave_max16(m);
+      m = swap_max16(m);
       const int row = 16 * qb + r16;
       if (g == 0) sm.pmax[H][row] = m;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           L[b][i] = exp2_fast(fmaf(L[b][i], scale_log2, ms));
           l += L[b][i];
         }
-      l = wave_sum16(l);
+      l = swap_sum16(l);
       if (g == 0) sm.psum[H][row] = l;
 #pragma unroll
       for (int x = 0; x < NR; ++x)
