@@ -18,12 +18,13 @@
 //              (waves 0-2, one 16x16 block each) the masked intra scores
 //            producers (waves 4-7): window scores of query rows 16(p&1).. over
 //              one half of the keys (ring chunks c-4..c-2, or c-1, c and the
-//              meta slots), the row maxima exchanged with the partner wave
-//              through LDS; exponentials and row sums -> LDS
+//              meta slots); exponentials from that half's own row maxima;
+//              maxima, row sums and exponentials -> LDS
 //   ---- barrier
-//   phase 2  consumers: O += A V (intra) + (P V over the V^T ring and the meta
-//              values) * mix / (l_0 + l_1); store o; v of chunk c+1 into the
-//              V^T ring
+//   phase 2  consumers: O += A V (intra) + the two halves' P V (V^T ring, meta
+//              values), each scaled by f_h mix / (f_0 l_0 + f_1 l_1) with
+//              f_h = 2^{(m_h - max(m_0, m_1)) scale}; store o; v of chunk c+1
+//              into the V^T ring
 //            producers: gate chunk c+1 (log2-gate cumsum, gated q and k tiles,
 //              k^T for the state update), raw q and raw k of c+1 into LDS;
 //              issue the loads of chunk c+3
@@ -64,9 +65,8 @@ struct Smem {
   alignas(16) float eR[2][kD];   // 2^{R_i} (1 for single-reference channels)
   alignas(16) float vij[kD];     // 2^{R_1 - R_0} (likewise)
   float pmax[2][kC];             // window: per key half, row maxima of the raw scores
-  float psum[2][kC];             // per key half, row sums of the exponentials
-  int fastw[4];
-  int flag[4];                   // per producer wave: chunk + 1 once its row maxima are written                  // per producer wave: its channels take one reference
+  float psum[2][kC];             // per key half, row sums of exponentials taken from that maximum
+  int fastw[4];                  // per producer wave: its channels take one reference
 };
 
 // [rows][128] and [rows][32] tiles, granules permuted by row
@@ -126,7 +126,6 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   // tiles that stay zero: the intra block above the diagonal, unused meta columns
   for (int e = tid; e < 16 * 16; e += 512) sm.a[at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
   for (int e = tid; e < kC * 16; e += 512) sm.p[kRing][at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
-  if (tid < 4) sm.flag[tid] = 0;
   {
     const bf16* mkh = mk + (size_t)h * M * kD;
     const bf16* mvh = mv + (size_t)h * M * kD;
@@ -274,40 +273,55 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) mma(O[nt][qb], vf[nt], af[qb]);
       }
-      // ---- phase 2: window, O^T[n][t] += sum_s vT[n][s] P[t][s] over the ring
-      // (slot of chunk c-4+r is (c+1+r) mod 5; meta slots >= M and P of keys
-      // outside the window are zero)
+      // ---- phase 2: window, O^T[n][t] += sum_s vT[n][s] P[t][s] over the ring.
+      // Slot of chunk c-4+r is (c+1+r) mod 5; meta slots >= M and P of keys
+      // outside the window are zero.  The two key halves (ring chunks c-4..c-2;
+      // c-1, c and the meta slots) carry exponentials from their own row
+      // maxima m_h with sums l_h: with m = max(m_0, m_1), f_h = 2^{(m_h - m) s},
+      // half h's product is scaled by f_h mix / (f_0 l_0 + f_1 l_1).
       {
-        const int s0 = (c + 1) % kRing;
-        bf16x8 wf[kRing + 1][2], pf[kRing + 1][2];
-        f32x4 Ow[2][2];  // window branch, unnormalised
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) Ow[nt][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r <= kRing; ++r) {
-          const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            wf[r][nt] = r == kRing - 1 ? vf[nt]
-                      : r == kRing     ? ld8<bf16>(&sm.mvT[at4(32 * cw + 16 * nt + r16, 8 * g)])
-                                       : ld8<bf16>(&sm.vT[sl][at4(32 * cw + 16 * nt + r16, 8 * g)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) pf[r][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
-        }
-#pragma unroll
-        for (int r = 0; r <= kRing; ++r)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) mma(Ow[nt][qb], wf[r][nt], pf[r][qb]);
+        float sc[2][2];  // [half][qb]
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int row = 16 * qb + r16;
-          const float sc = mix / (sm.psum[0][row] + sm.psum[1][row]);
+          const float m0 = sm.pmax[0][row], m1 = sm.pmax[1][row];
+          const float mm = fmaxf(m0, m1);
+          const float f0 = exp2_fast((m0 - mm) * scale_log2), f1 = exp2_fast((m1 - mm) * scale_log2);
+          const float inv = mix / (f0 * sm.psum[0][row] + f1 * sm.psum[1][row]);
+          sc[0][qb] = f0 * inv;
+          sc[1][qb] = f1 * inv;
+        }
+        const int s0 = (c + 1) % kRing;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) O[nt][qb] += Ow[nt][qb] * sc;
+        for (int h = 0; h < 2; ++h) {
+          const int r0 = h == 0 ? 0 : 3, r1 = h == 0 ? 2 : kRing;  // ring chunks (kRing: meta)
+          bf16x8 wf[3][2], pf[3][2];
+#pragma unroll
+          for (int r = r0; r <= r1; ++r) {
+            const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+              wf[r - r0][nt] = r == kRing - 1 ? vf[nt]
+                             : r == kRing     ? ld8<bf16>(&sm.mvT[at4(32 * cw + 16 * nt + r16, 8 * g)])
+                                              : ld8<bf16>(&sm.vT[sl][at4(32 * cw + 16 * nt + r16, 8 * g)]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) pf[r - r0][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
+          }
+          f32x4 Ow[2][2];  // this half of the window branch, unnormalised
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) Ow[nt][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = r0; r <= r1; ++r)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb) mma(Ow[nt][qb], wf[r - r0][nt], pf[r - r0][qb]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) O[nt][qb] += Ow[nt][qb] * sc[h][qb];
         }
       }
       // v of chunk c+1 into the slot of chunk c-4 (read above by this wave only);
@@ -470,10 +484,9 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     };
     // Window scores of query rows 16qb..16qb+15 of chunk c over one half of
     // the keys: ring chunks c-4..c-2 (half 0) or c-1, c and the meta slots
-    // (half 1).  Producers pw and pw^2 hold the two halves of the same rows and
-    // exchange their row maxima through LDS (a per-chunk flag, no work-group
-    // barrier); each writes its exponentials and row sums, and the consumers
-    // scale the product by mix / (l_0 + l_1).
+    // (half 1), one producer per (query block, half).  Each half's
+    // exponentials are taken from its own row maximum; the row maxima and sums
+    // go to LDS, and the consumers combine the two halves.
     auto window = [&](int c, int qb, auto half) {
       constexpr int H = decltype(half)::value;
       constexpr int R0 = H == 0 ? 0 : 3, NR = H == 0 ? 3 : 2;  // ring chunks r = R0 .. R0+NR-1
@@ -529,26 +542,17 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
         for (int i = 0; i < 4; ++i) L[NB - 1][i] = (4 * g + i < M) ? L[NB - 1][i] : -INFINITY;
       }
+      // exponentials from this half's own row maximum (scale > 0); a row with
+      // no key in this half keeps m at a finite floor, so its terms are 0 and
+      // the consumers' factor 2^{(m_h - m) s} underflows to 0
       float m = -INFINITY;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, L[b][i]);
-      m = swap_max16(m);
+      m = fmaxf(swap_max16(m), -1e30f);
       const int row = 16 * qb + r16;
       if (g == 0) sm.pmax[H][row] = m;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (lane == 0) *reinterpret_cast<volatile int*>(&sm.flag[pw]) = c + 1;
-      // the partner wave publishes its maxima for this chunk in the same phase;
-      // the wait is bounded so that a fault in this protocol cannot hang the GPU
-      for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (*reinterpret_cast<volatile int*>(&sm.flag[pw ^ 2]) > c) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      asm volatile("" ::: "memory");
-      // exact softmax over raw scores (scale > 0): key s = t lies in half 1, so
-      // the combined maximum is finite; the scale enters the exponent's fma
-      m = fmaxf(m, sm.pmax[1 - H][row]);
       const float ms = -m * scale_log2;
       float l = 0.f;
 #pragma unroll
