@@ -447,31 +447,39 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[4], e[5], e[6], e[7]};
         }
       }
-      // gated tiles, rounded to bf16 pairs as they are made
+      // gated tiles, rounded to bf16 pairs as they are made (the element loop
+      // is specialised on the uniform form: the single reference is 0)
       u32 qw[2][4], kw[2][4];
+      auto tiles = [&](auto single) {
+        constexpr bool kSingle = decltype(single)::value;
 #pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) {
-        float kx[2][2];
+        for (int c2 = 0; c2 < 4; ++c2) {
+          float kx[2][2];
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          float qx[2];
+          for (int rr = 0; rr < 2; ++rr) {
+            float qx[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int c = 2 * c2 + u;
+              const float d = kSingle ? b[rr][c] : b[rr][c] - Ri[c];
+              qx[u] = bf_at(x.q[rr], c) * exp2_fast(d);
+              kx[rr][u] = bf_at(x.k[rr], c) * exp2_fast(-d);
+            }
+            qw[rr][c2] = pack_bf2(qx[0], qx[1]);
+            kw[rr][c2] = pack_bf2(kx[rr][0], kx[rr][1]);
+          }
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int c = 2 * c2 + u;
-            const float d = b[rr][c] - Ri[c];
-            qx[u] = bf_at(x.q[rr], c) * exp2_fast(d);
-            kx[rr][u] = bf_at(x.k[rr], c) * exp2_fast(-d);
+            const float e = kSingle ? dl[c] : eKh[c];
+            *reinterpret_cast<u32*>(&sm.khT[at4(ch0 + c, 2 * rq)]) = pack_bf2(kx[0][u] * e, kx[1][u] * e);
           }
-          qw[rr][c2] = pack_bf2(qx[0], qx[1]);
-          kw[rr][c2] = pack_bf2(kx[rr][0], kx[rr][1]);
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int c = 2 * c2 + u;
-          *reinterpret_cast<u32*>(&sm.khT[at4(ch0 + c, 2 * rq)]) =
-              pack_bf2(kx[0][u] * eKh[c], kx[1][u] * eKh[c]);
-        }
-      }
+      };
+      if (fast)
+        tiles(std::true_type());
+      else
+        tiles(std::false_type());
       bf16* kring = sm.kr[ch % kRing];
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
