@@ -170,10 +170,15 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v,
 # ---------------------------------------------------------------------------
 # Backward (manual reverse mode of the definitions above)
 # ---------------------------------------------------------------------------
-def gla_backward(q, k, v, log_alpha, dO, h0=None, checkpoint=64):
-    """Reverse mode of gla_forward for the loss L = sum(dO * o).
+def gla_backward(q, k, v, log_alpha, dO, h0=None, checkpoint=64, dhT=None):
+    """Reverse mode of gla_forward for the loss L = sum(dO * o) + sum(dhT * hT).
 
-    Walks t = T-1 .. 0 with G = dL/dS_t:
+    dhT (optional, default 0) is the gradient of L with respect to the final
+    state hT: the state is the layer's constant-size memory [LZ-2a, LZ-4], so a
+    long sequence can be run in segments with hT of one segment as h0 of the
+    next, and the segments' backward passes are then chained the same way
+    (dh0 of a segment is dhT of the one before).
+    Walks t = T-1 .. 0 with G = dL/dS_t (G = dhT before the last token):
         G += q_t^T dO_t;  dq_t = S_t dO_t;  dk_t = G v_t;  dv_t = G^T k_t;
         dlog_alpha_t = alpha_t * rowsum(G * S_{t-1});  G <- diag(alpha_t) G.
     The states S_{t-1} are recomputed forward from checkpoints taken every
@@ -195,7 +200,7 @@ def gla_backward(q, k, v, log_alpha, dO, h0=None, checkpoint=64):
     dk_ = np.zeros_like(k)
     dv_ = np.zeros_like(v)
     dla = np.zeros_like(la)
-    G = np.zeros((B, H, dk, dv))
+    G = np.zeros((B, H, dk, dv)) if dhT is None else _f64(dhT).copy()
     for t0 in reversed(starts):
         t1 = min(T, t0 + checkpoint)
         states = [entering[t0]]                        # states[i] = S_{t0+i-1}
@@ -254,14 +259,16 @@ def window_meta_backward(q, k, v, meta_k, meta_v, window, scale, dO_swa):
     return dict(dq=dq, dk=dk_, dv=dv_, dmeta_k=dmk, dmeta_v=dmv)
 
 
-def hybrid_backward(q, k, v, log_alpha, meta_k, meta_v, window, scale, dO, mix=1.0, h0=None):
-    """Reverse mode of hybrid_forward for L = sum(dO * o) [LZ-2a weighted sum].
+def hybrid_backward(q, k, v, log_alpha, meta_k, meta_v, window, scale, dO, mix=1.0, h0=None,
+                    dhT=None):
+    """Reverse mode of hybrid_forward for L = sum(dO * o) + sum(dhT * hT)
+    [LZ-2a weighted sum; dhT as in gla_backward, default 0].
 
     dO_gla = dO and dO_swa = mix * dO; gradients of the two branches add.
     Returns dict(dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dh0).
     """
     dO = _f64(dO)
-    g = gla_backward(q, k, v, log_alpha, dO, h0)
+    g = gla_backward(q, k, v, log_alpha, dO, h0, dhT=dhT)
     w = window_meta_backward(q, k, v, meta_k, meta_v, window, scale, mix * dO)
     return dict(dq=g["dq"] + w["dq"], dk=g["dk"] + w["dk"], dv=g["dv"] + w["dv"],
                 dlog_alpha=g["dlog_alpha"], dmeta_k=w["dmeta_k"],

@@ -278,6 +278,56 @@ def test_I9_gradients_match_central_differences(mix):
         assert rel(g[gname], fd) < 1e-6, arg
 
 
+def test_state_gradient_matches_central_differences():
+    # loss with a term through the final state: L = sum(dO * o) + sum(dhT * hT)
+    B, H, T, d, w, M, s = 1, 1, 11, 4, 3, 2, 0.8
+    args = dict(q=rand(B, H, T, d), k=rand(B, H, T, d), v=rand(B, H, T, d),
+                log_alpha=logsig(rand(B, H, T, d) + 0.5), meta_k=rand(H, M, d),
+                meta_v=rand(H, M, d), h0=rand(B, H, d, d))
+    dO, dhT = rand(B, H, T, d), rand(B, H, d, d)
+
+    def loss():
+        r = oracle.hybrid_forward(window=w, scale=s, mix=0.9, **args)
+        return float((r["o"] * dO).sum() + (r["hT"] * dhT).sum())
+
+    g = oracle.hybrid_backward(args["q"], args["k"], args["v"], args["log_alpha"], args["meta_k"],
+                               args["meta_v"], w, s, dO, mix=0.9, h0=args["h0"], dhT=dhT)
+    h = 1e-6
+    for arg, gname in dict(q="dq", k="dk", v="dv", log_alpha="dlog_alpha", h0="dh0").items():
+        x = args[arg]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = loss()
+            x[idx] = keep - h
+            lm = loss()
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        assert rel(g[gname], fd) < 1e-6, arg
+
+
+def test_state_gradient_chains_over_segments():
+    # a sequence run as two segments (hT of the first as h0 of the second) has
+    # the same outputs, and chaining dh0 of the second segment into dhT of the
+    # first gives the whole sequence's gradients
+    B, H, T, T1, d = 2, 1, 90, 37, 5
+    q, k, v = rand(B, H, T, d), rand(B, H, T, d), rand(B, H, T, 3)
+    la, dO, h0 = logsig(rand(B, H, T, d) + 1.5), rand(B, H, T, 3), rand(B, H, d, 3)
+    full = oracle.gla_backward(q, k, v, la, dO, h0=h0)
+    a, b = slice(0, T1), slice(T1, T)
+    o1, h1 = oracle.gla_forward(q[:, :, a], k[:, :, a], v[:, :, a], la[:, :, a], h0)
+    o2, _ = oracle.gla_forward(q[:, :, b], k[:, :, b], v[:, :, b], la[:, :, b], h1)
+    o_full, _ = oracle.gla_forward(q, k, v, la, h0)
+    assert rel(np.concatenate([o1, o2], axis=2), o_full) < 1e-13
+    g2 = oracle.gla_backward(q[:, :, b], k[:, :, b], v[:, :, b], la[:, :, b], dO[:, :, b], h0=h1)
+    g1 = oracle.gla_backward(q[:, :, a], k[:, :, a], v[:, :, a], la[:, :, a], dO[:, :, a], h0=h0,
+                             dhT=g2["dh0"])
+    for key in ("dq", "dk", "dv", "dlog_alpha"):
+        assert rel(np.concatenate([g1[key], g2[key]], axis=2), full[key]) < 1e-12, key
+    assert rel(g1["dh0"], full["dh0"]) < 1e-12
+
+
 def test_I9_dlog_alpha_identity_over_chunks():
     # GLA part only: dlog_alpha = reverse cumsum over the sequence of q*dq - k*dk
     B, H, T, d = 2, 2, 150, 6
