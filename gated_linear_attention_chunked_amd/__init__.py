@@ -143,8 +143,10 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
 
 
 def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale=None, mix=1.0,
-               h0=None):
-    """Gradients of sum(dO * o).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v."""
+               h0=None, dhT=None, return_dh0=False):
+    """Gradients of sum(dO * o) + sum(dhT * hT) (dhT: the gradient of the final
+    state, optional).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v and,
+    with return_dh0, dh0 (the gradient of the initial state)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -154,6 +156,7 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
     _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
     _opt(h0, "h0", (B, H, dk, dv), torch.float32)
+    _opt(dhT, "dhT", (B, H, dk, dv), torch.float32)
     _need(o_swa, "o_swa", (B, H, T, dv), dt)
     _need(lse, "lse", (B, H, T), torch.float32)
     _need(dO, "dO", (B, H, T, dv), dt)
@@ -162,13 +165,15 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
          "dlog_alpha": torch.empty_like(log_alpha),
          "dmeta_k": torch.empty(H, M, dk, device=dev, dtype=torch.float32),
          "dmeta_v": torch.empty(H, M, dv, device=dev, dtype=torch.float32)}
+    if return_dh0:
+        g["dh0"] = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
     nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
     ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
     _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]), _p(g["dlog_alpha"]),
-        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(ws), nws, _stream()))
+        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")), _p(ws), nws, _stream()))
     return g
 
 

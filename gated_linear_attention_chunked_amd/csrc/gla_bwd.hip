@@ -82,7 +82,8 @@ __device__ __forceinline__ float wave_scan64(float x) {
 __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
-    bf16* __restrict__ S_all, bf16* __restrict__ dS_all, int BH, int T_len) {
+    const float* __restrict__ dhT, float* __restrict__ dh0, bf16* __restrict__ S_all,
+    bf16* __restrict__ dS_all, int BH, int T_len) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4, odd = lane & 1;
@@ -99,8 +100,11 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   f32x4 a1[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (!rev && h0) {
-    const float* hp = h0 + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
+  // the forward scan starts from h0, the reverse scan from dhT (the gradient of
+  // the final state), both [c][j] row-major; absent ones are zero
+  const float* start = rev ? dhT : h0;
+  if (start) {
+    const float* hp = start + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) a1[jb] = *reinterpret_cast<const f32x4*>(hp + 16 * jb);
   }
@@ -198,6 +202,12 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   for (int n = 0; n < nc; n += 2) {
     step(A, n);
     if (n + 1 < nc) step(B, n + 1);
+  }
+  // after chunk 0 the reverse scan holds dS_0, the gradient of the initial state
+  if (rev && dh0) {
+    float* hp = dh0 + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) *reinterpret_cast<f32x4*>(hp + 16 * jb) = a1[jb];
   }
 }
 
@@ -671,8 +681,8 @@ size_t gla_bwd_workspace_bytes(const Shape& s) {
 
 // Scans: S_c and dS_{c+1} for every chunk, into ws.
 hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const float* h0, const void* dO, void* ws,
-                                hipStream_t st) {
+                                const float* la, const float* h0, const float* dhT, float* dh0,
+                                const void* dO, void* ws, hipStream_t st) {
   typedef bf16 T;
   const int nc = (s.T + kC - 1) / kC;
   const int BH = s.B * s.H;
@@ -680,8 +690,8 @@ hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, co
   T* S_all = (T*)ws;
   T* dS_all = S_all + (size_t)BH * nc * kD * kD;
   hipLaunchKernelGGL(gla_bwd_scans, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, h0, S_all, dS_all, BH,
-                     s.T);
+                     (const T*)k, (const T*)v, la, (const T*)dO, h0, dhT, dh0, S_all, dS_all,
+                     BH, s.T);
   return hipGetLastError();
 }
 

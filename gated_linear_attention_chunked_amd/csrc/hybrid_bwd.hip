@@ -8,8 +8,8 @@ namespace lz {
 size_t gla_bwd_workspace_bytes(const Shape& s);
 size_t swa_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const float* h0, const void* dO, void* ws,
-                                hipStream_t st);
+                                const float* la, const float* h0, const float* dhT, float* dh0,
+                                const void* dO, void* ws, hipStream_t st);
 hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
                                 const float* la, const void* dO, void* dq, void* dk, void* dv,
                                 float* dla, const void* ws, hipStream_t st);
@@ -38,14 +38,18 @@ size_t bwd_workspace_bytes(const Shape& s) {
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
                              const float* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
-                             void* dk, void* dv, float* dla, float* dmk, float* dmv, void* ws,
-                             hipStream_t st) {
+                             void* dk, void* dv, float* dla, float* dmk, float* dmv,
+                             const float* dhT, float* dh0, void* ws, hipStream_t st) {
   if (s.T == 0 || s.B == 0) {
-    // no tokens: the meta-memory gradients are zero
+    // no tokens: the meta-memory gradients are zero, dh0 = dhT (or zero)
     const size_t n = (size_t)s.H * s.n_meta * s.dk;
     if (n > 0) {
       hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, dmk, n);
       hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, dmv, n);
+    }
+    if (dh0) {
+      const hipError_t e = launch_state_copy(s, dhT, dh0, st);
+      if (e != hipSuccess) return e;
     }
     return hipGetLastError();
   }
@@ -53,7 +57,7 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
   char* wswa = w + align256(gla_bwd_workspace_bytes(s));
   // The window branch writes dq, dk, dv; the GLA grad kernel (after the scans
   // that produce its states) adds its gradients to them.
-  hipError_t e = launch_gla_bwd_scans(s, q, k, v, la, h0, dO, w, st);
+  hipError_t e = launch_gla_bwd_scans(s, q, k, v, la, h0, dhT, dh0, dO, w, st);
   if (e != hipSuccess) return e;
   e = launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv, wswa, st);
   if (e != hipSuccess) return e;

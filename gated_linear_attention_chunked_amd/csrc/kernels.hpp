@@ -64,7 +64,7 @@ size_t bwd_workspace_bytes(const Shape& s);
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
                              const float* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
-                             void* dk, void* dv, float* dla, float* dmk, float* dmv, void* ws,
-                             hipStream_t st);
+                             void* dk, void* dv, float* dla, float* dmk, float* dmv,
+                             const float* dhT, float* dh0, void* ws, hipStream_t st);
 
 }  // namespace lz

@@ -123,21 +123,28 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
                                   void* o_swa, float* hT, void* ring_k, void* ring_v,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Hybrid backward for the loss sum(dO * o).  Reads the forward inputs plus the
- * o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv (desc->dtype),
- * dlog_alpha [B,H,T,dk], dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all float32 except
- * dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as in the forward
- * (its own gradient is not produced).  ws must hold lizard_workspace_bytes(desc,
- * LIZARD_OP_HYBRID_BWD) bytes: two bf16 dk x dv matrices per 64-token chunk
- * and head (S_c and dS_{c+1}) plus small per-token and per-tile buffers, so it
- * grows linearly with T.
+/* Hybrid backward for the loss sum(dO * o) + sum(dhT * hT).  Reads the forward
+ * inputs plus the o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv
+ * (desc->dtype), dlog_alpha [B,H,T,dk], dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all
+ * float32 except dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as
+ * in the forward.  dhT [B,H,dk,dv] float32 (nullable = zero) is the gradient of
+ * the final state hT; dh0 [B,H,dk,dv] float32 (nullable = not written) receives
+ * the gradient of the initial state.  A sequence run in segments (hT of one
+ * segment as h0 of the next, the window branch given its own inputs) is
+ * differentiated by chaining dh0 of a segment into dhT of the one before, the
+ * constant-size state of "Lizard: An Efficient Linearization Framework for Large
+ * Language Models" (gist.science summary, sections 2(a) and 4).  ws must hold
+ * lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_BWD) bytes: two bf16 dk x dv
+ * matrices per 64-token chunk and head (S_c and dS_{c+1}) plus small per-token
+ * and per-tile buffers, so it grows linearly with T.
  * This version supports BF16 with dk = dv = 64 (LIZARD_E_UNSUPPORTED otherwise). */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk,
                                   void* dv, float* dlog_alpha, float* dmeta_k, float* dmeta_v,
-                                  void* ws, size_t ws_bytes, hipStream_t stream);
+                                  const float* dhT, float* dh0, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* One constant-memory generation step for B sequences (desc->T is ignored).
  * q, k [B,H,dk], v [B,H,dv] in desc->dtype; log_alpha [B,H,dk] float32.
