@@ -264,12 +264,15 @@ def hybrid_backward(q, k, v, log_alpha, meta_k, meta_v, window, scale, dO, mix=1
     """Reverse mode of hybrid_forward for L = sum(dO * o) + sum(dhT * hT)
     [LZ-2a weighted sum; dhT as in gla_backward, default 0].
 
-    dO_gla = dO and dO_swa = mix * dO; gradients of the two branches add.
-    Returns dict(dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dh0).
+    dO_gla = dO and dO_swa = mix * dO; gradients of the two branches add.  The
+    mix weight enters only the final sum, so dmix = sum(dO * o_swa).
+    Returns dict(dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dh0, dmix).
     """
     dO = _f64(dO)
     g = gla_backward(q, k, v, log_alpha, dO, h0, dhT=dhT)
     w = window_meta_backward(q, k, v, meta_k, meta_v, window, scale, mix * dO)
     return dict(dq=g["dq"] + w["dq"], dk=g["dk"] + w["dk"], dv=g["dv"] + w["dv"],
                 dlog_alpha=g["dlog_alpha"], dmeta_k=w["dmeta_k"],
-                dmeta_v=w["dmeta_v"], dh0=g["dh0"])
+                dmeta_v=w["dmeta_v"], dh0=g["dh0"],
+                dmix=float((dO * window_meta_attention(q, k, v, meta_k, meta_v, window,
+                                                       scale)[0]).sum()))

@@ -276,6 +276,11 @@ def test_I9_gradients_match_central_differences(mix):
             x[idx] = keep
             fd[idx] = (lp - lm) / (2 * h)
         assert rel(g[gname], fd) < 1e-6, arg
+    # the mix weight
+    h = 1e-6
+    fd_mix = (_loss(dO, window=w, scale=s, mix=mix + h, **args)
+              - _loss(dO, window=w, scale=s, mix=mix - h, **args)) / (2 * h)
+    assert abs(g["dmix"] - fd_mix) < 1e-7 * max(1.0, abs(fd_mix))
 
 
 def test_state_gradient_matches_central_differences():
