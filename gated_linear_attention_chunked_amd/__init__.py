@@ -143,10 +143,11 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
 
 
 def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale=None, mix=1.0,
-               h0=None, dhT=None, return_dh0=False):
+               h0=None, dhT=None, return_dh0=False, return_dmix=False):
     """Gradients of sum(dO * o) + sum(dhT * hT) (dhT: the gradient of the final
     state, optional).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v and,
-    with return_dh0, dh0 (the gradient of the initial state)."""
+    with return_dh0, dh0 (the gradient of the initial state), with return_dmix,
+    dmix (a one-element float32 tensor, the gradient of the mix weight)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -167,13 +168,16 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
          "dmeta_v": torch.empty(H, M, dv, device=dev, dtype=torch.float32)}
     if return_dh0:
         g["dh0"] = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    if return_dmix:
+        g["dmix"] = torch.empty(1, device=dev, dtype=torch.float32)
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
     nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
     ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
     _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]), _p(g["dlog_alpha"]),
-        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")), _p(ws), nws, _stream()))
+        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")), _p(g.get("dmix")), _p(ws), nws,
+        _stream()))
     return g
 
 

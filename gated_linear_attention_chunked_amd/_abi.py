@@ -37,7 +37,7 @@ _SIGS = {
     "lizard_gla_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P, ctypes.c_size_t, P]),
     "lizard_swa_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P]),
     "lizard_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P, ctypes.c_size_t, P]),
-    "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 18 + [P, ctypes.c_size_t, P]),
+    "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 19 + [P, ctypes.c_size_t, P]),
     "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 11 + [P]),
     "lizard_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lizard_version": (ctypes.c_int32, []),

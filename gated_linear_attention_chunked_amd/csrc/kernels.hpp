@@ -65,6 +65,6 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
                              const float* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
                              void* dk, void* dv, float* dla, float* dmk, float* dmv,
-                             const float* dhT, float* dh0, void* ws, hipStream_t st);
+                             const float* dhT, float* dh0, float* dmix, void* ws, hipStream_t st);
 
 }  // namespace lz

@@ -142,8 +142,8 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
                                   float* dlog_alpha, float* dmeta_k, float* dmeta_v,
-                                  const float* dhT, float* dh0, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  const float* dhT, float* dh0, float* dmix, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
   const bool meta = desc->n_meta > 0 && desc->H > 0;
@@ -159,7 +159,7 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   return hip_status(lz::launch_hybrid_bwd(s, q, k, v, log_alpha, meta_k, meta_v, h0, o_swa, lse,
                                           dO, dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dhT, dh0,
-                                          ws, stream));
+                                          dmix, ws, stream));
 }
 
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,

@@ -129,7 +129,9 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
  * float32 except dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as
  * in the forward.  dhT [B,H,dk,dv] float32 (nullable = zero) is the gradient of
  * the final state hT; dh0 [B,H,dk,dv] float32 (nullable = not written) receives
- * the gradient of the initial state.  A sequence run in segments (hT of one
+ * the gradient of the initial state; dmix (one float32, nullable = not written)
+ * receives the gradient of the mix weight, sum(dO * o_swa), summed in a fixed
+ * order.  A sequence run in segments (hT of one
  * segment as h0 of the next, the window branch given its own inputs) is
  * differentiated by chaining dh0 of a segment into dhT of the one before, the
  * constant-size state of "Lizard: An Efficient Linearization Framework for Large
@@ -143,8 +145,8 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk,
                                   void* dv, float* dlog_alpha, float* dmeta_k, float* dmeta_v,
-                                  const float* dhT, float* dh0, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  const float* dhT, float* dh0, float* dmix, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* One constant-memory generation step for B sequences (desc->T is ignored).
  * q, k [B,H,dk], v [B,H,dv] in desc->dtype; log_alpha [B,H,dk] float32.

@@ -124,10 +124,10 @@ def test_backward_workspace_and_support():
     d = desc(T=256)
     need = lib.lizard_workspace_bytes(ctypes.byref(d), 3)
     assert need > 0
-    st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 18), FAKE, need - 1, None)
+    st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 19), FAKE, need - 1, None)
     assert st == 5
     # this version's backward covers bf16 with d = 64
     for kw in (dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32)):
         d2 = desc(**kw)
         assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
-        assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 18), FAKE, 1 << 30, None) == 4
+        assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 19), FAKE, 1 << 30, None) == 4

@@ -32,7 +32,7 @@ def run_grads(inp, w, s, mix, h0=None, dhT=None):
                       scale=s, mix=mix, h0=h0d, save_for_backward=True, return_state=True)
     g = lz.hybrid_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], w,
                       f["o_swa"], f["lse"], x["dO"], scale=s, mix=mix, h0=h0d, dhT=dhTd,
-                      return_dh0=True)
+                      return_dh0=True, return_dmix=True)
     torch.cuda.synchronize()
     g["hT"] = f["hT"]
     return g
@@ -70,6 +70,19 @@ def check(B, H, T, w, M, seed=0, mix=1.0, gate_mean=2.0, with_h0=False, steep_ch
         if n.startswith("dmeta") and M == 0:
             continue
         assert_close(n, g[n], ref[n], BF)
+    check_dmix(g["dmix"], ref["dmix"], inp, w, s)
+
+
+def check_dmix(got, ref, inp, w, s):
+    # dmix = sum(dO * o_swa): o_swa is saved in bf16 (relative rounding <= 2^-8
+    # per element) and the sum runs in fp32, so |error| <= 2^-8 sum(|dO| |o_swa|);
+    # the bound is on that scale because the sum itself may cancel
+    r = f64(inp)
+    o_swa, _ = oracle.window_meta_attention(r["q"], r["k"], r["v"], r["meta_k"], r["meta_v"], w, s)
+    scale = float((np.abs(r["dO"]) * np.abs(o_swa)).sum())
+    err = abs(float(got.item()) - ref)
+    print(f"  dmix: {float(got.item()):.6e} vs {ref:.6e} (error {err:.2e}, bound scale {scale:.2e})")
+    assert err <= 2.0 ** -8 * scale
 
 
 @pytest.mark.parametrize("T,w,M", [(64, 64, 4), (200, 64, 4), (257, 16, 16), (130, 1, 0),
@@ -131,7 +144,7 @@ def test_backward_deterministic():
     inp = make_inputs(2, 2, 300, 64, 64, 4, dtype="bf16", seed=9, with_grad_out=True)
     a = run_grads(inp, 64, 0.125, 1.0)
     b = run_grads(inp, 64, 0.125, 1.0)
-    for n in NAMES + ("hT",):
+    for n in NAMES + ("hT", "dmix"):
         assert torch.equal(a[n], b[n]), n
 
 
