@@ -31,6 +31,9 @@ the design notes):
     and denominator); the sink-only reading is the special case meta_v = 0.
   * the mix weight of the window branch is a scalar `mix` (the pages call it
     alpha, which would clash with the decay).
+  * the two branches may read different query/key inputs (the GLA branch its
+    feature-mapped q, k; the window branch its own q_w, k_w); by default both
+    read the same q, k.
 
 All arrays are numpy, laid out [B, H, T, D]; computations run in float64.
 """
@@ -124,30 +127,39 @@ def ring_from_sequence(k, v, window):
     return rk, rv
 
 
-def hybrid_forward(q, k, v, log_alpha, meta_k, meta_v, window, scale, mix=1.0, h0=None):
+def hybrid_forward(q, k, v, log_alpha, meta_k, meta_v, window, scale, mix=1.0, h0=None,
+                   q_w=None, k_w=None):
     """Hybrid layer output o = o_gla + mix * o_swa [LZ-2a, final weighted sum].
 
-    Returns a dict with o, o_gla, o_swa, lse, hT, ring_k, ring_v.
+    The GLA branch reads q, k; the window branch reads q_w, k_w (default q, k)
+    [LZ-2a: the gated branch takes feature-mapped queries and keys, the
+    window branch its own].  Returns a dict with o, o_gla, o_swa, lse, hT,
+    ring_k, ring_v (the window cache holds the window branch's keys).
     """
+    q_w = q if q_w is None else q_w
+    k_w = k if k_w is None else k_w
     o_gla, hT = gla_forward(q, k, v, log_alpha, h0)
-    o_swa, lse = window_meta_attention(q, k, v, meta_k, meta_v, window, scale)
-    rk, rv = ring_from_sequence(k, v, window)
+    o_swa, lse = window_meta_attention(q_w, k_w, v, meta_k, meta_v, window, scale)
+    rk, rv = ring_from_sequence(k_w, v, window)
     return dict(o=o_gla + mix * o_swa, o_gla=o_gla, o_swa=o_swa, lse=lse,
                 hT=hT, ring_k=rk, ring_v=rv)
 
 
 def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v,
-                window, scale, mix=1.0):
+                window, scale, mix=1.0, q_w=None, k_w=None):
     """One constant-memory generation step [LZ-2a state update; LZ-4].
 
     pos[b] tokens have been seen by sequence b.  The new token (q, k, v,
-    log_alpha: [B,H,d]) updates the state exactly as one step of gla_forward,
-    is written to ring slot pos mod w, and attends over the min(pos+1, w)
-    filled slots plus the meta slots.  Returns (o [B,H,dv], state', ring_k',
-    ring_v', pos + 1); the inputs are not modified.
+    log_alpha: [B,H,d]) updates the state exactly as one step of gla_forward;
+    its window key k_w (default k) is written to ring slot pos mod w, and its
+    window query q_w (default q) attends over the min(pos+1, w) filled slots
+    plus the meta slots.  Returns (o [B,H,dv], state', ring_k', ring_v',
+    pos + 1); the inputs are not modified.
     """
-    q, k, v, la, S, rk, rv, mk, mv = map(
-        _f64, (q, k, v, log_alpha, state, ring_k, ring_v, meta_k, meta_v))
+    q_w = q if q_w is None else q_w
+    k_w = k if k_w is None else k_w
+    q, k, v, la, S, rk, rv, mk, mv, q_w, k_w = map(
+        _f64, (q, k, v, log_alpha, state, ring_k, ring_v, meta_k, meta_v, q_w, k_w))
     pos = np.array(pos, dtype=np.int64, copy=True)
     B, H, dk = q.shape
     S = np.exp(la)[..., :, None] * S + k[..., :, None] * v[..., None, :]
@@ -155,12 +167,12 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v,
     o_swa = np.empty_like(o_gla)
     for b in range(B):
         slot = int(pos[b] % window)
-        rk[b, :, slot, :] = k[b]
+        rk[b, :, slot, :] = k_w[b]
         rv[b, :, slot, :] = v[b]
         n = int(min(pos[b] + 1, window))
         keys = np.concatenate([rk[b, :, :n, :], mk], axis=1)      # [H, n+M, dk]
         vals = np.concatenate([rv[b, :, :n, :], mv], axis=1)
-        logits = scale * np.matmul(keys, q[b, :, :, None])[..., 0]
+        logits = scale * np.matmul(keys, q_w[b, :, :, None])[..., 0]
         e = np.exp(logits - logits.max(axis=-1, keepdims=True))
         p = e / e.sum(axis=-1, keepdims=True)
         o_swa[b] = np.matmul(p[:, None, :], vals)[:, 0, :]
@@ -260,19 +272,28 @@ def window_meta_backward(q, k, v, meta_k, meta_v, window, scale, dO_swa):
 
 
 def hybrid_backward(q, k, v, log_alpha, meta_k, meta_v, window, scale, dO, mix=1.0, h0=None,
-                    dhT=None):
+                    dhT=None, q_w=None, k_w=None):
     """Reverse mode of hybrid_forward for L = sum(dO * o) + sum(dhT * hT)
     [LZ-2a weighted sum; dhT as in gla_backward, default 0].
 
     dO_gla = dO and dO_swa = mix * dO; gradients of the two branches add.  The
-    mix weight enters only the final sum, so dmix = sum(dO * o_swa).
-    Returns dict(dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dh0, dmix).
+    mix weight enters only the final sum, so dmix = sum(dO * o_swa).  With
+    separate window inputs (q_w, k_w given) dq, dk are the GLA branch's and
+    dq_w, dk_w the window branch's; otherwise dq, dk hold both.
+    Returns dict(dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dh0, dmix[, dq_w, dk_w]).
     """
     dO = _f64(dO)
+    sep = q_w is not None or k_w is not None
+    qw = q if q_w is None else q_w
+    kw = k if k_w is None else k_w
     g = gla_backward(q, k, v, log_alpha, dO, h0, dhT=dhT)
-    w = window_meta_backward(q, k, v, meta_k, meta_v, window, scale, mix * dO)
-    return dict(dq=g["dq"] + w["dq"], dk=g["dk"] + w["dk"], dv=g["dv"] + w["dv"],
-                dlog_alpha=g["dlog_alpha"], dmeta_k=w["dmeta_k"],
-                dmeta_v=w["dmeta_v"], dh0=g["dh0"],
-                dmix=float((dO * window_meta_attention(q, k, v, meta_k, meta_v, window,
-                                                       scale)[0]).sum()))
+    w = window_meta_backward(qw, kw, v, meta_k, meta_v, window, scale, mix * dO)
+    out = dict(dv=g["dv"] + w["dv"], dlog_alpha=g["dlog_alpha"], dmeta_k=w["dmeta_k"],
+               dmeta_v=w["dmeta_v"], dh0=g["dh0"],
+               dmix=float((dO * window_meta_attention(qw, kw, v, meta_k, meta_v, window,
+                                                      scale)[0]).sum()))
+    if sep:
+        out.update(dq=g["dq"], dk=g["dk"], dq_w=w["dq"], dk_w=w["dk"])
+    else:
+        out.update(dq=g["dq"] + w["dq"], dk=g["dk"] + w["dk"])
+    return out

@@ -283,6 +283,49 @@ def test_I9_gradients_match_central_differences(mix):
     assert abs(g["dmix"] - fd_mix) < 1e-7 * max(1.0, abs(fd_mix))
 
 
+def test_separate_window_inputs_gradients_match_central_differences():
+    # the window branch reads its own q_w, k_w; the GLA branch q, k
+    B, H, T, d, w, M, s = 1, 1, 12, 4, 4, 2, 0.6
+    args = dict(q=rand(B, H, T, d), k=rand(B, H, T, d), v=rand(B, H, T, d),
+                log_alpha=logsig(rand(B, H, T, d) + 1.0), meta_k=rand(H, M, d),
+                meta_v=rand(H, M, d), q_w=rand(B, H, T, d), k_w=rand(B, H, T, d))
+    dO = rand(B, H, T, d)
+    g = oracle.hybrid_backward(args["q"], args["k"], args["v"], args["log_alpha"], args["meta_k"],
+                               args["meta_v"], w, s, dO, mix=0.8, q_w=args["q_w"], k_w=args["k_w"])
+    h = 1e-6
+    for arg, gname in dict(q="dq", k="dk", q_w="dq_w", k_w="dk_w", v="dv", meta_k="dmeta_k").items():
+        x = args[arg]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(dO, window=w, scale=s, mix=0.8, **args)
+            x[idx] = keep - h
+            lm = _loss(dO, window=w, scale=s, mix=0.8, **args)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        assert rel(g[gname], fd) < 1e-6, arg
+
+
+def test_separate_window_inputs_decode_reproduces_prefill():
+    # decode steps with separate window inputs continue a prefill exactly; the
+    # window cache holds the window keys
+    B, H, T, d, w, M, s = 2, 2, 20, 3, 6, 2, 0.9
+    q, k, v, qw, kw = (rand(B, H, T, d) for _ in range(5))
+    la, mk, mv = logsig(rand(B, H, T, d) + 1), rand(H, M, d), rand(H, M, d)
+    full = oracle.hybrid_forward(q, k, v, la, mk, mv, w, s, mix=0.7, q_w=qw, k_w=kw)
+    T0 = 13
+    pre = oracle.hybrid_forward(q[:, :, :T0], k[:, :, :T0], v[:, :, :T0], la[:, :, :T0], mk, mv,
+                                w, s, mix=0.7, q_w=qw[:, :, :T0], k_w=kw[:, :, :T0])
+    S, rk, rv, pos = pre["hT"], pre["ring_k"], pre["ring_v"], np.full(B, T0)
+    for t in range(T0, T):
+        o, S, rk, rv, pos = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], la[:, :, t], S,
+                                               rk, rv, pos, mk, mv, w, s, mix=0.7,
+                                               q_w=qw[:, :, t], k_w=kw[:, :, t])
+        assert rel(o, full["o"][:, :, t]) < 1e-12
+    assert rel(S, full["hT"]) < 1e-12 and rel(rk, full["ring_k"]) < 1e-13
+
+
 def test_state_gradient_matches_central_differences():
     # loss with a term through the final state: L = sum(dO * o) + sum(dhT * hT)
     B, H, T, d, w, M, s = 1, 1, 11, 4, 3, 2, 0.8
