@@ -181,7 +181,9 @@ def test_I7_meta_slots_are_sinks_when_meta_v_is_zero():
     # meta only enlarges the denominator: o = o_(M=0) * Z_window / (Z_window + Z_meta)
     assert rel(o, o0 * np.exp(lse0 - lse)[..., None]) < 1e-12
     meta_logits = s * np.einsum("bhtc,hmc->bhtm", q, mk)
-    assert np.max(np.abs(np.exp(lse) - np.exp(lse0) - np.exp(meta_logits).sum(-1))) < 1e-12
+    # relative: the partition functions reach ~1e2 with these logits
+    Z, Z0, Zm = np.exp(lse), np.exp(lse0), np.exp(meta_logits).sum(-1)
+    assert np.max(np.abs(Z - Z0 - Zm) / Z) < 1e-13
 
 
 def test_I10_linear_in_values():
