@@ -181,7 +181,8 @@ def main():
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     dref = ctypes.byref(desc)
     hyb_args = (dref, P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]), P(x["meta_k"]),
-                P(x["meta_v"]), None, P(o), None, None, P(hT), P(rk), P(rv), P(ws), nws, stream)
+                P(x["meta_v"]), None, P(o), None, None, P(hT), P(rk), P(rv), None, None, P(ws), nws,
+                stream)
 
     def step():
         st = lib.lizard_hybrid_fwd(*hyb_args)

@@ -109,15 +109,26 @@ def swa_fwd(q, k, v, meta_k, meta_v, window, scale=None, return_lse=False):
     return (o, lse) if return_lse else o
 
 
+def _window_pair(q_w, k_w, shape, dt):
+    if (q_w is None) != (k_w is None):
+        raise ValueError("q_w and k_w: give both or neither")
+    if q_w is not None:
+        _need(q_w, "q_w", shape, dt)
+        _need(k_w, "k_w", shape, dt)
+
+
 def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, h0=None,
-               save_for_backward=False, return_state=False, return_ring=False):
+               save_for_backward=False, return_state=False, return_ring=False, q_w=None,
+               k_w=None):
     """o = o_gla + mix * o_swa.  Returns a dict with "o" and, on request, "lse" and
-    "o_swa" (save_for_backward), "hT" (return_state), "ring_k"/"ring_v" (return_ring)."""
+    "o_swa" (save_for_backward), "hT" (return_state), "ring_k"/"ring_v" (return_ring).
+    q_w, k_w (optional, both or neither): the window branch's own queries and keys."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     _need(q, "q", (B, H, T, dk), dt)
     _need(k, "k", (B, H, T, dk), dt)
+    _window_pair(q_w, k_w, (B, H, T, dk), dt)
     _need(v, "v", (B, H, T, dv), dt)
     _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
@@ -138,21 +149,24 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
     _abi.check("lizard_hybrid_fwd", lib().lizard_hybrid_fwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
-        _p(out.get("ring_k")), _p(out.get("ring_v")), _p(ws), nws, _stream()))
+        _p(out.get("ring_k")), _p(out.get("ring_v")), _p(q_w), _p(k_w), _p(ws), nws, _stream()))
     return out
 
 
 def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale=None, mix=1.0,
-               h0=None, dhT=None, return_dh0=False, return_dmix=False):
+               h0=None, dhT=None, return_dh0=False, return_dmix=False, q_w=None, k_w=None):
     """Gradients of sum(dO * o) + sum(dhT * hT) (dhT: the gradient of the final
     state, optional).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v and,
     with return_dh0, dh0 (the gradient of the initial state), with return_dmix,
-    dmix (a one-element float32 tensor, the gradient of the mix weight)."""
+    dmix (a one-element float32 tensor, the gradient of the mix weight).  With the
+    window branch's own q_w, k_w, dq and dk are the gated branch's gradients and
+    the dict also holds dq_w, dk_w."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     _need(q, "q", (B, H, T, dk), dt)
     _need(k, "k", (B, H, T, dk), dt)
+    _window_pair(q_w, k_w, (B, H, T, dk), dt)
     _need(v, "v", (B, H, T, dv), dt)
     _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
@@ -170,27 +184,32 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
         g["dh0"] = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
     if return_dmix:
         g["dmix"] = torch.empty(1, device=dev, dtype=torch.float32)
+    if q_w is not None:
+        g["dq_w"] = torch.empty_like(q_w)
+        g["dk_w"] = torch.empty_like(k_w)
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
     nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
     ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
     _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]), _p(g["dlog_alpha"]),
-        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")), _p(g.get("dmix")), _p(ws), nws,
-        _stream()))
+        _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")), _p(g.get("dmix")),
+        _p(q_w), _p(k_w), _p(g.get("dq_w")), _p(g.get("dk_w")), _p(ws), nws, _stream()))
     return g
 
 
 def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, scale=None,
-                mix=1.0, out=None):
+                mix=1.0, out=None, q_w=None, k_w=None):
     """One generation step for B sequences.  Updates state, ring_k/ring_v and pos
-    (int64 [B], device) in place and returns o [B,H,dv]."""
+    (int64 [B], device) in place and returns o [B,H,dv].  q_w, k_w (optional, both
+    or neither): the window branch's own query and key."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     window = ring_k.shape[2]
     _need(q, "q", (B, H, dk), dt)
     _need(k, "k", (B, H, dk), dt)
+    _window_pair(q_w, k_w, (B, H, dk), dt)
     _need(v, "v", (B, H, dv), dt)
     _need(log_alpha, "log_alpha", (B, H, dk), torch.float32)
     _need(state, "state", (B, H, dk, dv), torch.float32)
@@ -202,7 +221,7 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, 
     d = make_desc(B, H, 0, dk, dv, window, M, scale, mix, dt)
     _abi.check("lizard_decode_step", lib().lizard_decode_step(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(state), _p(ring_k), _p(ring_v),
-        _p(pos), _p(meta_k), _p(meta_v), _p(o), _stream()))
+        _p(pos), _p(meta_k), _p(meta_v), _p(q_w), _p(k_w), _p(o), _stream()))
     return o
 
 

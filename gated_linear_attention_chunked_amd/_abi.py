@@ -36,9 +36,9 @@ _SIGS = {
     "lizard_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Desc), ctypes.c_int32]),
     "lizard_gla_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P, ctypes.c_size_t, P]),
     "lizard_swa_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P]),
-    "lizard_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P, ctypes.c_size_t, P]),
-    "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 19 + [P, ctypes.c_size_t, P]),
-    "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 11 + [P]),
+    "lizard_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 15 + [P, ctypes.c_size_t, P]),
+    "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 23 + [P, ctypes.c_size_t, P]),
+    "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P]),
     "lizard_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lizard_version": (ctypes.c_int32, []),
 }

@@ -5,7 +5,9 @@
 // size hidden state instead of a growing KV cache.  One step for token p of a
 // sequence: S <- diag(alpha) S + k^T v; o_gla = q S; the window cache keeps the
 // last w keys/values in slot (position mod w); the window softmax runs over the
-// min(p+1, w) filled slots plus the M meta slots; o = o_gla + mix * o_swa.
+// min(p+1, w) filled slots plus the M meta slots; o = o_gla + mix * o_swa.  The
+// window branch may read a query and key of its own (qw, kw; else q, k); the
+// window cache then holds kw.
 //
 // One work-group per (batch, head).  The fp32 state (64 KiB at d = 128) is
 // streamed once in and once out with 16-byte accesses; it dominates the bytes
@@ -18,7 +20,8 @@ namespace {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 8) void decode_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ qw,
+    const T* __restrict__ kw, const T* __restrict__ v,
     const float* __restrict__ la, float* __restrict__ state, T* __restrict__ ring_k,
     T* __restrict__ ring_v, int64_t* __restrict__ pos, const T* __restrict__ mk,
     const T* __restrict__ mv, T* __restrict__ o, int H, int W, int M, float scale_log2,
@@ -28,7 +31,7 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
   constexpr int LPR = 16;          // lanes per key row in the logit pass
   constexpr int EPL = D / LPR;     // elements per lane in the logit pass
   extern __shared__ float logit[];  // W + M floats
-  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[D], sa[D];
+  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[D], sa[D], swq[D], swk[D];
   __shared__ __attribute__((aligned(16))) f32x4 red[RG][CQ];
   __shared__ __attribute__((aligned(16))) float wred[8];
 
@@ -48,6 +51,8 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
     sk[tid] = to_f(k[off]);
     sv[tid] = to_f(v[off]);
     sa[tid] = exp2_fast(la[off] * kLog2e);
+    swq[tid] = to_f(qw[off]);
+    swk[tid] = to_f(kw[off]);
   }
   __syncthreads();
 
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
   // ---- new token into its ring slot
   if (tid < D) {
     const size_t roff = ((size_t)bh * W + slot) * D + tid;
-    ring_k[roff] = to_t<T>(sk[tid]);
+    ring_k[roff] = to_t<T>(swk[tid]);
     ring_v[roff] = to_t<T>(sv[tid]);
   }
 
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
     const int part = tid % LPR;
     float qv[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[e] = sq[part * EPL + e];
+    for (int e = 0; e < EPL; ++e) qv[e] = swq[part * EPL + e];
     // loads are unconditional (the slot row's value is replaced by the new key
     // from LDS afterwards) so that several passes' loads are in flight at once
 #pragma unroll 3
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
         for (int e = 0; e < EPL; ++e) kv[e] = to_f(kp[part * EPL + e]);
         if (row == slot)
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) kv[e] = sk[part * EPL + e];
+          for (int e = 0; e < EPL; ++e) kv[e] = swk[part * EPL + e];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot += qv[e] * kv[e];
       }
@@ -178,13 +183,14 @@ __global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ 
 }
 
 template <typename T, int D>
-hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, const void* v,
-                               const float* la, float* state, void* ring_k, void* ring_v,
-                               int64_t* pos, const void* mk, const void* mv, void* o,
-                               hipStream_t st) {
+hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, const void* qw,
+                               const void* kw, const void* v, const float* la, float* state,
+                               void* ring_k, void* ring_v, int64_t* pos, const void* mk,
+                               const void* mv, void* o, hipStream_t st) {
   const size_t lds = sizeof(float) * (size_t)(s.window + s.n_meta);
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3(s.B * s.H), dim3(256), lds, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, state, (T*)ring_k, (T*)ring_v, pos,
+                     (const T*)k, (const T*)qw, (const T*)kw, (const T*)v, la, state,
+                     (T*)ring_k, (T*)ring_v, pos,
                      (const T*)mk, (const T*)mv, (T*)o, s.H, s.window, s.n_meta,
                      s.scale * kLog2e, s.mix);
   return hipGetLastError();
@@ -201,16 +207,20 @@ hipError_t ring_fill_typed(const Shape& s, const void* k, const void* v, void* r
 
 }  // namespace
 
-hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
-                         const float* la, float* state, void* ring_k, void* ring_v,
-                         int64_t* pos, const void* mk, const void* mv, void* o, hipStream_t st) {
+hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* qw,
+                         const void* kw, const void* v, const float* la, float* state,
+                         void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
+                         void* o, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
   if (s.dtype == 1) {
     if (s.dk == 128)
-      return launch_decode_typed<bf16, 128>(s, q, k, v, la, state, ring_k, ring_v, pos, mk, mv, o, st);
-    return launch_decode_typed<bf16, 64>(s, q, k, v, la, state, ring_k, ring_v, pos, mk, mv, o, st);
+      return launch_decode_typed<bf16, 128>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos,
+                                            mk, mv, o, st);
+    return launch_decode_typed<bf16, 64>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos, mk,
+                                         mv, o, st);
   }
-  return launch_decode_typed<float, 64>(s, q, k, v, la, state, ring_k, ring_v, pos, mk, mv, o, st);
+  return launch_decode_typed<float, 64>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos, mk,
+                                        mv, o, st);
 }
 
 hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* ring_k,

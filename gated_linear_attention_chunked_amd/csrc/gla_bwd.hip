@@ -238,13 +238,14 @@ __device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, in
   return i > j ? sm.vij[pair_of(i, j)][c] : (i == j ? 1.f : 0.f);
 }
 
-// One work-group per (chunk, head): dq, dk, dv (added to what dq, dk, dv hold)
-// and dlog_alpha of the GLA branch, from the chunk's inputs and the states S_c,
+// One work-group per (chunk, head): dq, dk, dv (added to what dq, dk, dv hold;
+// with kAddQK false dq and dk are written, not added to) and dlog_alpha of the GLA branch, from the chunk's inputs and the states S_c,
 // dS_{c+1} written by the two scans (dS_{c+1} is transposed here, in LDS).  Wave w owns token block w in both roles (query for
 // dq, key for dk and dv), so the work of the two halves balances.  Lane
 // (r16, g) owns token t = 16w + r16 and channels 16ct + 4g + r (ct, r < 4):
 // the accumulator layout of every output tile, in which the gate cumsum and
 // the dlog_alpha scans are also kept.
+template <bool kAddQK>
 __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
@@ -426,7 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   {
     u32x2 dqw[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) dqw[ct] = ld64v(bgq, (rowe + 16 * ct + 4 * g) * 2);
+    for (int ct = 0; ct < 4; ++ct)
+      dqw[ct] = kAddQK ? ld64v(bgq, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
     bf16x8 dof[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) dof[p] = ld8<bf16>(&sm.dor[at(t, 32 * p + 8 * g)]);
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     u32x2 dkw[4], dvw[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      dkw[ct] = ld64v(bgk, (rowe + 16 * ct + 4 * g) * 2);
+      dkw[ct] = kAddQK ? ld64v(bgk, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
       dvw[ct] = ld64v(bgv, (rowe + 16 * ct + 4 * g) * 2);
     }
     bf16x8 vf[2], kf[2];
@@ -695,17 +697,19 @@ hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, co
   return hipGetLastError();
 }
 
-// Per-chunk gradients from the scans' states; adds into dq, dk, dv.
+// Per-chunk gradients from the scans' states; adds into dv, and into dq, dk
+// when add_qk (else writes them).
 hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
                                 const float* la, const void* dO, void* dq, void* dk, void* dv,
-                                float* dla, const void* ws, hipStream_t st) {
+                                float* dla, const void* ws, bool add_qk, hipStream_t st) {
   typedef bf16 T;
   const int nc = (s.T + kC - 1) / kC;
   const int BH = s.B * s.H;
   if (nc == 0 || BH == 0) return hipSuccess;
   const T* S_all = (const T*)ws;
   const T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  hipLaunchKernelGGL(gla_bwd_chunk, dim3(nc, BH), dim3(kThreads), 0, st, (const T*)q,
+  hipLaunchKernelGGL(add_qk ? gla_bwd_chunk<true> : gla_bwd_chunk<false>, dim3(nc, BH),
+                     dim3(kThreads), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, la, (const T*)dO, S_all, dS_all, (T*)dq,
                      (T*)dk, (T*)dv, dla, s.T);
   return hipGetLastError();

@@ -1,5 +1,7 @@
 // Hybrid backward orchestration: the window branch writes dq, dk, dv, then the
 // GLA branch adds its gradients to them (read-modify-write in its grad kernel).
+// With separate window queries and keys (qw, kw) the window branch writes dqw,
+// dkw, dv instead, and the GLA branch writes dq, dk and adds to dv.
 // The mix weight of "Lizard: An Efficient Linearization Framework for Large
 // Language Models" (gist.science summary, section 2(a), final weighted sum)
 // enters only o = o_gla + mix * o_swa, so dmix = sum(dO * o_swa).
@@ -15,7 +17,7 @@ hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, co
                                 const void* dO, void* ws, hipStream_t st);
 hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
                                 const float* la, const void* dO, void* dq, void* dk, void* dv,
-                                float* dla, const void* ws, hipStream_t st);
+                                float* dla, const void* ws, bool add_qk, hipStream_t st);
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv, float* dmk, float* dmv,
@@ -79,8 +81,8 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
                              const float* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
                              void* dk, void* dv, float* dla, float* dmk, float* dmv,
-                             const float* dhT, float* dh0, float* dmix, void* ws,
-                             hipStream_t st) {
+                             const float* dhT, float* dh0, float* dmix, const void* qw,
+                             const void* kw, void* dqw, void* dkw, void* ws, hipStream_t st) {
   if (s.T == 0 || s.B == 0) {
     // no tokens: the meta-memory gradients are zero, dh0 = dhT (or zero)
     const size_t n = (size_t)s.H * s.n_meta * s.dk;
@@ -101,7 +103,9 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
   // that produce its states) adds its gradients to them.
   hipError_t e = launch_gla_bwd_scans(s, q, k, v, la, h0, dhT, dh0, dO, w, st);
   if (e != hipSuccess) return e;
-  e = launch_swa_bwd(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv, wswa, st);
+  const bool sep = qw != nullptr;
+  e = launch_swa_bwd(s, sep ? qw : q, sep ? kw : k, v, mk, mv, o_swa, lse, dO, sep ? dqw : dq,
+                     sep ? dkw : dk, dv, dmk, dmv, wswa, st);
   if (e != hipSuccess) return e;
   if (dmix) {
     float* part = (float*)(wswa + align256(swa_bwd_workspace_bytes(s)));
@@ -112,7 +116,7 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_gla_bwd_grads(s, q, k, v, la, dO, dq, dk, dv, dla, w, st);
+  return launch_gla_bwd_grads(s, q, k, v, la, dO, dq, dk, dv, dla, w, !sep, st);
 }
 
 }  // namespace lz

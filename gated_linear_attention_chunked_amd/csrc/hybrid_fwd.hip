@@ -106,8 +106,12 @@ __device__ __forceinline__ void intra_scores(Smem& sm, int i, int j, bool fast, 
   st4<bf16>(&sm.a[at4(16 * i + r16, 16 * j + 4 * g)], acc);
 }
 
+// kSep: the window branch reads its own queries and keys qw, kw (otherwise qw,
+// kw alias q, k and are not loaded a second time).
+template <bool kSep>
 __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ qw,
+    const bf16* __restrict__ kw, const bf16* __restrict__ v,
     const float* __restrict__ la, const bf16* __restrict__ mk, const bf16* __restrict__ mv,
     const float* __restrict__ h0, const float* __restrict__ ws_state,
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT,
@@ -363,6 +367,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const u32 o2 = (u32)((2 * rq * kD + ch0) * 2), o4 = (u32)((2 * rq * kD + ch0) * 4);
     struct In {
       u32x4 q[2], k[2], la[2][2];
+      u32x4 wq[2], wk[2];  // window queries and keys (kSep only)
     };
     auto issue = [&](int ch, In& x) {
       const size_t e0 = off + (size_t)ch * kC * kD;
@@ -374,6 +379,14 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         x.k[rr] = bk.ld128(o2 + rr * kD * 2);
         x.la[rr][0] = bl.ld128(o4 + rr * kD * 4);
         x.la[rr][1] = bl.ld128(o4 + rr * kD * 4 + 16);
+      }
+      if constexpr (kSep) {
+        const Buf bwq(qw + e0, rem * 2), bwk(kw + e0, rem * 2);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          x.wq[rr] = bwq.ld128(o2 + rr * kD * 2);
+          x.wk[rr] = bwk.ld128(o2 + rr * kD * 2);
+        }
       }
     };
     auto gate = [&](int ch, const In& x) {
@@ -486,8 +499,8 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         const int row = 2 * rq + rr;
         *reinterpret_cast<u32x4*>(&sm.qs[at16(row, ch0)]) = u32x4{qw[rr][0], qw[rr][1], qw[rr][2], qw[rr][3]};
         *reinterpret_cast<u32x4*>(&sm.ks[at16(row, ch0)]) = u32x4{kw[rr][0], kw[rr][1], kw[rr][2], kw[rr][3]};
-        *reinterpret_cast<u32x4*>(&sm.qr[at16(row, ch0)]) = x.q[rr];
-        *reinterpret_cast<u32x4*>(&kring[at16(row, ch0)]) = x.k[rr];
+        *reinterpret_cast<u32x4*>(&sm.qr[at16(row, ch0)]) = kSep ? x.wq[rr] : x.q[rr];
+        *reinterpret_cast<u32x4*>(&kring[at16(row, ch0)]) = kSep ? x.wk[rr] : x.k[rr];
       }
     };
     // Window scores of query rows 16qb..16qb+15 of chunk c over one half of
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       for (int r = 0; r < kRing - 1; ++r) {
         const int cr = c_begin - 4 + r;
         if (cr >= 0) {
-          const Buf bk(k + off + (size_t)cr * kC * kD, (u32)(kC * kD * 2));
+          const Buf bk(kw + off + (size_t)cr * kC * kD, (u32)(kC * kD * 2));
           kp[r][0] = bk.ld128(o2);
           kp[r][1] = bk.ld128(o2 + kD * 2);
         }
@@ -633,7 +646,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   // last min(T, W) tokens, zero for slots without a token; the head's segments
   // share the slots
   if (rk) {
-    const Buf bk(k + off, (u32)((size_t)T_len * kD * 2)), bv(v + off, (u32)((size_t)T_len * kD * 2));
+    const Buf bk(kw + off, (u32)((size_t)T_len * kD * 2)), bv(v + off, (u32)((size_t)T_len * kD * 2));
     const size_t rbase = (size_t)bh * W * kD;
     const u32x4 z = {0u, 0u, 0u, 0u};
     const int s_lo = (int)((long long)W * seg / G), s_hi = (int)((long long)W * (seg + 1) / G);
@@ -659,10 +672,10 @@ bool hybrid_fused_ok(const Shape& s) {
          s.n_meta <= 16 && s.T > 0;
 }
 
-hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* v,
-                               const float* la, const void* mk, const void* mv, const float* h0,
-                               void* o, float* hT, void* ring_k, void* ring_v, void* ws,
-                               hipStream_t st) {
+hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
+                               const void* kw, const void* v, const float* la, const void* mk,
+                               const void* mv, const float* h0, void* o, float* hT, void* ring_k,
+                               void* ring_v, void* ws, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
   int G = 1, cps = 1;
   hipError_t e = launch_gla_state(s, k, v, la, ws, &G, &cps, st);
@@ -670,10 +683,13 @@ hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, con
   const int BH = s.B * s.H;
   const float* ws_state = (const float*)ws;
   const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * kD * kD : nullptr;
-  hipLaunchKernelGGL(hybrid_fwd_fused, dim3(G, BH), dim3(512), 0, st, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, la, (const bf16*)mk, (const bf16*)mv, h0,
-                     ws_state, ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, s.T, s.H,
-                     s.window, s.n_meta, s.scale * kLog2e, s.mix, cps, G);
+  const bool sep = qw != nullptr;
+  auto kern = sep ? hybrid_fwd_fused<true> : hybrid_fwd_fused<false>;
+  hipLaunchKernelGGL(kern, dim3(G, BH), dim3(512), 0, st, (const bf16*)q, (const bf16*)k,
+                     (const bf16*)(sep ? qw : q), (const bf16*)(sep ? kw : k), (const bf16*)v, la,
+                     (const bf16*)mk, (const bf16*)mv, h0, ws_state, ws_gamma, (bf16*)o, hT,
+                     (bf16*)ring_k, (bf16*)ring_v, s.T, s.H, s.window, s.n_meta,
+                     s.scale * kLog2e, s.mix, cps, G);
   return hipGetLastError();
 }
 

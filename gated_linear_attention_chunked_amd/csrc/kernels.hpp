@@ -32,10 +32,11 @@ hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const 
 // o_swa, hT (optional) and the decode window cache (optional).  Only for the
 // shapes hybrid_fused_ok accepts.
 bool hybrid_fused_ok(const Shape& s);
-hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* v,
-                               const float* la, const void* mk, const void* mv, const float* h0,
-                               void* o, float* hT, void* ring_k, void* ring_v, void* ws,
-                               hipStream_t st);
+// qw, kw: the window branch's queries and keys (both null: q, k).
+hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
+                               const void* kw, const void* v, const float* la, const void* mk,
+                               const void* mv, const float* h0, void* o, float* hT, void* ring_k,
+                               void* ring_v, void* ws, hipStream_t st);
 
 // Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
 // accumulate != 0); o_swa and lse are optional extra outputs.
@@ -53,18 +54,22 @@ hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* 
 // hT <- h0 (or zeros) for T == 0.
 hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStream_t st);
 
-hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* v,
-                         const float* la, float* state, void* ring_k, void* ring_v,
-                         int64_t* pos, const void* mk, const void* mv, void* o, hipStream_t st);
+// qw, kw: the window branch's query and key (pass q, k when they are shared).
+hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* qw,
+                         const void* kw, const void* v, const float* la, float* state,
+                         void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
+                         void* o, hipStream_t st);
 
 // Backward (bf16, dk = dv = 64 in this version).  Workspace layout is owned by
-// gla_bwd / swa_bwd; it grows with T (two states per chunk).
+// gla_bwd / swa_bwd; it grows with T (two states per chunk).  qw, kw, dqw, dkw:
+// separate window queries and keys and their gradients (all null: shared).
 bool bwd_supported(const Shape& s);
 size_t bwd_workspace_bytes(const Shape& s);
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
                              const float* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
                              void* dk, void* dv, float* dla, float* dmk, float* dmv,
-                             const float* dhT, float* dh0, float* dmix, void* ws, hipStream_t st);
+                             const float* dhT, float* dh0, float* dmix, const void* qw,
+                             const void* kw, void* dqw, void* dkw, void* ws, hipStream_t st);
 
 }  // namespace lz

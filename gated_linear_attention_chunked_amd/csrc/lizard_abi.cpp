@@ -107,11 +107,16 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,
-                                  void* o_swa, float* hT, void* ring_k, void* ring_v, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+                                  void* o_swa, float* hT, void* ring_k, void* ring_v,
+                                  const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
   if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  if ((q_w == nullptr) != (k_w == nullptr)) return LIZARD_E_NULL;
+  // the window branch's queries and keys (the same as the GLA branch's by default)
+  const void* qw = q_w ? q_w : q;
+  const void* kw = k_w ? k_w : k;
   if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
   const Shape s = to_shape(desc);
@@ -122,17 +127,17 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
   hipError_t e = hipSuccess;
   if (desc->T > 0 && !lse && !o_swa && lz::hybrid_fused_ok(s)) {
     // state pass, then both branches in one output pass (o written once)
-    e = lz::launch_hybrid_fused(s, q, k, v, log_alpha, meta_k, meta_v, h0, o, hT, ring_k, ring_v,
-                                ws, stream);
+    e = lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, log_alpha, meta_k, meta_v, h0, o, hT,
+                                ring_k, ring_v, ws, stream);
   } else if (desc->T > 0) {
     // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
     e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, ws, stream);
     if (e == hipSuccess)
-      e = lz::launch_swa_fwd(s, q, k, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, ring_k,
+      e = lz::launch_swa_fwd(s, qw, kw, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, ring_k,
                              ring_v, stream);
   } else {
     if (hT) e = lz::launch_state_copy(s, h0, hT, stream);
-    if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, k, v, ring_k, ring_v, stream);
+    if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, kw, v, ring_k, ring_v, stream);
   }
   return hip_status(e);
 }
@@ -142,10 +147,14 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
                                   float* dlog_alpha, float* dmeta_k, float* dmeta_v,
-                                  const float* dhT, float* dh0, float* dmix, void* ws,
+                                  const float* dhT, float* dh0, float* dmix, const void* q_w,
+                                  const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
+  // separate window queries and keys come with their gradient outputs: all four or none
+  const int n_sep = !!q_w + !!k_w + !!dq_w + !!dk_w;
+  if (n_sep != 0 && n_sep != 4) return LIZARD_E_NULL;
   const bool meta = desc->n_meta > 0 && desc->H > 0;
   if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o_swa || !lse || !dO || !dq || !dk ||
                            !dv || !dlog_alpha))
@@ -159,15 +168,17 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   return hip_status(lz::launch_hybrid_bwd(s, q, k, v, log_alpha, meta_k, meta_v, h0, o_swa, lse,
                                           dO, dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dhT, dh0,
-                                          dmix, ws, stream));
+                                          dmix, q_w, k_w, dq_w, dk_w, ws, stream));
 }
 
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
                                    const void* v, const float* log_alpha, float* state,
                                    void* ring_k, void* ring_v, int64_t* pos, const void* meta_k,
-                                   const void* meta_v, void* o, hipStream_t stream) {
+                                   const void* meta_v, const void* q_w, const void* k_w, void* o,
+                                   hipStream_t stream) {
   lizard_status_t st = check_desc(desc, false);
   if (st != LIZARD_OK) return st;
+  if (!q_w != !k_w) return LIZARD_E_NULL;  // window query and key: both or neither
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   if (!q || !k || !v || !log_alpha || !state || !ring_k || !ring_v || !pos || !o)
     return LIZARD_E_NULL;
@@ -176,8 +187,9 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
   if ((long long)desc->window + desc->n_meta > 16384) return LIZARD_E_UNSUPPORTED;
   // the heads of a sequence count their completion in bits 40.. of pos[b]
   if (desc->H >= (1 << 22)) return LIZARD_E_UNSUPPORTED;
-  return hip_status(lz::launch_decode(to_shape(desc), q, k, v, log_alpha, state, ring_k, ring_v,
-                                      pos, meta_k, meta_v, o, stream));
+  return hip_status(lz::launch_decode(to_shape(desc), q, k, q_w ? q_w : q, k_w ? k_w : k, v,
+                                      log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, o,
+                                      stream));
 }
 
 }  // extern "C"

@@ -116,12 +116,18 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
  * lse and o_swa (needed by lizard_hybrid_bwd), hT = final GLA state, and the
  * window cache ring_k/ring_v for a prefill -> decode handoff (slot p mod w holds
  * token p for the last min(T, w) tokens; slots no token reached are zeroed).
+ * q_w, k_w [B,H,T,dk] (desc->dtype; both NULL, or both given, else
+ * LIZARD_E_NULL): the window branch's own queries and keys, for models whose
+ * gated branch reads feature-mapped q, k ("Lizard: An Efficient Linearization
+ * Framework for Large Language Models", gist.science summary, section 2(a));
+ * NULL means the window branch reads q, k.  The window cache holds k_w.
  * ws must hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) bytes. */
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,
                                   void* o_swa, float* hT, void* ring_k, void* ring_v,
-                                  void* ws, size_t ws_bytes, hipStream_t stream);
+                                  const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Hybrid backward for the loss sum(dO * o) + sum(dhT * hT).  Reads the forward
  * inputs plus the o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv
@@ -138,14 +144,19 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
  * Language Models" (gist.science summary, sections 2(a) and 4).  ws must hold
  * lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_BWD) bytes: two bf16 dk x dv
  * matrices per 64-token chunk and head (S_c and dS_{c+1}) plus small per-token
- * and per-tile buffers, so it grows linearly with T.
+ * and per-tile buffers, so it grows linearly with T.  q_w, k_w, dq_w, dk_w
+ * (all four NULL, or all four given, else LIZARD_E_NULL): the window branch's
+ * own queries and keys as passed to lizard_hybrid_fwd, and their gradients
+ * [B,H,T,dk] (desc->dtype, overwritten); dq, dk then hold the gated branch's
+ * gradients alone.  With them NULL, dq and dk hold both branches' gradients.
  * This version supports BF16 with dk = dv = 64 (LIZARD_E_UNSUPPORTED otherwise). */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const float* log_alpha, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk,
                                   void* dv, float* dlog_alpha, float* dmeta_k, float* dmeta_v,
-                                  const float* dhT, float* dh0, float* dmix, void* ws,
+                                  const float* dhT, float* dh0, float* dmix, const void* q_w,
+                                  const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
 /* One constant-memory generation step for B sequences (desc->T is ignored).
@@ -156,12 +167,14 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
  * increments every pos[b] by one.  |pos[b]| must stay below 2^39; while the
  * call runs, pos[b] holds intermediate values (the heads of a sequence count
  * their completion in its high bits), so it must not be read or written by
- * other work until the call has finished. */
+ * other work until the call has finished.  q_w, k_w [B,H,dk] (both NULL, or
+ * both given, else LIZARD_E_NULL): the window branch's own query and key, as
+ * in lizard_hybrid_fwd; k_w (else k) goes into the ring, q_w (else q) attends. */
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
                                    const void* v, const float* log_alpha, float* state,
                                    void* ring_k, void* ring_v, int64_t* pos,
-                                   const void* meta_k, const void* meta_v, void* o,
-                                   hipStream_t stream);
+                                   const void* meta_k, const void* meta_v, const void* q_w,
+                                   const void* k_w, void* o, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* lizard_status_str(lizard_status_t status);

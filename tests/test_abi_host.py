@@ -80,9 +80,23 @@ def test_null_pointers():
     assert lib.lizard_swa_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, None, None) == 1
     # one ring pointer without the other
     assert lib.lizard_hybrid_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
-                                 None, None, None, FAKE, None, None, 0, None) == 1
+                                 None, None, None, FAKE, None, None, None, None, 0, None) == 1
     assert lib.lizard_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
-                                  FAKE, FAKE, FAKE, None) == 1
+                                  FAKE, FAKE, None, None, FAKE, None) == 1
+
+
+def test_window_inputs_come_in_pairs():
+    # the window branch's own queries and keys: both or neither (and, in the
+    # backward, with both their gradient outputs)
+    lib = _abi.lib()
+    d = desc()
+    for qw, kw in ((FAKE, None), (None, FAKE)):
+        assert lib.lizard_hybrid_fwd(ctypes.byref(d), *([FAKE] * 13), qw, kw, FAKE, 1 << 30,
+                                     None) == 1
+        assert lib.lizard_decode_step(ctypes.byref(d), *([FAKE] * 10), qw, kw, FAKE, None) == 1
+    for four in ((FAKE, FAKE, FAKE, None), (FAKE, None, None, None), (None, None, FAKE, FAKE)):
+        assert lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 19), *four, FAKE, 1 << 30,
+                                     None) == 1
 
 
 def test_empty_problems_enqueue_nothing():
@@ -115,7 +129,7 @@ def test_forward_rejects_small_workspace():
     need = lib.lizard_workspace_bytes(ctypes.byref(d), 0)
     assert need > 0
     assert gla(d) == 5  # no workspace passed
-    st = lib.lizard_hybrid_fwd(ctypes.byref(d), *([FAKE] * 13), FAKE, need - 1, None)
+    st = lib.lizard_hybrid_fwd(ctypes.byref(d), *([FAKE] * 15), FAKE, need - 1, None)
     assert st == 5
 
 
@@ -124,10 +138,10 @@ def test_backward_workspace_and_support():
     d = desc(T=256)
     need = lib.lizard_workspace_bytes(ctypes.byref(d), 3)
     assert need > 0
-    st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 19), FAKE, need - 1, None)
+    st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 23), FAKE, need - 1, None)
     assert st == 5
     # this version's backward covers bf16 with d = 64
     for kw in (dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32)):
         d2 = desc(**kw)
         assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
-        assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 19), FAKE, 1 << 30, None) == 4
+        assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 23), FAKE, 1 << 30, None) == 4

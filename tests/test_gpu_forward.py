@@ -172,7 +172,7 @@ def test_outputs_fully_written_and_deterministic():
         st = lz.lib().lizard_hybrid_fwd(
             ctypes.byref(dsc), p(inp["q"]), p(inp["k"]), p(inp["v"]), p(inp["log_alpha"]),
             p(inp["meta_k"]), p(inp["meta_v"]), None, p(o), p(lse), p(osw), p(hT), p(rk), p(rv),
-            p(ws), nws, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            None, None, p(ws), nws, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         assert st == 0
         torch.cuda.synchronize()
         for t in (o, lse, osw, hT, rk, rv):

@@ -61,10 +61,11 @@ def _torch_dtype(name):
 
 
 def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
-                with_grad_out=False, with_h0=False, **_ignored):
+                with_grad_out=False, with_h0=False, with_window_qk=False, **_ignored):
     """Draw one prefill/training batch on the CPU.  Returns a dict of tensors:
     q, k [B,H,T,dk]; v [B,H,T,dv]; log_alpha [B,H,T,dk] fp32; meta_k [H,M,dk];
-    meta_v [H,M,dv]; optionally dO [B,H,T,dv] and h0 [B,H,dk,dv] fp32."""
+    meta_v [H,M,dv]; optionally dO [B,H,T,dv], h0 [B,H,dk,dv] fp32 and the window
+    branch's own q_w, k_w [B,H,T,dk] (drawn last, like q and k)."""
     g = torch.Generator().manual_seed(seed)
     dt = _torch_dtype(dtype)
     q = torch.randn(B, H, T, dk, generator=g) / math.sqrt(dk)
@@ -80,20 +81,29 @@ def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
         out["dO"] = torch.randn(B, H, T, dv, generator=g).to(dt)
     if with_h0:
         out["h0"] = torch.randn(B, H, dk, dv, generator=g) * 0.1
+    if with_window_qk:
+        out["q_w"] = (torch.randn(B, H, T, dk, generator=g) / math.sqrt(dk)).to(dt)
+        out["k_w"] = (torch.randn(B, H, T, dk, generator=g) / math.sqrt(dk)).to(dt)
     return out
 
 
-def make_decode_inputs(steps, B, H, dk, dv, dtype="bf16", seed=1, gate_mean=2.0, **_ignored):
+def make_decode_inputs(steps, B, H, dk, dv, dtype="bf16", seed=1, gate_mean=2.0,
+                       with_window_qk=False, **_ignored):
     """Per-step decode tokens: q, k [steps,B,H,dk]; v [steps,B,H,dv];
-    log_alpha [steps,B,H,dk] fp32, drawn in the order q, k, v, x."""
+    log_alpha [steps,B,H,dk] fp32, drawn in the order q, k, v, x (then q_w, k_w
+    [steps,B,H,dk] with with_window_qk)."""
     g = torch.Generator().manual_seed(seed)
     dt = _torch_dtype(dtype)
     q = torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)
     k = torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)
     v = torch.randn(steps, B, H, dv, generator=g) / math.sqrt(dv)
     x = torch.randn(steps, B, H, dk, generator=g) + gate_mean
-    return dict(q=q.to(dt), k=k.to(dt), v=v.to(dt),
-                log_alpha=torch.nn.functional.logsigmoid(x).float())
+    out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt),
+               log_alpha=torch.nn.functional.logsigmoid(x).float())
+    if with_window_qk:
+        out["q_w"] = (torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)).to(dt)
+        out["k_w"] = (torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)).to(dt)
+    return out
 
 
 def to_f64_numpy(t):
