@@ -40,6 +40,8 @@ All arrays are numpy, laid out [B, H, T, D]; computations run in float64.
 import numpy as np
 
 __all__ = [
+    "log_sigmoid",
+    "log_sigmoid_backward",
     "gla_forward",
     "window_meta_attention",
     "hybrid_forward",
@@ -53,6 +55,24 @@ __all__ = [
 
 def _f64(x):
     return None if x is None else np.array(x, dtype=np.float64, copy=True)
+
+
+# ---------------------------------------------------------------------------
+# Gate
+# ---------------------------------------------------------------------------
+def log_sigmoid(x):
+    """log alpha of the sigmoid gate alpha = sigma(x) [LZ-2a, learnable gate
+    Gamma = sigma(W_gamma x)], from the gate logits x:
+    log sigma(x) = -log(1 + exp(-x)), written as min(x, 0) - log1p(exp(-|x|))
+    so that no positive number is exponentiated."""
+    x = _f64(x)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def log_sigmoid_backward(x, d_log_alpha):
+    """Chain rule through log_sigmoid: d/dx log sigma(x) = sigma(-x), so the
+    gradient with respect to the logits is d_log_alpha * sigma(-x)."""
+    return _f64(d_log_alpha) * np.exp(log_sigmoid(-_f64(x)))
 
 
 # ---------------------------------------------------------------------------

@@ -52,6 +52,11 @@ MUTANTS = {
                                 "dv_[:, :, t, :] = np.matmul(k[:, :, t, None, :], np.swapaxes(G, -1, -2))[:, :, 0, :]"),
     "bwd_softmax_centering_dropped": ("dl = p * (dp - D)", "dl = p * dp"),
     "bwd_meta_key_grad_unscaled": ("dmk += scale * (dl", "dmk += (dl"),
+    "log_sigmoid_sign_of_x": ("return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))",
+                              "return np.minimum(-x, 0.0) - np.log1p(np.exp(-np.abs(x)))"),
+    "log_sigmoid_tail_dropped": ("return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))",
+                                 "return np.minimum(x, 0.0)"),
+    "log_sigmoid_grad_wrong_side": ("np.exp(log_sigmoid(-_f64(x)))", "np.exp(log_sigmoid(_f64(x)))"),
 }
 
 PIN_TESTS = [(name, fn) for name, fn in inspect.getmembers(pins, inspect.isfunction)

@@ -378,6 +378,70 @@ def test_state_gradient_chains_over_segments():
     assert rel(g1["dh0"], full["dh0"]) < 1e-12
 
 
+# ------------------------------------------------------------ logit gates
+def test_log_sigmoid_special_values_and_symmetry():
+    # sigma(0) = 1/2; sigma(x) + sigma(-x) = 1, so log sigma(x) - log sigma(-x) = x
+    assert oracle.log_sigmoid(np.array(0.0)) == -np.log(2.0)
+    x = np.concatenate([rand(200) * 6, [-700.0, -40.0, -1e-9, 1e-9, 40.0, 700.0]])
+    ls, lm = oracle.log_sigmoid(x), oracle.log_sigmoid(-x)
+    assert np.max(np.abs(ls - lm - x) / np.maximum(1.0, np.abs(x))) < 1e-15
+    assert np.max(np.abs(np.exp(ls) + np.exp(lm) - 1.0)) < 1e-15
+    assert np.all(ls <= 0.0)
+    # asymptotes: log sigma(x) -> x for x -> -inf, -e^{-x} for x -> +inf
+    assert oracle.log_sigmoid(np.array(-40.0)) == -40.0 - np.exp(-40.0)
+    assert abs(oracle.log_sigmoid(np.array(40.0)) + np.exp(-40.0)) < 1e-30
+    # the textbook form where it is accurate (|x| moderate)
+    xm = rand(100) * 4
+    assert rel(np.exp(oracle.log_sigmoid(xm)), 1.0 / (1.0 + np.exp(-xm))) < 1e-15
+
+
+def test_log_sigmoid_gradient_matches_central_differences():
+    x = np.concatenate([rand(50) * 5, [-30.0, 30.0]])
+    g = rand(x.size)
+    got = oracle.log_sigmoid_backward(x, g)
+    h = 1e-6
+    fd = g * (oracle.log_sigmoid(x + h) - oracle.log_sigmoid(x - h)) / (2 * h)
+    assert np.max(np.abs(got - fd)) < 1e-8
+    # sigma(-x) at the extremes, computed without cancellation
+    assert oracle.log_sigmoid_backward(np.array(40.0), np.array(1.0)) == pytest.approx(
+        np.exp(-40.0), rel=1e-14)
+    assert oracle.log_sigmoid_backward(np.array(-40.0), np.array(1.0)) == pytest.approx(1.0, rel=1e-15)
+
+
+def test_logit_gates_drive_the_recurrence_as_sigmoid_decays():
+    # the state recurrence with alpha_t = 1 / (1 + e^{-x_t}) applied directly,
+    # token by token, against the oracle fed log_sigmoid(x)
+    B, H, T, d = 1, 2, 23, 4
+    q, k, v, x = rand(B, H, T, d), rand(B, H, T, d), rand(B, H, T, d), rand(B, H, T, d) * 3 + 1
+    S = np.zeros((B, H, d, d))
+    o = np.zeros((B, H, T, d))
+    for t in range(T):
+        alpha = 1.0 / (1.0 + np.exp(-x[:, :, t]))
+        S = alpha[..., None] * S + k[:, :, t, :, None] * v[:, :, t, None, :]
+        o[:, :, t] = np.einsum("bhc,bhcn->bhn", q[:, :, t], S)
+    got, hT = oracle.gla_forward(q, k, v, oracle.log_sigmoid(x))
+    assert rel(got, o) < 1e-13 and rel(hT, S) < 1e-13
+
+
+def test_logit_gate_gradient_through_the_layer():
+    # d loss / d x by central differences in x, against the chain rule through
+    # the backward's d log_alpha
+    B, H, T, d, w, M, s = 1, 1, 11, 3, 4, 2, 0.7
+    q, k, v, dO = rand(B, H, T, d), rand(B, H, T, d), rand(B, H, T, d), rand(B, H, T, d)
+    x = rand(B, H, T, d) * 2 + 1
+    mk, mv = rand(H, M, d), rand(H, M, d)
+    loss = lambda xx: float((oracle.hybrid_forward(q, k, v, oracle.log_sigmoid(xx), mk, mv, w, s)["o"] * dO).sum())
+    g = oracle.hybrid_backward(q, k, v, oracle.log_sigmoid(x), mk, mv, w, s, dO)
+    dx = oracle.log_sigmoid_backward(x, g["dlog_alpha"])
+    h = 1e-6
+    for idx in [(0, 0, 0, 0), (0, 0, 5, 1), (0, 0, 10, 2), (0, 0, 3, 0)]:
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd = (loss(xp) - loss(xm)) / (2 * h)
+        assert abs(dx[idx] - fd) < 1e-7 * max(1.0, abs(fd))
+
+
 def test_I9_dlog_alpha_identity_over_chunks():
     # GLA part only: dlog_alpha = reverse cumsum over the sequence of q*dq - k*dk
     B, H, T, d = 2, 2, 150, 6
