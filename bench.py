@@ -37,11 +37,13 @@ def algorithmic_flops(B, H, T, d, C, w, M):
     return 2.0 * B * H * (gla + win * 2 * d)
 
 
-def hybrid_bytes(B, H, T, d, w, M):
-    """Hybrid forward: q, k, v (bf16) and log_alpha (fp32) read once, o written
-    once, the final state (fp32) and the window cache (bf16 K and V) written
-    once, the meta keys and values read once."""
-    return B * H * (T * (3 * d * 2 + d * 4 + d * 2) + d * d * 4 + 2 * w * d * 2) + H * M * d * 2 * 2
+def hybrid_bytes(B, H, T, d, w, M, gate_bytes=4):
+    """Hybrid forward: q, k, v (bf16) and the gates (fp32 log_alpha, or bf16
+    logits with gate_bytes=2) read once, o written once, the final state (fp32)
+    and the window cache (bf16 K and V) written once, the meta keys and values
+    read once."""
+    return (B * H * (T * (3 * d * 2 + d * gate_bytes + d * 2) + d * d * 4 + 2 * w * d * 2)
+            + H * M * d * 2 * 2)
 
 
 def decode_bytes_per_step(B, H, d, w, M, pos):
@@ -241,6 +243,7 @@ def main():
     }
 
     if not args.no_extras:
+        out["prefill_gate_logits"] = bench_prefill_gate_logits(lz, torch, dev, args)
         out["long_prefill"] = bench_long_prefill(lz, torch, dev, args, ms / (B * T))
         out["decode"] = bench_decode(lz, torch, dev)
         try:
@@ -250,6 +253,43 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def bench_prefill_gate_logits(lz, torch, dev, args):
+    """The headline prefill workload with the gates given as bf16 logits x
+    (alpha = sigmoid(x), the same N(2, 1) draw), log-sigmoid taken in the
+    kernels: half the gate bytes of fp32 log_alpha."""
+    from gated_linear_attention_chunked_amd import _abi
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["prefill_bf16_b2_h32_t4096_d128"]
+    B, H, T, d, w, M = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta
+    x = {n: t.to(dev) for n, t in make_inputs(B, H, T, d, d, M, dtype=wl.dtype, seed=0,
+                                              with_gate_logits=True).items()}
+    o = torch.empty_like(x["v"])
+    hT = torch.empty(B, H, d, d, device=dev)
+    rk = torch.empty(B, H, w, d, device=dev, dtype=torch.bfloat16)
+    rv = torch.empty_like(rk)
+    desc = lz.make_desc(B, H, T, d, d, w, M, wl.scale, wl.mix, torch.bfloat16,
+                        gate=_abi.LIZARD_GATE_LOGIT)
+    nws = lz.workspace_bytes(desc, _abi.OP_HYBRID_FWD)
+    ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (ctypes.byref(desc), P(x["q"]), P(x["k"]), P(x["v"]), P(x["gate_x"]), P(x["meta_k"]),
+         P(x["meta_v"]), None, P(o), None, None, P(hT), P(rk), P(rv), None, None, P(ws), nws, stream)
+    lib = lz.lib()
+
+    def step():
+        st = lib.lizard_hybrid_fwd(*a)
+        if st != 0:
+            raise RuntimeError(f"lizard_hybrid_fwd (logit gates): status {st}")
+
+    ms = event_time_ms(step, args.steps, args.warmup)
+    nbytes = hybrid_bytes(B, H, T, d, w, M, gate_bytes=2)
+    return {"workload": "prefill_bf16_b2_h32_t4096_d128, bf16 gate logits", "ms_per_step": ms,
+            "tokens_per_s": B * T / (ms / 1e3), "algorithmic_bytes": nbytes,
+            "achieved_GBs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_long_prefill(lz, torch, dev, args, ms_per_token_headline):

@@ -7,7 +7,9 @@ include/lizard.h (same names without the `lizard_` prefix).  torch only
 allocates device memory and supplies the current HIP stream; every step of the
 computation runs in liblizard.so.  Shapes follow the ABI: q, k [B,H,T,dk];
 v [B,H,T,dv]; log_alpha [B,H,T,dk] float32; meta_k [H,M,dk]; meta_v [H,M,dv];
-states [B,H,dk,dv] float32.
+states [B,H,dk,dv] float32.  Wherever log_alpha is taken it may instead be a
+bfloat16 tensor of gate logits x (alpha = sigmoid(x), bf16 problems only); the
+gradient returned as dlog_alpha is then the float32 gradient with respect to x.
 """
 import ctypes
 import math
@@ -24,11 +26,21 @@ _DTYPES = {torch.float32: _abi.LIZARD_F32, torch.bfloat16: _abi.LIZARD_BF16}
 
 
 def make_desc(B, H, T, dk, dv, window=1, n_meta=0, scale=None, mix=1.0, dtype=torch.bfloat16,
-              chunk=64):
+              chunk=64, gate=_abi.LIZARD_GATE_LOG_ALPHA):
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
     return _abi.Desc(B, H, T, dk, dv, chunk, window, n_meta,
-                     0.0 if scale is None else float(scale), float(mix), _DTYPES[dtype])
+                     0.0 if scale is None else float(scale), float(mix), _DTYPES[dtype], gate)
+
+
+def _gate(log_alpha, name, shape):
+    """The gate input is float32 log alpha, or bfloat16 logits x with
+    alpha = sigmoid(x).  Returns the desc gate code."""
+    if log_alpha is not None and log_alpha.dtype == torch.bfloat16:
+        _need(log_alpha, name, shape, torch.bfloat16)
+        return _abi.LIZARD_GATE_LOGIT
+    _need(log_alpha, name, shape, torch.float32)
+    return _abi.LIZARD_GATE_LOG_ALPHA
 
 
 def _p(t):
@@ -79,11 +91,11 @@ def gla_fwd(q, k, v, log_alpha, h0=None, return_state=False):
     _need(q, "q", (B, H, T, dk), dt)
     _need(k, "k", (B, H, T, dk), dt)
     _need(v, "v", (B, H, T, dv), dt)
-    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    gate = _gate(log_alpha, "log_alpha", (B, H, T, dk))
     _opt(h0, "h0", (B, H, dk, dv), torch.float32)
     o = torch.empty_like(v)
     hT = torch.empty(B, H, dk, dv, device=q.device, dtype=torch.float32) if return_state else None
-    d = make_desc(B, H, T, dk, dv, dtype=dt)
+    d = make_desc(B, H, T, dk, dv, dtype=dt, gate=gate)
     nws = workspace_bytes(d, _abi.OP_GLA_FWD)
     ws = torch.empty(nws, device=q.device, dtype=torch.uint8) if nws else None
     _abi.check("lizard_gla_fwd", lib().lizard_gla_fwd(
@@ -130,7 +142,7 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
     _need(k, "k", (B, H, T, dk), dt)
     _window_pair(q_w, k_w, (B, H, T, dk), dt)
     _need(v, "v", (B, H, T, dv), dt)
-    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    gate = _gate(log_alpha, "log_alpha", (B, H, T, dk))
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
     _opt(h0, "h0", (B, H, dk, dv), torch.float32)
     dev = q.device
@@ -143,7 +155,7 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
     if return_ring:
         out["ring_k"] = torch.empty(B, H, window, dk, device=dev, dtype=dt)
         out["ring_v"] = torch.empty(B, H, window, dv, device=dev, dtype=dt)
-    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
+    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt, gate=gate)
     nws = workspace_bytes(d, _abi.OP_HYBRID_FWD)
     ws = torch.empty(nws, device=dev, dtype=torch.uint8) if nws else None
     _abi.check("lizard_hybrid_fwd", lib().lizard_hybrid_fwd(
@@ -168,7 +180,7 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
     _need(k, "k", (B, H, T, dk), dt)
     _window_pair(q_w, k_w, (B, H, T, dk), dt)
     _need(v, "v", (B, H, T, dv), dt)
-    _need(log_alpha, "log_alpha", (B, H, T, dk), torch.float32)
+    gate = _gate(log_alpha, "log_alpha", (B, H, T, dk))
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
     _opt(h0, "h0", (B, H, dk, dv), torch.float32)
     _opt(dhT, "dhT", (B, H, dk, dv), torch.float32)
@@ -177,7 +189,7 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
     _need(dO, "dO", (B, H, T, dv), dt)
     dev = q.device
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
-         "dlog_alpha": torch.empty_like(log_alpha),
+         "dlog_alpha": torch.empty(log_alpha.shape, device=dev, dtype=torch.float32),
          "dmeta_k": torch.empty(H, M, dk, device=dev, dtype=torch.float32),
          "dmeta_v": torch.empty(H, M, dv, device=dev, dtype=torch.float32)}
     if return_dh0:
@@ -187,7 +199,7 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
     if q_w is not None:
         g["dq_w"] = torch.empty_like(q_w)
         g["dk_w"] = torch.empty_like(k_w)
-    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt)
+    d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt, gate=gate)
     nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
     ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
     _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
@@ -211,14 +223,14 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, 
     _need(k, "k", (B, H, dk), dt)
     _window_pair(q_w, k_w, (B, H, dk), dt)
     _need(v, "v", (B, H, dv), dt)
-    _need(log_alpha, "log_alpha", (B, H, dk), torch.float32)
+    gate = _gate(log_alpha, "log_alpha", (B, H, dk))
     _need(state, "state", (B, H, dk, dv), torch.float32)
     _need(ring_k, "ring_k", (B, H, window, dk), dt)
     _need(ring_v, "ring_v", (B, H, window, dv), dt)
     _need(pos, "pos", (B,), torch.int64)
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
     o = torch.empty(B, H, dv, device=q.device, dtype=dt) if out is None else out
-    d = make_desc(B, H, 0, dk, dv, window, M, scale, mix, dt)
+    d = make_desc(B, H, 0, dk, dv, window, M, scale, mix, dt, gate=gate)
     _abi.check("lizard_decode_step", lib().lizard_decode_step(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(state), _p(ring_k), _p(ring_v),
         _p(pos), _p(meta_k), _p(meta_v), _p(q_w), _p(k_w), _p(o), _stream()))

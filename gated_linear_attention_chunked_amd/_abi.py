@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "liblizard.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "lizard.h")
 
 LIZARD_F32, LIZARD_BF16 = 0, 1
+LIZARD_GATE_LOG_ALPHA, LIZARD_GATE_LOGIT = 0, 1
 OP_GLA_FWD, OP_SWA_FWD, OP_HYBRID_FWD, OP_HYBRID_BWD, OP_DECODE = range(5)
 STATUS = {0: "LIZARD_OK", 1: "LIZARD_E_NULL", 2: "LIZARD_E_SHAPE", 3: "LIZARD_E_DTYPE",
           4: "LIZARD_E_UNSUPPORTED", 5: "LIZARD_E_WORKSPACE", 6: "LIZARD_E_HIP"}
@@ -22,7 +23,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("n_meta", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("mix", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("mix", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32)]
 
 
 class LizardError(RuntimeError):

@@ -15,6 +15,7 @@
 // 16 + 4g + (i-4) otherwise, which is exactly what an accumulator tile pair
 // holds and so lets a product's result feed the next product without moving.
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -172,6 +173,61 @@ __device__ __forceinline__ typename Pair<T>::type ld_pair(const Buf& b, u32 off)
 template <> __device__ __forceinline__ u32 ld_pair<bf16>(const Buf& b, u32 off) { return b.ld32(off); }
 template <> __device__ __forceinline__ U2 ld_pair<float>(const Buf& b, u32 off) { return b.ld64(off); }
 
+// Gate inputs.  A gate is given either as log alpha (float) or as a bf16 logit
+// x of the sigmoid gate alpha = sigmoid(x) of "Lizard: An Efficient
+// Linearization Framework for Large Language Models" (gist.science summary,
+// section 2(a), the learnable gate).  The kernels work with log2 alpha:
+//   log alpha:  log2 alpha = log_alpha * log2(e)
+//   logit:      log2 sigmoid(x) = min(x, 0) log2(e) - log2(1 + 2^{-|x| log2(e)})
+// (the second form never exponentiates a positive number).
+__device__ __forceinline__ float gate_log2(float la, float) { return la * kLog2e; }
+__device__ __forceinline__ float gate_log2(float x, bf16) {
+  const float t = x * kLog2e;
+  return fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t)));
+}
+// d log(alpha) / dx = sigmoid(-x) = 1 / (1 + 2^{x log2(e)}) for a logit x; 1 for
+// log alpha itself.
+__device__ __forceinline__ float gate_dlog(float, float) { return 1.f; }
+__device__ __forceinline__ float gate_dlog(float x, bf16) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_fast(x * kLog2e));
+}
+
+// Log2 gate of a token row: rows at or past the sequence end (loaded as zero
+// bytes) must not decay.  A float log gate of 0 already means alpha = 1; a
+// logit of 0 would mean alpha = 1/2, so logit rows there are masked to 0.
+template <typename GT>
+__device__ __forceinline__ float gate_row(float log2_gate, bool valid) {
+  if constexpr (sizeof(GT) == 2)
+    return valid ? log2_gate : 0.f;
+  else
+    return log2_gate;
+}
+
+// Eight consecutive gate inputs of one token: two 16-byte words of float log
+// alpha, or one 16-byte word of bf16 logits.
+template <typename G>
+struct Gate8 {
+  static constexpr int kWords = sizeof(G) / 2;
+  u32x4 w[kWords];
+  // elem: element offset from the buffer base
+  __device__ __forceinline__ void load(const Buf& b, u32 elem) {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = b.ld128(elem * (u32)sizeof(G) + 16u * i);
+  }
+  __device__ __forceinline__ float log2_at(int c) const {
+    if constexpr (sizeof(G) == 4)
+      return gate_log2(f_at(w[c >> 2], c & 3), G());
+    else
+      return gate_log2(bf_at(w[0], c), G());
+  }
+  __device__ __forceinline__ float raw_at(int c) const {
+    if constexpr (sizeof(G) == 4)
+      return f_at(w[c >> 2], c & 3);
+    else
+      return bf_at(w[0], c);
+  }
+};
+
 // Two fp32 values as a packed pair of T (one LDS store).
 template <typename T> __device__ __forceinline__ void st_pair(T* p, float a, float b);
 template <> __device__ __forceinline__ void st_pair<bf16>(bf16* p, float a, float b) {
@@ -255,6 +311,25 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 ld64v(const Buf& b, u32 off) {
   return __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
 }
+
+// Four consecutive gate inputs of one token (float log alpha or bf16 logits).
+template <typename G>
+struct Gate4 {
+  typename std::conditional<sizeof(G) == 4, u32x4, u32x2>::type w;
+  __device__ __forceinline__ void load(const Buf& b, u32 elem) {
+    if constexpr (sizeof(G) == 4)
+      w = b.ld128(elem * 4);
+    else
+      w = ld64v(b, elem * 2);
+  }
+  __device__ __forceinline__ float raw_at(int r) const {
+    if constexpr (sizeof(G) == 4)
+      return as_f(w[r]);
+    else
+      return (r & 1) ? bf_hi(w[r >> 1]) : bf_lo(w[r >> 1]);
+  }
+  __device__ __forceinline__ float log2_at(int r) const { return gate_log2(raw_at(r), G()); }
+};
 
 __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -18,11 +18,11 @@
 namespace lz {
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, typename G>
 __global__ __launch_bounds__(256, 8) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ qw,
     const T* __restrict__ kw, const T* __restrict__ v,
-    const float* __restrict__ la, float* __restrict__ state, T* __restrict__ ring_k,
+    const G* __restrict__ la, float* __restrict__ state, T* __restrict__ ring_k,
     T* __restrict__ ring_v, int64_t* __restrict__ pos, const T* __restrict__ mk,
     const T* __restrict__ mv, T* __restrict__ o, int H, int W, int M, float scale_log2,
     float mix) {
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
     sq[tid] = to_f(q[off]);
     sk[tid] = to_f(k[off]);
     sv[tid] = to_f(v[off]);
-    sa[tid] = exp2_fast(la[off] * kLog2e);
+    sa[tid] = exp2_fast(gate_log2(to_f(la[off]), G()));
     swq[tid] = to_f(qw[off]);
     swk[tid] = to_f(kw[off]);
   }
@@ -182,14 +182,14 @@ __global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ 
     dst[d] = (p >= 0) ? x[((size_t)bh * T_len + p) * D + d] : to_t<T>(0.f);
 }
 
-template <typename T, int D>
+template <typename T, int D, typename G>
 hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, const void* qw,
-                               const void* kw, const void* v, const float* la, float* state,
+                               const void* kw, const void* v, const void* la, float* state,
                                void* ring_k, void* ring_v, int64_t* pos, const void* mk,
                                const void* mv, void* o, hipStream_t st) {
   const size_t lds = sizeof(float) * (size_t)(s.window + s.n_meta);
-  hipLaunchKernelGGL((decode_kernel<T, D>), dim3(s.B * s.H), dim3(256), lds, st, (const T*)q,
-                     (const T*)k, (const T*)qw, (const T*)kw, (const T*)v, la, state,
+  hipLaunchKernelGGL((decode_kernel<T, D, G>), dim3(s.B * s.H), dim3(256), lds, st, (const T*)q,
+                     (const T*)k, (const T*)qw, (const T*)kw, (const T*)v, (const G*)la, state,
                      (T*)ring_k, (T*)ring_v, pos,
                      (const T*)mk, (const T*)mv, (T*)o, s.H, s.window, s.n_meta,
                      s.scale * kLog2e, s.mix);
@@ -208,19 +208,26 @@ hipError_t ring_fill_typed(const Shape& s, const void* k, const void* v, void* r
 }  // namespace
 
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* qw,
-                         const void* kw, const void* v, const float* la, float* state,
+                         const void* kw, const void* v, const void* la, float* state,
                          void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
                          void* o, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
   if (s.dtype == 1) {
+    if (s.gate == 1) {
+      if (s.dk == 128)
+        return launch_decode_typed<bf16, 128, bf16>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
+                                                     pos, mk, mv, o, st);
+      return launch_decode_typed<bf16, 64, bf16>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
+                                                  pos, mk, mv, o, st);
+    }
     if (s.dk == 128)
-      return launch_decode_typed<bf16, 128>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos,
-                                            mk, mv, o, st);
-    return launch_decode_typed<bf16, 64>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos, mk,
-                                         mv, o, st);
+      return launch_decode_typed<bf16, 128, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
+                                                    pos, mk, mv, o, st);
+    return launch_decode_typed<bf16, 64, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
+                                                 pos, mk, mv, o, st);
   }
-  return launch_decode_typed<float, 64>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos, mk,
-                                        mv, o, st);
+  return launch_decode_typed<float, 64, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos,
+                                               mk, mv, o, st);
 }
 
 hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* ring_k,

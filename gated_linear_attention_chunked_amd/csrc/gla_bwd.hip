@@ -79,9 +79,10 @@ __device__ __forceinline__ float wave_scan64(float x) {
   return x;
 }
 
+template <typename GT>
 __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
+    const GT* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
     const float* __restrict__ dhT, float* __restrict__ dh0, bf16* __restrict__ S_all,
     bf16* __restrict__ dS_all, int BH, int T_len) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
@@ -91,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   const int bh = rev ? blockIdx.x - BH : blockIdx.x;
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
-  const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb), bla(la + off, 2 * nb);
+  const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb),
+      bla(la + off, nb / 2 * (u32)sizeof(GT));
   const int nc = (T_len + kC - 1) / kC;
   const int cw = 16 * w;                  // this wave's first channel
   const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
@@ -110,13 +112,13 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   }
   // lane = token of the chunk; 16 channels from cw
   struct In {
-    u32x4 la[4];
+    Gate8<GT> la[2];
     u32x4 x[2], y[2];
   };
   auto load = [&](In& d, int ch) {
     const u32 e = (u32)(ch * kC + lane) * kD + cw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.la[i] = bla.ld128((e + 4 * i) * 4);
+    for (int i = 0; i < 2; ++i) d.la[i].load(bla, e + 8 * i);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       d.x[i] = bx.ld128((e + 8 * i) * 2);
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     // gate cumsum over the chunk, per channel
     float b[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) b[c] = wave_scan64(f_at(d.la[c >> 2], c & 3) * kLog2e);
+    for (int c = 0; c < 16; ++c)
+      b[c] = wave_scan64(gate_row<GT>(d.la[c >> 3].log2_at(c & 7), ch * kC + lane < T_len));
     float bl[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c)
@@ -245,10 +248,10 @@ __device__ __forceinline__ float pair_factor(const BwdSmem& sm, int i, int j, in
 // (r16, g) owns token t = 16w + r16 and channels 16ct + 4g + r (ct, r < 4):
 // the accumulator layout of every output tile, in which the gate cumsum and
 // the dlog_alpha scans are also kept.
-template <bool kAddQK>
+template <bool kAddQK, typename GT>
 __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
+    const GT* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
     const bf16* __restrict__ dS_all, bf16* __restrict__ dq,
     bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dla, int T_len) {
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
   const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
-  const Buf bla(la + off, 2 * nb);
+  const Buf bla(la + off, nb / 2 * (u32)sizeof(GT));
   const size_t soff = ((size_t)bh * nc + ch) * kTile;
   const u32 sb = (u32)(kTile * sizeof(bf16));
   const Buf bS(S_all + soff, sb), bdS(dS_all + soff, sb);
@@ -268,12 +271,12 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   const u32 rowe = (u32)(t0 + t) * kD;  // element offset of this lane's token row
 
   // ---- 0. every global read of the work-group, issued up front
-  u32x4 la4[4];
+  Gate4<GT> la4[4];
   u32x2 q2[4], k2[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const u32 e = rowe + 16 * ct + 4 * g;
-    la4[ct] = bla.ld128(e * 4);
+    la4[ct].load(bla, e);
     q2[ct] = ld64v(bq, e * 2);
     k2[ct] = ld64v(bk, e * 2);
   }
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) b[ct][r] = f_at(la4[ct], r) * kLog2e;
+    for (int r = 0; r < 4; ++r) b[ct][r] = gate_row<GT>(la4[ct].log2_at(r), live);
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -668,7 +671,8 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     for (int j = 0; j < w; ++j) add += *reinterpret_cast<const f32x4*>(&sm.sy[j][c0]);
     f32x4 o;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = X[ct][r] + Y[ct][r] + add[r];
+    // with logit gates, d logit = d log(alpha) * sigmoid(-logit)
+    for (int r = 0; r < 4; ++r) o[r] = (X[ct][r] + Y[ct][r] + add[r]) * gate_dlog(la4[ct].raw_at(r), GT());
     if (live) *reinterpret_cast<f32x4*>(dla + off + rowe + c0) = o;
   }
 }
@@ -683,7 +687,7 @@ size_t gla_bwd_workspace_bytes(const Shape& s) {
 
 // Scans: S_c and dS_{c+1} for every chunk, into ws.
 hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const float* h0, const float* dhT, float* dh0,
+                                const void* la, const float* h0, const float* dhT, float* dh0,
                                 const void* dO, void* ws, hipStream_t st) {
   typedef bf16 T;
   const int nc = (s.T + kC - 1) / kC;
@@ -691,16 +695,21 @@ hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, co
   if (nc == 0 || BH == 0) return hipSuccess;
   T* S_all = (T*)ws;
   T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  hipLaunchKernelGGL(gla_bwd_scans, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, h0, dhT, dh0, S_all, dS_all,
-                     BH, s.T);
+  if (s.gate == 1)
+    hipLaunchKernelGGL(gla_bwd_scans<bf16>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
+                       (const T*)k, (const T*)v, (const bf16*)la, (const T*)dO, h0, dhT, dh0,
+                       S_all, dS_all, BH, s.T);
+  else
+    hipLaunchKernelGGL(gla_bwd_scans<float>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
+                       (const T*)k, (const T*)v, (const float*)la, (const T*)dO, h0, dhT, dh0,
+                       S_all, dS_all, BH, s.T);
   return hipGetLastError();
 }
 
 // Per-chunk gradients from the scans' states; adds into dv, and into dq, dk
 // when add_qk (else writes them).
 hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const void* dO, void* dq, void* dk, void* dv,
+                                const void* la, const void* dO, void* dq, void* dk, void* dv,
                                 float* dla, const void* ws, bool add_qk, hipStream_t st) {
   typedef bf16 T;
   const int nc = (s.T + kC - 1) / kC;
@@ -708,10 +717,18 @@ hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, co
   if (nc == 0 || BH == 0) return hipSuccess;
   const T* S_all = (const T*)ws;
   const T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  hipLaunchKernelGGL(add_qk ? gla_bwd_chunk<true> : gla_bwd_chunk<false>, dim3(nc, BH),
-                     dim3(kThreads), 0, st, (const T*)q,
-                     (const T*)k, (const T*)v, la, (const T*)dO, S_all, dS_all, (T*)dq,
-                     (T*)dk, (T*)dv, dla, s.T);
+  auto go = [&](auto gate_type) {
+    typedef decltype(gate_type) GT;
+    auto kern = add_qk ? gla_bwd_chunk<true, GT> : gla_bwd_chunk<false, GT>;
+    hipLaunchKernelGGL(kern, dim3(nc, BH),
+                       dim3(kThreads), 0, st, (const T*)q, (const T*)k, (const T*)v,
+                       (const GT*)la, (const T*)dO, S_all, dS_all, (T*)dq, (T*)dk, (T*)dv, dla,
+                       s.T);
+  };
+  if (s.gate == 1)
+    go(bf16());
+  else
+    go(float());
   return hipGetLastError();
 }
 

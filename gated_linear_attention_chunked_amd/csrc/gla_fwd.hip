@@ -86,12 +86,13 @@ struct StateSmem {
   float decay[DK];
 };
 
-// Per-thread gating slice: 8 rows (8*rg ..) x 2 channels (2*cp, 2*cp+1).
-template <typename T, int DK>
+// Per-thread gating slice: 8 rows (8*rg ..) x 2 channels (2*cp, 2*cp+1); GT is
+// the gate input type (float log alpha or bf16 logit).
+template <typename T, int DK, typename GT = float>
 struct Slice {
   static constexpr int ES = sizeof(T);
   typename Pair<T>::type q[8], k[8], v[8];
-  U2 la[8];
+  typename Pair<GT>::type la[8];
   __device__ __forceinline__ void load(const Buf& bq, const Buf& bk, const Buf& bv,
                                        const Buf& bla, int t0, int rg, int cp, bool need_q) {
     const u32 row0 = (u32)(t0 + 8 * rg);
@@ -101,20 +102,21 @@ struct Slice {
       if (need_q) q[rr] = ld_pair<T>(bq, e * ES);
       k[rr] = ld_pair<T>(bk, e * ES);
       v[rr] = ld_pair<T>(bv, e * ES);
-      la[rr] = bla.ld64(e * 4);
+      la[rr] = ld_pair<GT>(bla, e * (u32)sizeof(GT));
     }
   }
 };
 
 // Local (row-group) log2 cumsum of the slice's gates; returns the group total.
-template <typename T, int DK>
-__device__ __forceinline__ f32x2 local_cumsum(const Slice<T, DK>& sl, f32x2* b) {
+template <typename T, int DK, typename GT>
+// vrows: rows of the slice before the sequence end
+__device__ __forceinline__ f32x2 local_cumsum(const Slice<T, DK, GT>& sl, f32x2* b, int vrows) {
   f32x2 run = {0.f, 0.f};
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
-    const f32x2 la = unpack2(sl.la[rr], 0.f);
-    run[0] += la[0] * kLog2e;
-    run[1] += la[1] * kLog2e;
+    const f32x2 la = unpack2(sl.la[rr], GT());
+    run[0] += gate_row<GT>(gate_log2(la[0], GT()), rr < vrows);
+    run[1] += gate_row<GT>(gate_log2(la[1], GT()), rr < vrows);
     b[rr] = run;
   }
   return run;
@@ -144,9 +146,9 @@ __device__ __forceinline__ f32x8 scale8(const f32x8& x, const float* f) {
 }
 
 // ------------------------------------------------------------------ pass 1
-template <typename T, int DK>
+template <typename T, int DK, typename GT>
 __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
-    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ la,
+    const T* __restrict__ k, const T* __restrict__ v, const GT* __restrict__ la,
     float* __restrict__ ws_state, float* __restrict__ ws_gamma, int T_len, int cps, int G) {
   constexpr int NCB = DK / 16;
   typedef typename Frag<T>::type F;
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
   const size_t off = (size_t)bh * T_len * DK;
   const Buf bk(k + off, (u32)((size_t)T_len * DK * sizeof(T)));
   const Buf bv(v + off, (u32)((size_t)T_len * DK * sizeof(T)));
-  const Buf bla(la + off, (u32)((size_t)T_len * DK * 4));
+  const Buf bla(la + off, (u32)((size_t)T_len * DK * sizeof(GT)));
   const int nc = (T_len + kC - 1) / kC;
   const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);
 
@@ -167,11 +169,11 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
   for (int cb = 0; cb < NCB; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x2 gsum = {0.f, 0.f};
 
-  Slice<T, DK> cur;
+  Slice<T, DK, GT> cur;
   cur.load(bk, bk, bv, bla, c_begin * kC, rg, cp, false);
   for (int ch = c_begin; ch < c_end; ++ch) {
     f32x2 b[8];
-    const f32x2 tot = local_cumsum(cur, b);
+    const f32x2 tot = local_cumsum(cur, b, T_len - ch * kC - 8 * rg);
     typename Pair<T>::type kk[8], vv[8];
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) { kk[rr] = cur.k[rr]; vv[rr] = cur.v[rr]; }
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
   for (int ch = c_begin; ch < c_end; ++ch) {
     const int t0 = ch * kC;
     f32x2 b[8];
-    const f32x2 tot = local_cumsum(cur, b);
+    const f32x2 tot = local_cumsum(cur, b, T_len - ch * kC - 8 * rg);
     typename Pair<T>::type qq[8], kk[8], vv[8];
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) { qq[rr] = cur.q[rr]; kk[rr] = cur.k[rr]; vv[rr] = cur.v[rr]; }
@@ -563,10 +565,10 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * kC + ((((col >> 3) ^ row ^ (row >> 3)) & 7) << 3) + (col & 7);
 }
 
-template <int DK>
+template <int DK, typename GT>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
+    const GT* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT, int T_len,
     int cps, int G) {
   constexpr int NCB = DK / 16;             // 16-row blocks of the state
@@ -784,23 +786,23 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     // per-thread byte offsets inside a chunk, fixed for the whole kernel: the
     // chunk moves the (scalar) buffer base instead, so no address register is
     // rewritten while a load that reads it may still be queued
-    const u32 vo2 = (u32)((4 * rq * DK + ch0) * 2), vo4 = (u32)((4 * rq * DK + ch0) * 4);
+    const u32 vo2 = (u32)((4 * rq * DK + ch0) * 2), ve = (u32)(4 * rq * DK + ch0);
 
-    u32x4 nq[4], nk[4], nla[4][2];  // loads in flight
-    u32x4 hq[4], hk[4], hla[4][2];  // chunk held for gating
+    u32x4 nq[4], nk[4];  // loads in flight
+    u32x4 hq[4], hk[4];  // chunk held for gating
+    Gate8<GT> nla[4], hla[4];
     // loads of one chunk, one row of the quad at a time (issued spread over the
     // gating work, so a wave never blocks on a full memory queue for long)
     struct Src { Buf q, k, la; };
     auto src_of = [&](int ch) {
       const size_t e0 = off + (size_t)ch * kC * DK;
       const u32 rem = (u32)(T_len - ch * kC) * DK;  // elements from the chunk start to the end
-      return Src{Buf(q + e0, rem * 2), Buf(k + e0, rem * 2), Buf(la + e0, rem * 4)};
+      return Src{Buf(q + e0, rem * 2), Buf(k + e0, rem * 2), Buf(la + e0, rem * (u32)sizeof(GT))};
     };
     auto issue_row = [&](const Src& sr, int rr) {
       nq[rr] = sr.q.ld128(vo2 + rr * DK * 2);
       nk[rr] = sr.k.ld128(vo2 + rr * DK * 2);
-      nla[rr][0] = sr.la.ld128(vo4 + rr * DK * 4);
-      nla[rr][1] = sr.la.ld128(vo4 + rr * DK * 4 + 16);
+      nla[rr].load(sr.la, ve + rr * DK);
     };
     auto issue = [&](int ch) {
       const Src sr = src_of(ch);
@@ -812,11 +814,10 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
       for (int rr = 0; rr < 4; ++rr) {
         hq[rr] = nq[rr];
         hk[rr] = nk[rr];
-        hla[rr][0] = nla[rr][0];
-        hla[rr][1] = nla[rr][1];
+        hla[rr] = nla[rr];
       }
     };
-    auto gate = [&](PipeBuf<DK>& X, const Src& sr) {
+    auto gate = [&](PipeBuf<DK>& X, const Src& sr, int gch) {  // gch: the chunk gated
       issue_row(sr, 0);
       // b: inclusive log2 cumsum from the chunk start (in-thread over 4 rows,
       // then a scan over the 16 row quads inside the 16-lane row)
@@ -826,7 +827,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
         float run = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          run += f_at(hla[rr][c >> 2], c & 3) * kLog2e;
+          run += gate_row<GT>(hla[rr].log2_at(c), 4 * rq + rr < T_len - gch * kC);
           b[rr][c] = run;
         }
         inc[c] = run;
@@ -940,7 +941,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     // ---- prologue: chunk c_begin gated, c_begin+1 taken
     issue(c_begin);
     take();
-    gate(sm.x[c_begin & 1], src_of(min(c_begin + 1, c_end - 1)));
+    gate(sm.x[c_begin & 1], src_of(min(c_begin + 1, c_end - 1)), c_begin);
     take();
     lds_barrier();
     // Loads are issued at the top of an iteration and taken at its end, so no
@@ -949,7 +950,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     for (int ch = c_begin; ch < c_end; ++ch) {
       const Src nx = src_of(min(ch + 2, c_end - 1));
       if (ch + 1 < c_end) {
-        gate(sm.x[(ch + 1) & 1], nx);
+        gate(sm.x[(ch + 1) & 1], nx, ch + 1);
       } else {
         issue(min(ch + 2, c_end - 1));
       }
@@ -965,24 +966,26 @@ __global__ void state_copy_kernel(const float* __restrict__ h0, float* __restric
   if (i < n) hT[i] = h0 ? h0[i] : 0.f;
 }
 
-template <typename T, int DK>
+template <typename T, int DK, typename GT>
 hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const void* k,
-                        const void* v, const float* la, const float* h0, void* o, float* hT,
+                        const void* v, const void* la_, const float* h0, void* o, float* hT,
                         void* ws, hipStream_t st) {
+  const GT* la = (const GT*)la_;
   const int BH = s.B * s.H;
   float* ws_state = (float*)ws;
   float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * DK * DK;
   if (pl.G > 1) {
-    hipLaunchKernelGGL((gla_state_pass<T, DK>), dim3(pl.G - 1, BH), dim3(4 * DK), 0, st,
+    hipLaunchKernelGGL((gla_state_pass<T, DK, GT>), dim3(pl.G - 1, BH), dim3(4 * DK), 0, st,
                        (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((gla_output_ws<DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const bf16*)q,
+    hipLaunchKernelGGL((gla_output_ws<DK, GT>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, la, h0, ws_state, ws_gamma, (bf16*)o, hT, s.T, pl.cps,
                        pl.G);
   } else {
+    static_assert(sizeof(GT) == 4, "fp32 problems take float log gates");
     hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,
                        (const T*)k, (const T*)v, la, h0, ws_state, ws_gamma, (T*)o, hT, s.T, pl.cps, pl.G);
   }
@@ -1003,7 +1006,7 @@ hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const float* la,
+hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const void* la,
                             void* ws, int* G, int* cps, hipStream_t st) {
   const Plan pl = make_plan(s);
   *G = pl.G;
@@ -1012,21 +1015,31 @@ hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const 
   const int BH = s.B * s.H;
   float* ws_state = (float*)ws;
   float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * 128 * 128;
-  hipLaunchKernelGGL((gla_state_pass<bf16, 128>), dim3(pl.G - 1, BH), dim3(512), 0, st,
-                     (const bf16*)k, (const bf16*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
+  if (s.gate == 1)
+    hipLaunchKernelGGL((gla_state_pass<bf16, 128, bf16>), dim3(pl.G - 1, BH), dim3(512), 0, st,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)la, ws_state, ws_gamma, s.T,
+                       pl.cps, pl.G);
+  else
+    hipLaunchKernelGGL((gla_state_pass<bf16, 128, float>), dim3(pl.G - 1, BH), dim3(512), 0, st,
+                       (const bf16*)k, (const bf16*)v, (const float*)la, ws_state, ws_gamma, s.T,
+                       pl.cps, pl.G);
   return hipGetLastError();
 }
 
 hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                          const float* la, const float* h0, void* o, float* hT, void* ws,
+                          const void* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st) {
   if (s.T == 0) return hT ? launch_state_copy(s, h0, hT, st) : hipSuccess;
   const Plan pl = make_plan(s);
   if (s.dtype == 1) {
-    if (s.dk == 128) return launch_typed<bf16, 128>(s, pl, q, k, v, la, h0, o, hT, ws, st);
-    return launch_typed<bf16, 64>(s, pl, q, k, v, la, h0, o, hT, ws, st);
+    if (s.gate == 1) {
+      if (s.dk == 128) return launch_typed<bf16, 128, bf16>(s, pl, q, k, v, la, h0, o, hT, ws, st);
+      return launch_typed<bf16, 64, bf16>(s, pl, q, k, v, la, h0, o, hT, ws, st);
+    }
+    if (s.dk == 128) return launch_typed<bf16, 128, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
+    return launch_typed<bf16, 64, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
   }
-  return launch_typed<float, 64>(s, pl, q, k, v, la, h0, o, hT, ws, st);
+  return launch_typed<float, 64, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
 }
 
 }  // namespace lz

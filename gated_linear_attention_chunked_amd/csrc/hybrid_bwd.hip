@@ -13,10 +13,10 @@ namespace lz {
 size_t gla_bwd_workspace_bytes(const Shape& s);
 size_t swa_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const float* h0, const float* dhT, float* dh0,
+                                const void* la, const float* h0, const float* dhT, float* dh0,
                                 const void* dO, void* ws, hipStream_t st);
 hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
-                                const float* la, const void* dO, void* dq, void* dk, void* dv,
+                                const void* la, const void* dO, void* dq, void* dk, void* dv,
                                 float* dla, const void* ws, bool add_qk, hipStream_t st);
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
@@ -78,7 +78,7 @@ size_t bwd_workspace_bytes(const Shape& s) {
 }
 
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
-                             const float* la, const void* mk, const void* mv, const float* h0,
+                             const void* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
                              void* dk, void* dv, float* dla, float* dmk, float* dmv,
                              const float* dhT, float* dh0, float* dmix, const void* qw,

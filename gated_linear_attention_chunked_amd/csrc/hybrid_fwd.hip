@@ -107,12 +107,13 @@ __device__ __forceinline__ void intra_scores(Smem& sm, int i, int j, bool fast, 
 }
 
 // kSep: the window branch reads its own queries and keys qw, kw (otherwise qw,
-// kw alias q, k and are not loaded a second time).
-template <bool kSep>
+// kw alias q, k and are not loaded a second time).  GT: gate input type (float
+// log alpha or bf16 logit).
+template <bool kSep, typename GT>
 __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ qw,
     const bf16* __restrict__ kw, const bf16* __restrict__ v,
-    const float* __restrict__ la, const bf16* __restrict__ mk, const bf16* __restrict__ mv,
+    const GT* __restrict__ la, const bf16* __restrict__ mk, const bf16* __restrict__ mv,
     const float* __restrict__ h0, const float* __restrict__ ws_state,
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT,
     bf16* __restrict__ rk, bf16* __restrict__ rv, int T_len, int H, int W, int M,
@@ -364,21 +365,21 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+7, rows 2rq, 2rq+1
     const int ch0 = 32 * pw + 8 * ol;
     const int isub = rq >> 3;                   // 16-row sub-block of the rows
-    const u32 o2 = (u32)((2 * rq * kD + ch0) * 2), o4 = (u32)((2 * rq * kD + ch0) * 4);
+    const u32 oe = (u32)(2 * rq * kD + ch0), o2 = oe * 2;
     struct In {
-      u32x4 q[2], k[2], la[2][2];
+      u32x4 q[2], k[2];
+      Gate8<GT> la[2];
       u32x4 wq[2], wk[2];  // window queries and keys (kSep only)
     };
     auto issue = [&](int ch, In& x) {
       const size_t e0 = off + (size_t)ch * kC * kD;
       const u32 rem = (u32)max(0, T_len - ch * kC) * kD;  // elements from the chunk start to the end
-      const Buf bq(q + e0, rem * 2), bk(k + e0, rem * 2), bl(la + e0, rem * 4);
+      const Buf bq(q + e0, rem * 2), bk(k + e0, rem * 2), bl(la + e0, rem * (u32)sizeof(GT));
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         x.q[rr] = bq.ld128(o2 + rr * kD * 2);
         x.k[rr] = bk.ld128(o2 + rr * kD * 2);
-        x.la[rr][0] = bl.ld128(o4 + rr * kD * 4);
-        x.la[rr][1] = bl.ld128(o4 + rr * kD * 4 + 16);
+        x.la[rr].load(bl, oe + rr * kD);
       }
       if constexpr (kSep) {
         const Buf bwq(qw + e0, rem * 2), bwk(kw + e0, rem * 2);
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         float run = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          run += f_at(x.la[rr][c >> 2], c & 3) * kLog2e;
+          run += gate_row<GT>(x.la[rr].log2_at(c), 2 * rq + rr < T_len - ch * kC);
           b[rr][c] = run;
         }
         inc[c] = run;
@@ -672,8 +673,21 @@ bool hybrid_fused_ok(const Shape& s) {
          s.n_meta <= 16 && s.T > 0;
 }
 
+template <bool kSep, typename GT>
+void launch_fused_kernel(const Shape& s, const void* q, const void* k, const void* qw,
+                         const void* kw, const void* v, const void* la, const void* mk,
+                         const void* mv, const float* h0, const float* ws_state,
+                         const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
+                         int cps, int G_, hipStream_t st) {
+  hipLaunchKernelGGL((hybrid_fwd_fused<kSep, GT>), dim3(G_, s.B * s.H), dim3(512), 0, st,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)qw, (const bf16*)kw,
+                     (const bf16*)v, (const GT*)la, (const bf16*)mk, (const bf16*)mv, h0, ws_state,
+                     ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, s.T, s.H, s.window,
+                     s.n_meta, s.scale * kLog2e, s.mix, cps, G_);
+}
+
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
-                               const void* kw, const void* v, const float* la, const void* mk,
+                               const void* kw, const void* v, const void* la, const void* mk,
                                const void* mv, const float* h0, void* o, float* hT, void* ring_k,
                                void* ring_v, void* ws, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
@@ -684,12 +698,16 @@ hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, con
   const float* ws_state = (const float*)ws;
   const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * kD * kD : nullptr;
   const bool sep = qw != nullptr;
-  auto kern = sep ? hybrid_fwd_fused<true> : hybrid_fwd_fused<false>;
-  hipLaunchKernelGGL(kern, dim3(G, BH), dim3(512), 0, st, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)(sep ? qw : q), (const bf16*)(sep ? kw : k), (const bf16*)v, la,
-                     (const bf16*)mk, (const bf16*)mv, h0, ws_state, ws_gamma, (bf16*)o, hT,
-                     (bf16*)ring_k, (bf16*)ring_v, s.T, s.H, s.window, s.n_meta,
-                     s.scale * kLog2e, s.mix, cps, G);
+  const void* qw_ = sep ? qw : q;
+  const void* kw_ = sep ? kw : k;
+  auto go = [&](auto kernel_launch) {
+    kernel_launch(s, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT, ring_k,
+                  ring_v, cps, G, st);
+  };
+  if (s.gate == 1)
+    sep ? go(launch_fused_kernel<true, bf16>) : go(launch_fused_kernel<false, bf16>);
+  else
+    sep ? go(launch_fused_kernel<true, float>) : go(launch_fused_kernel<false, float>);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ struct Shape {
   float scale;  // resolved (> 0)
   float mix;
   int dtype;    // 0 = f32, 1 = bf16
+  int gate;     // gate input: 0 = float log alpha, 1 = bf16 logit x (alpha = sigmoid(x))
 };
 
 // GLA branch: o = o_gla; hT (optional) = final state.  ws holds
@@ -19,13 +20,13 @@ struct Shape {
 // T >= 16 chunks).
 size_t gla_fwd_workspace_bytes(const Shape& s);
 hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                          const float* la, const float* h0, void* o, float* hT, void* ws,
+                          const void* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st);
 
 // State pass of the GLA branch alone (bf16, dk = dv = 128): the local end states
 // and decays of segments 0..G-2 into ws (same layout as launch_gla_fwd's
 // workspace); G segments of cps 64-token chunks each.
-hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const float* la,
+hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const void* la,
                             void* ws, int* G, int* cps, hipStream_t st);
 
 // Both branches' outputs in one pass after launch_gla_state: o = o_gla + mix *
@@ -34,7 +35,7 @@ hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const 
 bool hybrid_fused_ok(const Shape& s);
 // qw, kw: the window branch's queries and keys (both null: q, k).
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
-                               const void* kw, const void* v, const float* la, const void* mk,
+                               const void* kw, const void* v, const void* la, const void* mk,
                                const void* mv, const float* h0, void* o, float* hT, void* ring_k,
                                void* ring_v, void* ws, hipStream_t st);
 
@@ -56,7 +57,7 @@ hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStre
 
 // qw, kw: the window branch's query and key (pass q, k when they are shared).
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* qw,
-                         const void* kw, const void* v, const float* la, float* state,
+                         const void* kw, const void* v, const void* la, float* state,
                          void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
                          void* o, hipStream_t st);
 
@@ -66,7 +67,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* k, const voi
 bool bwd_supported(const Shape& s);
 size_t bwd_workspace_bytes(const Shape& s);
 hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const void* v,
-                             const float* la, const void* mk, const void* mv, const float* h0,
+                             const void* la, const void* mk, const void* mv, const float* h0,
                              const void* o_swa, const float* lse, const void* dO, void* dq,
                              void* dk, void* dv, float* dla, float* dmk, float* dmv,
                              const float* dhT, float* dh0, float* dmix, const void* qw,

@@ -10,11 +10,12 @@ namespace {
 
 using lz::Shape;
 
-constexpr int32_t kVersion = 10000;  // 1.0.0
+constexpr int32_t kVersion = 10100;  // 1.1.0
 
 lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
   if (!d) return LIZARD_E_NULL;
   if (d->dtype != LIZARD_F32 && d->dtype != LIZARD_BF16) return LIZARD_E_DTYPE;
+  if (d->gate != LIZARD_GATE_LOG_ALPHA && d->gate != LIZARD_GATE_LOGIT) return LIZARD_E_DTYPE;
   if (d->B < 0 || d->H < 0 || (need_T && d->T < 0)) return LIZARD_E_SHAPE;
   if (d->dk <= 0 || d->dv <= 0 || d->chunk <= 0 || d->window < 1 || d->n_meta < 0)
     return LIZARD_E_SHAPE;
@@ -23,6 +24,7 @@ lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
   if (d->dk != d->dv) return LIZARD_E_UNSUPPORTED;
   if (d->dk != 64 && d->dk != 128) return LIZARD_E_UNSUPPORTED;
   if (d->dtype == LIZARD_F32 && d->dk != 64) return LIZARD_E_UNSUPPORTED;
+  if (d->gate == LIZARD_GATE_LOGIT && d->dtype != LIZARD_BF16) return LIZARD_E_UNSUPPORTED;
   if (d->n_meta > 16) return LIZARD_E_UNSUPPORTED;
   const long long bh = (long long)d->B * d->H;
   if (bh > 65535) return LIZARD_E_UNSUPPORTED;  // work-group grid limit of the prefill kernels
@@ -43,6 +45,7 @@ Shape to_shape(const lizard_desc_t* d) {
   s.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
   s.mix = d->mix;
   s.dtype = d->dtype;
+  s.gate = d->gate;
   return s;
 }
 
@@ -79,16 +82,16 @@ size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op) {
 }
 
 lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
-                               const void* v, const float* log_alpha, const float* h0, void* o,
+                               const void* v, const void* gate, const float* h0, void* o,
                                float* hT, void* ws, size_t ws_bytes, hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
-  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  if (has_tokens(desc) && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
   const size_t need = lz::gla_fwd_workspace_bytes(to_shape(desc));
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
-  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, log_alpha, h0, o, hT, ws, stream));
+  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, gate, h0, o, hT, ws, stream));
 }
 
 lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
@@ -105,14 +108,14 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
 }
 
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,
                                   void* o_swa, float* hT, void* ring_k, void* ring_v,
                                   const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
-  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o)) return LIZARD_E_NULL;
+  if (has_tokens(desc) && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
   if ((q_w == nullptr) != (k_w == nullptr)) return LIZARD_E_NULL;
   // the window branch's queries and keys (the same as the GLA branch's by default)
   const void* qw = q_w ? q_w : q;
@@ -127,11 +130,11 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
   hipError_t e = hipSuccess;
   if (desc->T > 0 && !lse && !o_swa && lz::hybrid_fused_ok(s)) {
     // state pass, then both branches in one output pass (o written once)
-    e = lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, log_alpha, meta_k, meta_v, h0, o, hT,
+    e = lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o, hT,
                                 ring_k, ring_v, ws, stream);
   } else if (desc->T > 0) {
     // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
-    e = lz::launch_gla_fwd(s, q, k, v, log_alpha, h0, o, hT, ws, stream);
+    e = lz::launch_gla_fwd(s, q, k, v, gate, h0, o, hT, ws, stream);
     if (e == hipSuccess)
       e = lz::launch_swa_fwd(s, qw, kw, v, meta_k, meta_v, o, s.mix, 1, o_swa, lse, ring_k,
                              ring_v, stream);
@@ -143,10 +146,10 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
 }
 
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                                  float* dlog_alpha, float* dmeta_k, float* dmeta_v,
+                                  float* dgate, float* dmeta_k, float* dmeta_v,
                                   const float* dhT, float* dh0, float* dmix, const void* q_w,
                                   const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
@@ -156,8 +159,8 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
   const int n_sep = !!q_w + !!k_w + !!dq_w + !!dk_w;
   if (n_sep != 0 && n_sep != 4) return LIZARD_E_NULL;
   const bool meta = desc->n_meta > 0 && desc->H > 0;
-  if (has_tokens(desc) && (!q || !k || !v || !log_alpha || !o_swa || !lse || !dO || !dq || !dk ||
-                           !dv || !dlog_alpha))
+  if (has_tokens(desc) && (!q || !k || !v || !gate || !o_swa || !lse || !dO || !dq || !dk ||
+                           !dv || !dgate))
     return LIZARD_E_NULL;
   if (meta && (!meta_k || !meta_v || !dmeta_k || !dmeta_v)) return LIZARD_E_NULL;
   const Shape s = to_shape(desc);
@@ -166,13 +169,13 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
-  return hip_status(lz::launch_hybrid_bwd(s, q, k, v, log_alpha, meta_k, meta_v, h0, o_swa, lse,
-                                          dO, dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v, dhT, dh0,
+  return hip_status(lz::launch_hybrid_bwd(s, q, k, v, gate, meta_k, meta_v, h0, o_swa, lse,
+                                          dO, dq, dk, dv, dgate, dmeta_k, dmeta_v, dhT, dh0,
                                           dmix, q_w, k_w, dq_w, dk_w, ws, stream));
 }
 
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
-                                   const void* v, const float* log_alpha, float* state,
+                                   const void* v, const void* gate, float* state,
                                    void* ring_k, void* ring_v, int64_t* pos, const void* meta_k,
                                    const void* meta_v, const void* q_w, const void* k_w, void* o,
                                    hipStream_t stream) {
@@ -180,7 +183,7 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
   if (st != LIZARD_OK) return st;
   if (!q_w != !k_w) return LIZARD_E_NULL;  // window query and key: both or neither
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
-  if (!q || !k || !v || !log_alpha || !state || !ring_k || !ring_v || !pos || !o)
+  if (!q || !k || !v || !gate || !state || !ring_k || !ring_v || !pos || !o)
     return LIZARD_E_NULL;
   if (desc->n_meta > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   // the window softmax keeps w + M logits in LDS
@@ -188,7 +191,7 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
   // the heads of a sequence count their completion in bits 40.. of pos[b]
   if (desc->H >= (1 << 22)) return LIZARD_E_UNSUPPORTED;
   return hip_status(lz::launch_decode(to_shape(desc), q, k, q_w ? q_w : q, k_w ? k_w : k, v,
-                                      log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, o,
+                                      gate, state, ring_k, ring_v, pos, meta_k, meta_v, o,
                                       stream));
 }
 

@@ -23,7 +23,12 @@
  *   - Tensors are dense, row-major, device memory owned by the caller:
  *       q, k        [B, H, T, dk]      dtype of desc->dtype
  *       v, o        [B, H, T, dv]      dtype of desc->dtype
- *       log_alpha   [B, H, T, dk]      float32, finite, <= 0
+ *       gate        [B, H, T, dk]      the per-channel decay, as desc->gate says:
+ *                                      LIZARD_GATE_LOG_ALPHA: float32 log alpha,
+ *                                      finite, <= 0;  LIZARD_GATE_LOGIT: bf16
+ *                                      logits x, alpha = sigmoid(x) (the
+ *                                      section's learnable sigmoid gate), half
+ *                                      the bytes, log-sigmoid taken in-kernel
  *       meta_k      [H, M, dk]         dtype of desc->dtype (shared by the batch)
  *       meta_v      [H, M, dv]         dtype of desc->dtype
  *       state/h0/hT [B, H, dk, dv]     float32 (row = key channel)
@@ -68,6 +73,9 @@ typedef enum {
 
 typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype_t;
 
+/* Format of the gate input (desc->gate). */
+typedef enum { LIZARD_GATE_LOG_ALPHA = 0, LIZARD_GATE_LOGIT = 1 } lizard_gate_t;
+
 typedef enum {
   LIZARD_OP_GLA_FWD = 0,
   LIZARD_OP_SWA_FWD = 1,
@@ -86,6 +94,7 @@ typedef struct {
   float scale;       /* softmax logit scale; <= 0 selects 1/sqrt(dk)                 */
   float mix;         /* weight of the window branch in the combine                   */
   int32_t dtype;     /* lizard_dtype_t of q, k, v, o, meta, ring, dq, dk, dv          */
+  int32_t gate;      /* lizard_gate_t of the gate input; LIZARD_GATE_LOGIT needs BF16 */
 } lizard_desc_t;
 
 /* Bytes of scratch memory `op` needs for `desc` (0 if none).  Never fails: an
@@ -101,7 +110,7 @@ size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op);
  * (h0, or zeros, when T == 0).  ws must hold lizard_workspace_bytes(desc,
  * LIZARD_OP_GLA_FWD) bytes (it may be NULL when that is 0). */
 lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const void* k,
-                               const void* v, const float* log_alpha, const float* h0,
+                               const void* v, const void* gate, const float* h0,
                                void* o, float* hT, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
@@ -123,7 +132,7 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
  * NULL means the window branch reads q, k.  The window cache holds k_w.
  * ws must hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) bytes. */
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,
                                   void* o_swa, float* hT, void* ring_k, void* ring_v,
                                   const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
@@ -131,7 +140,8 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
 
 /* Hybrid backward for the loss sum(dO * o) + sum(dhT * hT).  Reads the forward
  * inputs plus the o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv
- * (desc->dtype), dlog_alpha [B,H,T,dk], dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all
+ * (desc->dtype), dgate [B,H,T,dk] (the gradient with respect to the gate input:
+ * d log_alpha, or d x = d log_alpha * sigmoid(-x) for logits), dmeta_k [H,M,dk], dmeta_v [H,M,dv] (all
  * float32 except dq/dk/dv).  Every output is fully overwritten.  h0 (nullable) as
  * in the forward.  dhT [B,H,dk,dv] float32 (nullable = zero) is the gradient of
  * the final state hT; dh0 [B,H,dk,dv] float32 (nullable = not written) receives
@@ -151,16 +161,16 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
  * gradients alone.  With them NULL, dq and dk hold both branches' gradients.
  * This version supports BF16 with dk = dv = 64 (LIZARD_E_UNSUPPORTED otherwise). */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const float* log_alpha, const void* meta_k,
+                                  const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,
                                   const float* lse, const void* dO, void* dq, void* dk,
-                                  void* dv, float* dlog_alpha, float* dmeta_k, float* dmeta_v,
+                                  void* dv, float* dgate, float* dmeta_k, float* dmeta_v,
                                   const float* dhT, float* dh0, float* dmix, const void* q_w,
                                   const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
 /* One constant-memory generation step for B sequences (desc->T is ignored).
- * q, k [B,H,dk], v [B,H,dv] in desc->dtype; log_alpha [B,H,dk] float32.
+ * q, k [B,H,dk], v [B,H,dv] in desc->dtype; gate [B,H,dk] as desc->gate says.
  * pos [B] int64 (device): tokens already seen by each sequence.  The call
  * updates state in place, writes (k, v) to ring slot pos mod w, attends over the
  * min(pos+1, w) filled slots plus the M meta slots, writes o [B,H,dv] and then
@@ -171,7 +181,7 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
  * both given, else LIZARD_E_NULL): the window branch's own query and key, as
  * in lizard_hybrid_fwd; k_w (else k) goes into the ring, q_w (else q) attends. */
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,
-                                   const void* v, const float* log_alpha, float* state,
+                                   const void* v, const void* gate, float* state,
                                    void* ring_k, void* ring_v, int64_t* pos,
                                    const void* meta_k, const void* meta_v, const void* q_w,
                                    const void* k_w, void* o, hipStream_t stream);

@@ -20,10 +20,11 @@ NULLP = None
 
 def desc(**kw):
     base = dict(B=1, H=2, T=128, dk=64, dv=64, chunk=64, window=64, n_meta=4, scale=0.0, mix=1.0,
-                dtype=_abi.LIZARD_BF16)
+                dtype=_abi.LIZARD_BF16, gate=_abi.LIZARD_GATE_LOG_ALPHA)
     base.update(kw)
     return _abi.Desc(base["B"], base["H"], base["T"], base["dk"], base["dv"], base["chunk"],
-                     base["window"], base["n_meta"], base["scale"], base["mix"], base["dtype"])
+                     base["window"], base["n_meta"], base["scale"], base["mix"], base["dtype"],
+                     base["gate"])
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
@@ -55,11 +56,12 @@ def test_status_strings_and_version():
     for code in range(7):
         assert lib.lizard_status_str(code)
     assert lib.lizard_status_str(99) == b"unknown status"
-    assert lib.lizard_version() == 10000
+    assert lib.lizard_version() == 10100
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=7), 3),
+    (dict(dtype=7), 3), (dict(gate=2), 3), (dict(gate=-1), 3),
+    (dict(gate=_abi.LIZARD_GATE_LOGIT, dtype=_abi.LIZARD_F32), 4),
     (dict(B=-1), 2), (dict(T=-5), 2), (dict(dk=0), 2), (dict(window=0), 2), (dict(n_meta=-1), 2),
     (dict(chunk=0), 2), (dict(scale=float("nan")), 2), (dict(mix=float("inf")), 2),
     (dict(chunk=32), 4), (dict(dk=96, dv=96), 4), (dict(dk=64, dv=128), 4),

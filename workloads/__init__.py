@@ -61,11 +61,15 @@ def _torch_dtype(name):
 
 
 def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
-                with_grad_out=False, with_h0=False, with_window_qk=False, **_ignored):
+                with_grad_out=False, with_h0=False, with_window_qk=False, with_gate_logits=False,
+                **_ignored):
     """Draw one prefill/training batch on the CPU.  Returns a dict of tensors:
     q, k [B,H,T,dk]; v [B,H,T,dv]; log_alpha [B,H,T,dk] fp32; meta_k [H,M,dk];
-    meta_v [H,M,dv]; optionally dO [B,H,T,dv], h0 [B,H,dk,dv] fp32 and the window
-    branch's own q_w, k_w [B,H,T,dk] (drawn last, like q and k)."""
+    meta_v [H,M,dv]; optionally dO [B,H,T,dv], h0 [B,H,dk,dv] fp32, the window
+    branch's own q_w, k_w [B,H,T,dk] (drawn last, like q and k) and, with
+    with_gate_logits, gate_x [B,H,T,dk] bf16: the same gate draw x as logits
+    (log_alpha = logsigmoid(x) is computed from the fp32 draw, so the two
+    differ by the bf16 rounding of x)."""
     g = torch.Generator().manual_seed(seed)
     dt = _torch_dtype(dtype)
     q = torch.randn(B, H, T, dk, generator=g) / math.sqrt(dk)
@@ -77,6 +81,8 @@ def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
     meta_v = torch.randn(H, n_meta, dv, generator=g)
     out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), log_alpha=log_alpha,
                meta_k=meta_k.to(dt), meta_v=meta_v.to(dt))
+    if with_gate_logits:
+        out["gate_x"] = x.to(torch.bfloat16)
     if with_grad_out:
         out["dO"] = torch.randn(B, H, T, dv, generator=g).to(dt)
     if with_h0:
@@ -88,7 +94,7 @@ def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
 
 
 def make_decode_inputs(steps, B, H, dk, dv, dtype="bf16", seed=1, gate_mean=2.0,
-                       with_window_qk=False, **_ignored):
+                       with_window_qk=False, with_gate_logits=False, **_ignored):
     """Per-step decode tokens: q, k [steps,B,H,dk]; v [steps,B,H,dv];
     log_alpha [steps,B,H,dk] fp32, drawn in the order q, k, v, x (then q_w, k_w
     [steps,B,H,dk] with with_window_qk)."""
@@ -100,6 +106,8 @@ def make_decode_inputs(steps, B, H, dk, dv, dtype="bf16", seed=1, gate_mean=2.0,
     x = torch.randn(steps, B, H, dk, generator=g) + gate_mean
     out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt),
                log_alpha=torch.nn.functional.logsigmoid(x).float())
+    if with_gate_logits:
+        out["gate_x"] = x.to(torch.bfloat16)
     if with_window_qk:
         out["q_w"] = (torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)).to(dt)
         out["k_w"] = (torch.randn(steps, B, H, dk, generator=g) / math.sqrt(dk)).to(dt)
