@@ -245,6 +245,7 @@ def main():
     if not args.no_extras:
         out["prefill_gate_logits"] = bench_prefill_gate_logits(lz, torch, dev, args)
         out["long_prefill"] = bench_long_prefill(lz, torch, dev, args, ms / (B * T))
+        out["prefill_varlen"] = bench_prefill_varlen(lz, torch, dev, args)
         out["decode"] = bench_decode(lz, torch, dev)
         try:
             out["train"] = bench_train(lz, torch, dev, args)
@@ -310,6 +311,54 @@ def bench_long_prefill(lz, torch, dev, args, ms_per_token_headline):
     return {"workload": "prefill_bf16_b1_h32_t32768_d128", "ms_per_call": ms,
             "tokens_per_s": wl.B * wl.T / (ms / 1e3),
             "time_per_token_vs_headline": per_tok / ms_per_token_headline}
+
+
+def bench_prefill_varlen(lz, torch, dev, args):
+    """Serving prefill: a packed batch of 16 sequences of 64..8192 tokens (seeded
+    lengths), H=32, d=128, w=128, M=4, through lizard_hybrid_fwd_varlen with the
+    final states and window caches; inputs drawn on the device with a seeded
+    generator (the headline's value families)."""
+    from gated_linear_attention_chunked_amd import _abi
+    from workloads import packed_lengths
+    lengths = packed_lengths(16, 64, 8192, seed=0)
+    H, d, w, M = 32, 128, 128, 4
+    N, B = sum(lengths), len(lengths)
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape, mean=0.0, scale=1.0, dt=torch.bfloat16):
+        return (torch.randn(*shape, device=dev, generator=g) * scale + mean).to(dt)
+
+    s = 1.0 / math.sqrt(d)
+    q, k, v = (rnd(H, N, d, scale=s) for _ in range(3))
+    la = torch.nn.functional.logsigmoid(rnd(H, N, d, mean=2.0, dt=torch.float32))
+    mk, mv = rnd(H, M, d), rnd(H, M, d)
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths), 0).to(torch.int32)
+    cu = cu.to(dev)
+    o = torch.empty_like(v)
+    hT = torch.empty(B, H, d, d, device=dev)
+    rk = torch.empty(B, H, w, d, device=dev, dtype=torch.bfloat16)
+    rv = torch.empty_like(rk)
+    desc = lz.make_desc(B, H, max(lengths), d, d, w, M, s, 1.0, torch.bfloat16)
+    nws = lz.workspace_bytes(desc, _abi.OP_HYBRID_FWD)
+    ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (ctypes.byref(desc), P(cu), N, P(q), P(k), P(v), P(la), P(mk), P(mv), None, P(o), P(hT),
+         P(rk), P(rv), None, None, P(ws), nws, stream)
+    lib = lz.lib()
+
+    def step():
+        st = lib.lizard_hybrid_fwd_varlen(*a)
+        if st != 0:
+            raise RuntimeError(f"lizard_hybrid_fwd_varlen: status {st}")
+
+    ms = event_time_ms(step, max(10, args.steps // 5), max(5, args.warmup // 5))
+    nbytes = H * N * (3 * d * 2 + d * 4 + d * 2) + B * H * (d * d * 4 + 2 * w * d * 2) + H * M * d * 4
+    return {"workload": "packed serving prefill: 16 sequences of 64..8192 tokens (seed 0), "
+                        "H32 d128 w128 M4", "tokens": N, "ms_per_call": ms,
+            "tokens_per_s": N / (ms / 1e3), "algorithmic_GBs": nbytes / (ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_decode(lz, torch, dev):

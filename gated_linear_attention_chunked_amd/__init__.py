@@ -19,7 +19,7 @@ import torch
 from . import _abi
 from ._abi import LizardError, lib  # noqa: F401
 
-__all__ = ["gla_fwd", "swa_fwd", "hybrid_fwd", "hybrid_bwd", "decode_step",
+__all__ = ["gla_fwd", "swa_fwd", "hybrid_fwd", "hybrid_fwd_varlen", "hybrid_bwd", "decode_step",
            "workspace_bytes", "make_desc", "LizardError", "lib"]
 
 _DTYPES = {torch.float32: _abi.LIZARD_F32, torch.bfloat16: _abi.LIZARD_BF16}
@@ -162,6 +162,43 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
         _p(out.get("ring_k")), _p(out.get("ring_v")), _p(q_w), _p(k_w), _p(ws), nws, _stream()))
+    return out
+
+
+def hybrid_fwd_varlen(q, k, v, log_alpha, meta_k, meta_v, window, cu_seqlens, max_seqlen,
+                      scale=None, mix=1.0, h0=None, return_state=False, return_ring=False,
+                      q_w=None, k_w=None):
+    """Hybrid forward over a packed batch: q, k, log_alpha (and q_w, k_w) [H, N, dk],
+    v [H, N, dv]; sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32
+    device tensor [B+1]); max_seqlen bounds every length.  Returns a dict with "o"
+    [H, N, dv] and, on request, the per-sequence "hT" [B,H,dk,dv] and
+    "ring_k"/"ring_v" [B,H,w,d]."""
+    H, N, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    B = cu_seqlens.shape[0] - 1
+    _need(q, "q", (H, N, dk), dt)
+    _need(k, "k", (H, N, dk), dt)
+    _need(v, "v", (H, N, dv), dt)
+    _need(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32)
+    _window_pair(q_w, k_w, (H, N, dk), dt)
+    gate = _gate(log_alpha, "log_alpha", (H, N, dk))
+    meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
+    _opt(h0, "h0", (B, H, dk, dv), torch.float32)
+    dev = q.device
+    out = {"o": torch.empty_like(v)}
+    if return_state:
+        out["hT"] = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    if return_ring:
+        out["ring_k"] = torch.empty(B, H, window, dk, device=dev, dtype=dt)
+        out["ring_v"] = torch.empty(B, H, window, dv, device=dev, dtype=dt)
+    d = make_desc(B, H, int(max_seqlen), dk, dv, window, M, scale, mix, dt, gate=gate)
+    nws = workspace_bytes(d, _abi.OP_HYBRID_FWD)
+    ws = torch.empty(nws, device=dev, dtype=torch.uint8) if nws else None
+    _abi.check("lizard_hybrid_fwd_varlen", lib().lizard_hybrid_fwd_varlen(
+        ctypes.byref(d), _p(cu_seqlens), N, _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k),
+        _p(meta_v), _p(h0), _p(out["o"]), _p(out.get("hT")), _p(out.get("ring_k")),
+        _p(out.get("ring_v")), _p(q_w), _p(k_w), _p(ws), nws, _stream()))
     return out
 
 

@@ -39,6 +39,8 @@ _SIGS = {
     "lizard_gla_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P, ctypes.c_size_t, P]),
     "lizard_swa_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P]),
     "lizard_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 15 + [P, ctypes.c_size_t, P]),
+    "lizard_hybrid_fwd_varlen": (ctypes.c_int, [ctypes.POINTER(Desc), P, ctypes.c_int32]
+                                 + [P] * 13 + [P, ctypes.c_size_t, P]),
     "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 23 + [P, ctypes.c_size_t, P]),
     "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P]),
     "lizard_status_str": (ctypes.c_char_p, [ctypes.c_int]),

@@ -192,6 +192,21 @@ __device__ __forceinline__ float gate_dlog(float x, bf16) {
   return __builtin_amdgcn_rcpf(1.f + exp2_fast(x * kLog2e));
 }
 
+// Token rows of one (sequence, head) pair.  Dense batches [B, H, T, d]: T rows
+// from (b H + h) T.  Packed batches [H, N, d]: sequence b is rows cu[b] ..
+// cu[b+1]-1 of head h's N rows (clamped into [0, N], and its length to T).
+struct SeqRows {
+  size_t row0;
+  int len;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int* cu, int N, int T, int H, int bh) {
+  if (!cu) return SeqRows{(size_t)bh * T, T};
+  const int b = bh / H, h = bh - b * H;
+  const int s0 = min(max(cu[b], 0), N);
+  const int s1 = min(max(cu[b + 1], s0), N);
+  return SeqRows{(size_t)h * N + s0, min(s1 - s0, T)};
+}
+
 // Log2 gate of a token row: rows at or past the sequence end (loaded as zero
 // bytes) must not decay.  A float log gate of 0 already means alpha = 1; a
 // logit of 0 would mean alpha = 1/2, so logit rows there are masked to 0.

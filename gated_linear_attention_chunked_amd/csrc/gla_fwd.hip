@@ -149,7 +149,8 @@ __device__ __forceinline__ f32x8 scale8(const f32x8& x, const float* f) {
 template <typename T, int DK, typename GT>
 __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
     const T* __restrict__ k, const T* __restrict__ v, const GT* __restrict__ la,
-    float* __restrict__ ws_state, float* __restrict__ ws_gamma, int T_len, int cps, int G) {
+    float* __restrict__ ws_state, float* __restrict__ ws_gamma, int T_arg, int cps, int G,
+    const int* __restrict__ cu, int N, int H) {
   constexpr int NCB = DK / 16;
   typedef typename Frag<T>::type F;
   __shared__ StateSmem<T, DK> sm;
@@ -157,7 +158,13 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
   const int r16 = lane & 15, g = lane >> 4;
   const int cp = tid % (DK / 2), rg = tid / (DK / 2);
   const int seg = blockIdx.x, bh = blockIdx.y;
-  const size_t off = (size_t)bh * T_len * DK;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
+  const size_t off = sr.row0 * DK;
+  // a packed sequence has its own segment count; only segments before its
+  // last one need a local end state
+  const int nc_seq = (T_len + kC - 1) / kC;
+  if (cu && seg >= max(1, (nc_seq + cps - 1) / cps) - 1) return;
   const Buf bk(k + off, (u32)((size_t)T_len * DK * sizeof(T)));
   const Buf bv(v + off, (u32)((size_t)T_len * DK * sizeof(T)));
   const Buf bla(la + off, (u32)((size_t)T_len * DK * sizeof(GT)));
@@ -976,7 +983,8 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
   float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * DK * DK;
   if (pl.G > 1) {
     hipLaunchKernelGGL((gla_state_pass<T, DK, GT>), dim3(pl.G - 1, BH), dim3(4 * DK), 0, st,
-                       (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G);
+                       (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G,
+                       (const int*)nullptr, 0, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1018,11 +1026,11 @@ hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const 
   if (s.gate == 1)
     hipLaunchKernelGGL((gla_state_pass<bf16, 128, bf16>), dim3(pl.G - 1, BH), dim3(512), 0, st,
                        (const bf16*)k, (const bf16*)v, (const bf16*)la, ws_state, ws_gamma, s.T,
-                       pl.cps, pl.G);
+                       pl.cps, pl.G, s.cu, s.n_tokens, s.H);
   else
     hipLaunchKernelGGL((gla_state_pass<bf16, 128, float>), dim3(pl.G - 1, BH), dim3(512), 0, st,
                        (const bf16*)k, (const bf16*)v, (const float*)la, ws_state, ws_gamma, s.T,
-                       pl.cps, pl.G);
+                       pl.cps, pl.G, s.cu, s.n_tokens, s.H);
   return hipGetLastError();
 }
 

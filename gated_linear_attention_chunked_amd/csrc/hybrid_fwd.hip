@@ -116,14 +116,20 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const GT* __restrict__ la, const bf16* __restrict__ mk, const bf16* __restrict__ mv,
     const float* __restrict__ h0, const float* __restrict__ ws_state,
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT,
-    bf16* __restrict__ rk, bf16* __restrict__ rv, int T_len, int H, int W, int M,
-    float scale_log2, float mix, int cps, int G) {
+    bf16* __restrict__ rk, bf16* __restrict__ rv, int T_arg, int H, int W, int M,
+    float scale_log2, float mix, int cps, int G, const int* __restrict__ cu, int N) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
-  const size_t off = (size_t)bh * T_len * kD;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
+  const size_t off = sr.row0 * kD;
   const int nc = (T_len + kC - 1) / kC;
+  // a packed sequence covers the first Gs of the plan's segments (at least
+  // one, which for an empty sequence writes hT = h0 and an empty cache)
+  const int Gs = cu ? max(1, (nc + 2 * cps - 1) / (2 * cps)) : G;
+  if (seg >= Gs) return;
   // segments are whole 64-token chunks of the state pass
   const int c_begin = 2 * seg * cps, c_end = min(nc, c_begin + 2 * cps);
   const size_t s_base = (size_t)bh * kD * kD;
@@ -144,7 +150,11 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     }
   }
 
-  if (wave < 4) {
+  if (nc == 0) {
+    // an empty packed sequence: the state passes through unchanged
+    if (hT)
+      for (int e = tid; e < kD * kD; e += 512) hT[s_base + e] = h0 ? h0[s_base + e] : 0.f;
+  } else if (wave < 4) {
     // ------------------------------------------------------------ consumers
     const int cw = wave;
     // state entering the segment: h0 carried through the earlier segments'
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       step(c + 1, V0);
     }
     if (c < c_end) step(c, V1);
-    if (hT && seg == G - 1) {
+    if (hT && seg == Gs - 1) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -650,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const Buf bk(kw + off, (u32)((size_t)T_len * kD * 2)), bv(v + off, (u32)((size_t)T_len * kD * 2));
     const size_t rbase = (size_t)bh * W * kD;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const int s_lo = (int)((long long)W * seg / G), s_hi = (int)((long long)W * (seg + 1) / G);
+    const int s_lo = (int)((long long)W * seg / Gs), s_hi = (int)((long long)W * (seg + 1) / Gs);
     for (int e = s_lo * 16 + tid; e < s_hi * 16; e += 512) {
       const int slot = e >> 4, c = (e & 15) * 8;
       const int p = slot < T_len % W ? T_len - T_len % W + slot : T_len - T_len % W - W + slot;
@@ -683,7 +693,7 @@ void launch_fused_kernel(const Shape& s, const void* q, const void* k, const voi
                      (const bf16*)q, (const bf16*)k, (const bf16*)qw, (const bf16*)kw,
                      (const bf16*)v, (const GT*)la, (const bf16*)mk, (const bf16*)mv, h0, ws_state,
                      ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, s.T, s.H, s.window,
-                     s.n_meta, s.scale * kLog2e, s.mix, cps, G_);
+                     s.n_meta, s.scale * kLog2e, s.mix, cps, G_, s.cu, s.n_tokens);
 }
 
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,

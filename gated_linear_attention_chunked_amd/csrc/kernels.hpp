@@ -13,6 +13,10 @@ struct Shape {
   float mix;
   int dtype;    // 0 = f32, 1 = bf16
   int gate;     // gate input: 0 = float log alpha, 1 = bf16 logit x (alpha = sigmoid(x))
+  // packed batches (single-pass forward only): tensors [H, n_tokens, d], sequence b
+  // = tokens cu[b] .. cu[b+1]-1 (device array of B+1), T = the longest length
+  const int* cu = nullptr;
+  int n_tokens = 0;
 };
 
 // GLA branch: o = o_gla; hT (optional) = final state.  ws holds

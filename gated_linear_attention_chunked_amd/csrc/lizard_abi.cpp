@@ -145,6 +145,36 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
   return hip_status(e);
 }
 
+lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_t* cu_seqlens,
+                                         int32_t n_tokens, const void* q, const void* k,
+                                         const void* v, const void* gate, const void* meta_k,
+                                         const void* meta_v, const float* h0, void* o, float* hT,
+                                         void* ring_k, void* ring_v, const void* q_w,
+                                         const void* k_w, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (n_tokens < 0) return LIZARD_E_SHAPE;
+  if ((q_w == nullptr) != (k_w == nullptr)) return LIZARD_E_NULL;
+  if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
+  if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
+  Shape s = to_shape(desc);
+  // packed batches run on the single-pass kernels only
+  if (desc->T < 1 || !lz::hybrid_fused_ok(s)) return LIZARD_E_UNSUPPORTED;
+  // per-head token rows are addressed with 32-bit byte offsets
+  if ((long long)n_tokens * desc->dk * 4 >= (1LL << 31)) return LIZARD_E_UNSUPPORTED;
+  const size_t need = lz::gla_fwd_workspace_bytes(s);
+  if (ws_bytes < need) return LIZARD_E_WORKSPACE;
+  if (need > 0 && !ws) return LIZARD_E_NULL;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  if (!cu_seqlens) return LIZARD_E_NULL;
+  if (n_tokens > 0 && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
+  s.cu = cu_seqlens;
+  s.n_tokens = n_tokens;
+  return hip_status(lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o,
+                                            hT, ring_k, ring_v, ws, stream));
+}
+
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,

@@ -138,6 +138,30 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* Hybrid forward over a packed batch of sequences of different lengths (serving
+ * prefill).  q, k, v, gate, o (and q_w, k_w) are [H, n_tokens, d]: sequence b
+ * holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head.  cu_seqlens is
+ * a device array of B+1 int32 with 0 = cu[0] <= cu[1] <= ... <= cu[B] =
+ * n_tokens, and desc->T must be at least the longest length (it sizes the
+ * work split and the workspace); the kernels clamp entries into [0, n_tokens]
+ * and lengths to desc->T.  h0, hT [B,H,dk,dv] and ring_k/ring_v [B,H,w,d] are
+ * per sequence, as in lizard_hybrid_fwd, so lizard_decode_step continues
+ * every sequence from pos[b] = its length.  Each sequence's outputs equal those
+ * of lizard_hybrid_fwd on that sequence alone (the state of "Lizard: An
+ * Efficient Linearization Framework for Large Language Models", gist.science
+ * summary, section 2(a), starts from h0 at each sequence's first token, and no
+ * window reaches into another sequence).  Inference outputs only (no lse,
+ * o_swa); bf16 with dk = dv = 128 and w <= 129 (LIZARD_E_UNSUPPORTED
+ * otherwise).  ws must hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD)
+ * bytes. */
+lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_t* cu_seqlens,
+                                         int32_t n_tokens, const void* q, const void* k,
+                                         const void* v, const void* gate, const void* meta_k,
+                                         const void* meta_v, const float* h0, void* o, float* hT,
+                                         void* ring_k, void* ring_v, const void* q_w,
+                                         const void* k_w, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
+
 /* Hybrid backward for the loss sum(dO * o) + sum(dhT * hT).  Reads the forward
  * inputs plus the o_swa and lse that lizard_hybrid_fwd saved.  Writes dq, dk, dv
  * (desc->dtype), dgate [B,H,T,dk] (the gradient with respect to the gate input:

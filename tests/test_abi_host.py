@@ -101,6 +101,23 @@ def test_window_inputs_come_in_pairs():
                                      None) == 1
 
 
+def test_packed_forward_arguments_are_checked():
+    lib = _abi.lib()
+    d = desc(dk=128, dv=128, T=4096)
+    need = lib.lizard_workspace_bytes(ctypes.byref(d), 2)
+    call = lambda dd, cu=FAKE, n=100, ws_bytes=need, qw=None, kw=None: lib.lizard_hybrid_fwd_varlen(
+        ctypes.byref(dd), cu, n, *([FAKE] * 6), None, FAKE, None, None, None, qw, kw, FAKE,
+        ws_bytes, None)
+    assert call(d, n=-1) == 2
+    assert call(d, cu=None) == 1
+    assert call(d, qw=FAKE) == 1
+    assert call(d, ws_bytes=need - 1) == 5
+    assert call(desc(T=4096)) == 4                           # d = 64: no single-pass kernel
+    assert call(desc(dk=128, dv=128, T=4096, window=200)) == 4
+    assert call(desc(dk=128, dv=128, T=0)) == 4               # the longest length must be >= 1
+    assert call(desc(dk=128, dv=128, T=4096, B=0)) == 0       # nothing to do
+
+
 def test_empty_problems_enqueue_nothing():
     # B*H == 0: valid, nothing to do, no HIP call
     assert gla(desc(B=0), q=None, k=None, v=None, la=None, o=None) == 0

@@ -93,6 +93,44 @@ def make_inputs(B, H, T, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
     return out
 
 
+def packed_lengths(n_seq, lo, hi, seed):
+    """Sequence lengths of a packed (serving) batch: n_seq draws uniform in
+    [lo, hi] from a seeded generator."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, (n_seq,), generator=g).tolist()
+
+
+def make_packed_inputs(lengths, H, dk, dv, n_meta, dtype="bf16", seed=0, gate_mean=2.0,
+                       with_h0=False, with_window_qk=False, with_gate_logits=False):
+    """A packed batch: q, k, log_alpha [H, N, dk], v [H, N, dv] (N = sum of the
+    lengths), sequence b at tokens cu[b] .. cu[b+1]-1; cu_seqlens int32 [B+1];
+    meta_k/meta_v [H, M, d]; optionally h0 [B, H, dk, dv] fp32, the window
+    branch's q_w, k_w and bf16 gate logits gate_x.  Same value families as
+    make_inputs."""
+    g = torch.Generator().manual_seed(seed)
+    dt = _torch_dtype(dtype)
+    N, B = int(sum(lengths)), len(lengths)
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    q = torch.randn(H, N, dk, generator=g) / math.sqrt(dk)
+    k = torch.randn(H, N, dk, generator=g) / math.sqrt(dk)
+    v = torch.randn(H, N, dv, generator=g) / math.sqrt(dv)
+    x = torch.randn(H, N, dk, generator=g) + gate_mean
+    meta_k = torch.randn(H, n_meta, dk, generator=g)
+    meta_v = torch.randn(H, n_meta, dv, generator=g)
+    out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt),
+               log_alpha=torch.nn.functional.logsigmoid(x).float(),
+               meta_k=meta_k.to(dt), meta_v=meta_v.to(dt), cu_seqlens=cu)
+    if with_h0:
+        out["h0"] = torch.randn(B, H, dk, dv, generator=g) * 0.1
+    if with_window_qk:
+        out["q_w"] = (torch.randn(H, N, dk, generator=g) / math.sqrt(dk)).to(dt)
+        out["k_w"] = (torch.randn(H, N, dk, generator=g) / math.sqrt(dk)).to(dt)
+    if with_gate_logits:
+        out["gate_x"] = x.to(torch.bfloat16)
+    return out
+
+
 def make_decode_inputs(steps, B, H, dk, dv, dtype="bf16", seed=1, gate_mean=2.0,
                        with_window_qk=False, with_gate_logits=False, **_ignored):
     """Per-step decode tokens: q, k [steps,B,H,dk]; v [steps,B,H,dv];
