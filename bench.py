@@ -149,7 +149,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on a single GPU; multi-GPU runs are not supported "
+        print("bench.py: the library runs on a single GPU; multi-GPU runs are not supported "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -63,7 +63,7 @@ const char* lizard_status_str(lizard_status_t s) {
     case LIZARD_E_NULL: return "a required pointer is NULL";
     case LIZARD_E_SHAPE: return "invalid size or parameter";
     case LIZARD_E_DTYPE: return "unknown dtype";
-    case LIZARD_E_UNSUPPORTED: return "configuration not supported by this build";
+    case LIZARD_E_UNSUPPORTED: return "configuration not supported in this version";
     case LIZARD_E_WORKSPACE: return "workspace too small";
     case LIZARD_E_HIP: return "HIP launch failed";
   }
