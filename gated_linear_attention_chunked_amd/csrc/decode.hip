@@ -170,16 +170,19 @@ __global__ __launch_bounds__(256, 8) void decode_kernel(
 
 template <typename T>
 __global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                 T* __restrict__ rk, T* __restrict__ rv, int T_len, int W, int D) {
+                                 T* __restrict__ rk, T* __restrict__ rv, int T_arg, int W, int D,
+                                 const int* __restrict__ cu, int N, int H) {
   const int slot = blockIdx.x, bh = blockIdx.y;
   const T* x = blockIdx.z ? v : k;  // z = 0: keys, z = 1: values
   T* ring = blockIdx.z ? rv : rk;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
   // the position p = slot (mod W) inside [T - W, T), if any
   long base = (long)T_len - W;
   long p = base + ((((long)slot - base) % W) + W) % W;
   T* dst = ring + ((size_t)bh * W + slot) * D;
   for (int d = threadIdx.x; d < D; d += blockDim.x)
-    dst[d] = (p >= 0) ? x[((size_t)bh * T_len + p) * D + d] : to_t<T>(0.f);
+    dst[d] = (p >= 0) ? x[(sr.row0 + p) * D + d] : to_t<T>(0.f);
 }
 
 template <typename T, int D, typename G>
@@ -201,7 +204,7 @@ hipError_t ring_fill_typed(const Shape& s, const void* k, const void* v, void* r
                            hipStream_t st) {
   dim3 grid(s.window, s.B * s.H, 2);  // dk == dv
   hipLaunchKernelGGL(ring_fill_kernel<T>, grid, dim3(64), 0, st, (const T*)k, (const T*)v,
-                     (T*)rk, (T*)rv, s.T, s.window, s.dk);
+                     (T*)rk, (T*)rv, s.T, s.window, s.dk, s.cu, s.n_tokens, s.H);
   return hipGetLastError();
 }
 

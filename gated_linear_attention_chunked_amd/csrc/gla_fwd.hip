@@ -576,8 +576,8 @@ template <int DK, typename GT>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const GT* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
-    const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT, int T_len,
-    int cps, int G) {
+    const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT, int T_arg,
+    int cps, int G, const int* __restrict__ cu, int N, int H) {
   constexpr int NCB = DK / 16;             // 16-row blocks of the state
   constexpr int KS = DK / 32;              // contraction steps over channels
   constexpr int NWC = DK / 32;             // consumer waves (= producer waves)
@@ -590,10 +590,20 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
   const int r16 = lane & 15, g = lane >> 4;
   const bool consumer = wave < NWC;
   const int seg = blockIdx.x, bh = blockIdx.y;
-  const size_t off = (size_t)bh * T_len * DK;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
+  const size_t off = sr.row0 * DK;
   const int nc = (T_len + kC - 1) / kC;
   const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);
   const size_t s_base = (size_t)bh * DK * DK;
+  // a packed sequence covers the first Gs of the plan's segments
+  const int Gs = cu ? max(1, (nc + cps - 1) / cps) : G;
+  if (seg >= Gs) return;
+  if (nc == 0) {  // an empty packed sequence: the state passes through unchanged
+    if (hT)
+      for (int e = tid; e < DK * DK; e += 4 * DK) hT[s_base + e] = h0 ? h0[s_base + e] : 0.f;
+    return;
+  }
 
   for (int e = tid; e < 512; e += 4 * DK) {
     const int z = e >> 8, t = (e >> 4) & 15, s = e & 15;
@@ -775,7 +785,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
       if (has_next) store_vT(sm.x[(ch + 1) & 1]);
       lds_barrier();  // (B) chunk done
     }
-    if (hT && seg == G - 1) {
+    if (hT && seg == Gs - 1) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -984,14 +994,14 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
   if (pl.G > 1) {
     hipLaunchKernelGGL((gla_state_pass<T, DK, GT>), dim3(pl.G - 1, BH), dim3(4 * DK), 0, st,
                        (const T*)k, (const T*)v, la, ws_state, ws_gamma, s.T, pl.cps, pl.G,
-                       (const int*)nullptr, 0, s.H);
+                       s.cu, s.n_tokens, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2) {
     hipLaunchKernelGGL((gla_output_ws<DK, GT>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, la, h0, ws_state, ws_gamma, (bf16*)o, hT, s.T, pl.cps,
-                       pl.G);
+                       pl.G, s.cu, s.n_tokens, s.H);
   } else {
     static_assert(sizeof(GT) == 4, "fp32 problems take float log gates");
     hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,

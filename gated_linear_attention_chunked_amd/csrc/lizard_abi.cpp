@@ -159,8 +159,8 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
   if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   Shape s = to_shape(desc);
-  // packed batches run on the single-pass kernels only
-  if (desc->T < 1 || !lz::hybrid_fused_ok(s)) return LIZARD_E_UNSUPPORTED;
+  // packed batches: bf16 problems (the fp32 output pass has no packed form)
+  if (desc->T < 1 || desc->dtype != LIZARD_BF16) return LIZARD_E_UNSUPPORTED;
   // per-head token rows are addressed with 32-bit byte offsets
   if ((long long)n_tokens * desc->dk * 4 >= (1LL << 31)) return LIZARD_E_UNSUPPORTED;
   const size_t need = lz::gla_fwd_workspace_bytes(s);
@@ -171,8 +171,15 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   if (n_tokens > 0 && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
   s.cu = cu_seqlens;
   s.n_tokens = n_tokens;
-  return hip_status(lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o,
-                                            hT, ring_k, ring_v, ws, stream));
+  if (lz::hybrid_fused_ok(s))
+    return hip_status(lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o,
+                                              hT, ring_k, ring_v, ws, stream));
+  // other shapes: the GLA branch writes o, the window branch adds mix * o_swa
+  hipError_t e = lz::launch_gla_fwd(s, q, k, v, gate, h0, o, hT, ws, stream);
+  if (e == hipSuccess)
+    e = lz::launch_swa_fwd(s, q_w ? q_w : q, k_w ? k_w : k, v, meta_k, meta_v, o, s.mix, 1,
+                           nullptr, nullptr, ring_k, ring_v, stream);
+  return hip_status(e);
 }
 
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,

@@ -34,8 +34,8 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ mk, const T* __restrict__ mv, T* __restrict__ o,
-    T* __restrict__ o_swa, float* __restrict__ lse, int T_len, int H, int W, int M,
-    float scale_log2, float out_scale, int accumulate) {
+    T* __restrict__ o_swa, float* __restrict__ lse, int T_arg, int H, int W, int M,
+    float scale_log2, float out_scale, int accumulate, const int* __restrict__ cu, int N) {
   constexpr int KS = DK / 32;
   constexpr int NT = DV / 16;
   typedef typename Frag<T>::type F;
@@ -46,11 +46,14 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
   const int nqt = gridDim.x;
   const int logical = xcd_remap(blockIdx.y * nqt + blockIdx.x, nqt * gridDim.y);
   const int bh = logical / nqt, h = bh % H;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
   const int t0 = (logical % nqt) * kQT;
+  if (t0 >= T_len) return;            // tiles past a packed sequence's end
   const int tq0 = t0 + 16 * wave;     // first query of this wave
   const int tq = tq0 + r16;           // this lane's query (column of the logit tiles)
-  const size_t qk_base = (size_t)bh * T_len * DK;
-  const size_t v_base = (size_t)bh * T_len * DV;
+  const size_t qk_base = sr.row0 * DK;
+  const size_t v_base = sr.row0 * DV;
   const Buf bk(k + qk_base, (u32)((size_t)T_len * DK * sizeof(T)));
   const Buf bv(v + v_base, (u32)((size_t)T_len * DV * sizeof(T)));
 
@@ -242,7 +245,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ mk, const T* __restrict__ mv, T* __restrict__ o,
     T* __restrict__ o_swa, float* __restrict__ lse, T* __restrict__ rk, T* __restrict__ rv,
-    int T_len, int H, int W, int M, float scale_log2, float out_scale, int accumulate, int cps) {
+    int T_arg, int H, int W, int M, float scale_log2, float out_scale, int accumulate, int cps,
+    const int* __restrict__ cu, int N) {
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int NPREV = NS - 2;
@@ -260,10 +264,16 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
   const int nseg = gridDim.x;
   const int logical = xcd_remap(blockIdx.y * nseg + blockIdx.x, nseg * gridDim.y);
   const int bh = logical / nseg, h = bh % H, seg = logical % nseg;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
   const int nc = (T_len + kKT - 1) / kKT;
+  // a packed sequence covers the first Gs segments (an empty one: one segment
+  // that only clears its window cache)
+  const int Gs = cu ? max(1, (nc + cps - 1) / cps) : nseg;
+  if (seg >= Gs) return;
   const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);  // cps is even
   const int half = wave >> 2, wq = wave & 3;  // this wave's tile of the step, block in it
-  const size_t base = (size_t)bh * T_len * D;
+  const size_t base = sr.row0 * D;
   const u32 nbytes = (u32)((size_t)T_len * D * sizeof(T));
   const Buf bq(q + base, nbytes), bk(k + base, nbytes), bv(v + base, nbytes);
 
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_ring(
     constexpr int RG = D / PER;               // 16-byte pieces per row
     const size_t rbase = (size_t)bh * W * D;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const int s_lo = (int)((long long)W * seg / nseg), s_hi = (int)((long long)W * (seg + 1) / nseg);
+    const int s_lo = (int)((long long)W * seg / Gs), s_hi = (int)((long long)W * (seg + 1) / Gs);
     for (int e = s_lo * RG + tid; e < s_hi * RG; e += 512) {
       const int slot = e / RG, c = (e % RG) * PER;
       const int p = slot < T_len % W ? T_len - T_len % W + slot : T_len - T_len % W - W + slot;
@@ -531,18 +541,20 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
     if (s.window <= kKT + 1) {
       hipLaunchKernelGGL((swa_fwd_ring<T, D, 3>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
-                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps,
+                         s.cu, s.n_tokens);
     } else {
       hipLaunchKernelGGL((swa_fwd_ring<T, D, 4>), dim3(G, s.B * s.H), dim3(512), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa,
-                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps);
+                         lse, (T*)rk, (T*)rv, s.T, s.H, s.window, s.n_meta, sl, out_scale, acc, cps,
+                         s.cu, s.n_tokens);
     }
     return hipGetLastError();
   }
   dim3 grid((s.T + kQT - 1) / kQT, s.B * s.H);
   hipLaunchKernelGGL((swa_fwd_kernel<T, D, D>), grid, dim3(256), 0, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa, lse, s.T, s.H,
-                     s.window, s.n_meta, s.scale * kLog2e, out_scale, acc);
+                     s.window, s.n_meta, s.scale * kLog2e, out_scale, acc, s.cu, s.n_tokens);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && rk) e = launch_ring_fill(s, k, v, rk, rv, st);
   return e;

@@ -112,8 +112,7 @@ def test_packed_forward_arguments_are_checked():
     assert call(d, cu=None) == 1
     assert call(d, qw=FAKE) == 1
     assert call(d, ws_bytes=need - 1) == 5
-    assert call(desc(T=4096)) == 4                           # d = 64: no single-pass kernel
-    assert call(desc(dk=128, dv=128, T=4096, window=200)) == 4
+    assert call(desc(T=4096, dtype=_abi.LIZARD_F32)) == 4     # packed batches: bf16 only
     assert call(desc(dk=128, dv=128, T=0)) == 4               # the longest length must be >= 1
     assert call(desc(dk=128, dv=128, T=4096, B=0)) == 0       # nothing to do
 

@@ -4,10 +4,11 @@ fp64 oracle run on every sequence alone.
 Each sequence's o rows, final state and window cache must match the oracle's
 single-sequence forward (its own h0, no window reaching into a neighbour).
 Cases: lengths 0, 1, chunk-aligned and ragged, several state segments, a bound
-max_seqlen larger than every length, an initial state per sequence, gate logits
-and separate window inputs, decode continuing every sequence from its own
-position, and the serving-mix workload (16 sequences of 64..8192 tokens, H=32,
-d=128) on sampled sequences and heads.
+max_seqlen larger than every length, d = 64 and windows past 129 (the
+two-kernel path, with the streaming and the tiled window kernels), an initial
+state per sequence, gate logits and separate window inputs, decode continuing
+every sequence from its own position, and the serving-mix workload (16
+sequences of 64..8192 tokens, H=32, d=128) on sampled sequences and heads.
 """
 import math
 
@@ -62,15 +63,18 @@ def check_all(inp, out, w, s, mix, sep=False, logits=False, seqs=None, heads=Non
         assert_close(f"ring_v[seq {b}]", out["ring_v"][b:b + 1, hs], ref["ring_v"], BF, tol=0.0)
 
 
-@pytest.mark.parametrize("lengths,w,M,bound", [
-    ([0, 1, 31, 32, 33, 300, 2100, 129], 128, 4, 0),
-    ([700, 64, 0, 1500], 64, 0, 4096),        # max_seqlen above every length
-    ([5000], 129, 16, 0),                     # one long sequence
+@pytest.mark.parametrize("lengths,d,w,M,bound", [
+    ([0, 1, 31, 32, 33, 300, 2100, 129], 128, 128, 4, 0),  # single-pass kernel
+    ([700, 64, 0, 1500], 128, 64, 0, 4096),                 # max_seqlen above every length
+    ([5000], 128, 129, 16, 0),                              # one long sequence
+    ([0, 1, 65, 300, 1300, 64], 64, 64, 4, 0),              # d = 64: two-kernel path
+    ([257, 0, 900, 3], 64, 200, 2, 1000),                   # tiled window (w > 129)
+    ([129, 640, 0, 77], 128, 300, 4, 0),
 ])
-def test_packed_forward_matches_each_sequence(lengths, w, M, bound):
-    print(f"[case] varlen lengths {lengths} w{w} M{M} bound{bound}", flush=True)
-    s, mix = 1.0 / math.sqrt(D), 0.85
-    inp = make_packed_inputs(lengths, 2, D, D, M, seed=sum(lengths) % 97, with_h0=True)
+def test_packed_forward_matches_each_sequence(lengths, d, w, M, bound):
+    print(f"[case] varlen lengths {lengths} d{d} w{w} M{M} bound{bound}", flush=True)
+    s, mix = 1.0 / math.sqrt(d), 0.85
+    inp = make_packed_inputs(lengths, 2, d, d, M, seed=sum(lengths) % 97, with_h0=True)
     out = run(inp, w, s, mix, max(max(lengths), bound, 1))
     check_all(inp, out, w, s, mix)
 
