@@ -49,18 +49,23 @@ constexpr int kD = 128;            // d_k = d_v
 constexpr int kRing = 5;           // window ring slots: chunks c-4 .. c
 constexpr int kMaxW = 4 * kC + 1;  // widest window the ring holds
 constexpr float kFast = 64.f;      // single reference while every chunk decay >= 2^-64
+// Row of the transposed [channel][token] tiles (k-hat^T, the V^T ring, meta V^T):
+// 32 tokens padded to 80 bytes.  Their staging stores write four rows 8 apart
+// per instruction; at 64-byte rows those rows share one set of banks, at 80
+// bytes they fall on two, and the 16-row fragment reads stay conflict-free.
+constexpr int kTP = kC + 8;
 
 struct Smem {
   bf16 qs[kC * kD];              // gated q [t][ch]: q 2^{b_t} (or 2^{b_t - R_i})
   bf16 ks[kC * kD];              // gated k [s][ch]: k 2^{-b_s} (or 2^{R_j - b_s})
-  bf16 khT[kD * kC];             // [ch][s]: k 2^{b_last - b_s}
+  bf16 khT[kD * kTP];            // [ch][s]: k 2^{b_last - b_s}
   bf16 a[kC * kC];               // masked intra scores [t][s]
   bf16 p[kRing + 1][kC * kC];    // window probabilities [t][s] per ring chunk, meta last
-  bf16 vT[kRing][kD * kC];       // V^T ring [n][s]
+  bf16 vT[kRing][kD * kTP];      // V^T ring [n][s]
   bf16 kr[kRing][kC * kD];       // raw K ring [s][ch]
   bf16 qr[kC * kD];              // raw q [t][ch]
   bf16 mk[16 * kD];              // meta keys (rows >= M zero)
-  bf16 mvT[kD * kC];             // meta values transposed (slots >= M zero)
+  bf16 mvT[kD * kTP];            // meta values transposed (slots >= M zero)
   alignas(16) float decay[kD];   // 2^{b_last}
   alignas(16) float eR[2][kD];   // 2^{R_i} (1 for single-reference channels)
   alignas(16) float vij[kD];     // 2^{R_1 - R_0} (likewise)
@@ -72,6 +77,8 @@ struct Smem {
 // [rows][128] and [rows][32] tiles, granules permuted by row
 __device__ __forceinline__ int at16(int row, int col) { return swz_at<16>(row, col); }
 __device__ __forceinline__ int at4(int row, int col) { return swz_at<4>(row, col); }
+// (row, col) of a padded transposed tile
+__device__ __forceinline__ int atp(int row, int col) { return row * kTP + col; }
 
 // Split-map fragment (elements col..col+3 and col+16..col+19) of a [rows][128] tile.
 __device__ __forceinline__ bf16x8 ld_split16(const bf16* t, int row, int col) {
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     }
     for (int e = tid; e < kD * kC; e += 512) {
       const int c = e / kC, t = e % kC;
-      sm.mvT[at4(c, t)] = t < M ? mvh[t * kD + c] : (bf16)0.f;
+      sm.mvT[atp(c, t)] = t < M ? mvh[t * kD + c] : (bf16)0.f;
     }
   }
 
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const u32 w0 = x[0][c >> 1], w1 = x[1][c >> 1];
-        *reinterpret_cast<u32*>(&dst[at4(32 * cw + 8 * vo + c, 2 * vr)]) =
+        *reinterpret_cast<u32*>(&dst[atp(32 * cw + 8 * vo + c, 2 * vr)]) =
             (c & 1) ? hi2(w0, w1) : lo2(w0, w1);
       }
     };
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
     for (int r = 0; r < kRing; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32*>(&sm.vT[r][at4(32 * cw + 8 * vo + c, 2 * vr)]) = 0u;
+      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32*>(&sm.vT[r][atp(32 * cw + 8 * vo + c, 2 * vr)]) = 0u;
     {  // ring: chunks c_begin-4 .. c_begin
       u32x4 pro[kRing][2];
 #pragma unroll
@@ -264,11 +271,11 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       // ---- phase 1: state update, S = diag(2^{b_last}) S + khT V
       bf16x8 vf[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) vf[nt] = ld8<bf16>(&sm.vT[slot][at4(32 * cw + 16 * nt + r16, 8 * g)]);
+      for (int nt = 0; nt < 2; ++nt) vf[nt] = ld8<bf16>(&sm.vT[slot][atp(32 * cw + 16 * nt + r16, 8 * g)]);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const f32x4 dec = *reinterpret_cast<const f32x4*>(&sm.decay[16 * cb + 4 * g]);
-        const bf16x8 kf = ld8<bf16>(&sm.khT[at4(16 * cb + r16, 8 * g)]);
+        const bf16x8 kf = ld8<bf16>(&sm.khT[atp(16 * cb + r16, 8 * g)]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           S[nt][cb] *= dec;
@@ -317,8 +324,8 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
               wf[r - r0][nt] = r == kRing - 1 ? vf[nt]
-                             : r == kRing     ? ld8<bf16>(&sm.mvT[at4(32 * cw + 16 * nt + r16, 8 * g)])
-                                              : ld8<bf16>(&sm.vT[sl][at4(32 * cw + 16 * nt + r16, 8 * g)]);
+                             : r == kRing     ? ld8<bf16>(&sm.mvT[atp(32 * cw + 16 * nt + r16, 8 * g)])
+                                              : ld8<bf16>(&sm.vT[sl][atp(32 * cw + 16 * nt + r16, 8 * g)]);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) pf[r - r0][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
           }
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           for (int u = 0; u < 2; ++u) {
             const int c = 2 * c2 + u;
             const float e = kSingle ? dl[c] : eKh[c];
-            *reinterpret_cast<u32*>(&sm.khT[at4(ch0 + c, 2 * rq)]) = pack_bf2(kx[0][u] * e, kx[1][u] * e);
+            *reinterpret_cast<u32*>(&sm.khT[atp(ch0 + c, 2 * rq)]) = pack_bf2(kx[0][u] * e, kx[1][u] * e);
           }
         }
       };
