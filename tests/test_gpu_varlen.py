@@ -79,14 +79,15 @@ def test_packed_forward_matches_each_sequence(lengths, d, w, M, bound):
     check_all(inp, out, w, s, mix)
 
 
-def test_packed_forward_gate_logits_and_window_inputs():
+@pytest.mark.parametrize("d,w", [(128, 100), (64, 64), (64, 180)])
+def test_packed_forward_gate_logits_and_window_inputs(d, w):
     lengths = [257, 0, 1100, 40]
-    print(f"[case] varlen logits + window inputs {lengths}", flush=True)
-    s, mix = 1.0 / math.sqrt(D), 0.7
-    inp = make_packed_inputs(lengths, 2, D, D, 4, seed=3, gate_mean=-1.0, with_h0=True,
+    print(f"[case] varlen logits + window inputs {lengths} d{d} w{w}", flush=True)
+    s, mix = 1.0 / math.sqrt(d), 0.7
+    inp = make_packed_inputs(lengths, 2, d, d, 4, seed=3, gate_mean=-1.0, with_h0=True,
                              with_window_qk=True, with_gate_logits=True)
-    out = run(inp, 100, s, mix, max(lengths), sep=True, logits=True)
-    check_all(inp, out, 100, s, mix, sep=True, logits=True)
+    out = run(inp, w, s, mix, max(lengths), sep=True, logits=True)
+    check_all(inp, out, w, s, mix, sep=True, logits=True)
 
 
 def test_decode_continues_each_packed_sequence():
