@@ -80,11 +80,13 @@ def counter_traffic(workload, digest):
     return None
 
 
+# minimum warm-up time of the secondary lines (a quarter of --min-warmup-seconds)
+_MIN_WARM = [0.25]
+
+
 def event_time_ms(fn, steps, warmup):
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(fn, warmup, _MIN_WARM[0])
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
@@ -95,31 +97,71 @@ def event_time_ms(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def cpu_baseline(wl, seconds):
-    """The fp64 oracle as it stands, on one host core, on whole heads of the same
-    workload until about `seconds` of CPU work; reported in tokens/s."""
-    import numpy as np
+def _oracle_worker(task):
+    """One host process: the oracle on the same head again and again until
+    `seconds` have passed; returns (heads done, seconds)."""
+    x, wl, seconds = task
     import oracle
-    from workloads import make_inputs, to_f64_numpy
     from threadpoolctl import threadpool_limits
-    inp = make_inputs(1, 1, wl["T"], wl["dk"], wl["dv"], wl["n_meta"], dtype=wl["dtype"], seed=0)
-    x = {n: to_f64_numpy(t) for n, t in inp.items()}
-    heads, tokens = 0, 0
+    heads = 0
     with threadpool_limits(1):
         t0 = time.perf_counter()
         while True:
             oracle.hybrid_forward(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"],
                                   x["meta_v"], wl["window"], wl["scale"], mix=wl["mix"])
             heads += 1
-            tokens += wl["T"]
             if time.perf_counter() - t0 >= seconds:
                 break
-        dt = time.perf_counter() - t0
+    return heads, time.perf_counter() - t0
+
+
+def host_cores():
+    """Host cores for the CPU baseline: the process's affinity set, capped at the
+    16-core share a one-GPU machine gives a job."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, seconds, cores):
+    """The fp64 oracle as it stands, on `cores` host processes (BLAS limited to
+    one thread each), each running whole heads of the same workload for about
+    `seconds`; reported in layer tokens/s.  Runs before the GPU is touched, so
+    the worker processes are plain forks of a process with no GPU context."""
+    import multiprocessing as mp
+    from workloads import make_inputs, to_f64_numpy
+    inp = make_inputs(1, 1, wl["T"], wl["dk"], wl["dv"], wl["n_meta"], dtype=wl["dtype"], seed=0)
+    x = {n: to_f64_numpy(t) for n, t in inp.items()}
+    task = (x, dict(wl), seconds)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_worker, [task] * cores)
+    wall = time.perf_counter() - t0
+    heads = sum(h for h, _ in res)
     # one head of T tokens is 1/H of a batch element's work: tokens/s of the
     # whole layer = head-tokens/s / H
-    return {"value": tokens / dt / wl["H"], "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} head(s) x T={wl['T']} of the same workload "
-                      f"(one head of one sequence per pass), fp64 numpy, {dt:.1f} s"}
+    return {"value": heads * wl["T"] / wall / wl["H"], "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} head(s) x T={wl['T']} of the same workload (one head of one "
+                      f"sequence per pass, heads spread over {cores} processes, BLAS 1 thread "
+                      f"each), fp64 numpy, {wall:.1f} s wall"}
+
+
+def warm_up(fn, steps, min_seconds=1.0):
+    """At least `steps` untimed calls, and more until `min_seconds` have passed
+    (the GPU runs about 10% slower until its clocks settle); returns the number
+    of calls made."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < min_seconds:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def main():
@@ -138,7 +180,10 @@ def main():
                     help="only time the training step (forward + backward), for profiling")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode steps, for profiling")
+    ap.add_argument("--min-warmup-seconds", type=float, default=1.0,
+                    help="keep warming up past --warmup steps until this much time has passed")
     args = ap.parse_args()
+    _MIN_WARM[0] = args.min_warmup_seconds / 4
     if args.copy_probe:
         import torch
         a = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -153,10 +198,17 @@ def main():
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    from workloads import WORKLOADS, make_inputs
+    name = "prefill_bf16_b2_h32_t4096_d128"
+    wl = WORKLOADS[name]
+    cpu = None
+    if not (args.no_cpu_baseline or args.decode_only or args.train_only):
+        # before anything touches the GPU: the workers are forks of this process
+        cpu = cpu_baseline(wl, args.cpu_seconds, host_cores())
+
     import torch
     import gated_linear_attention_chunked_amd as lz
     from gated_linear_attention_chunked_amd import _abi
-    from workloads import WORKLOADS, make_inputs
 
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(lz, torch, torch.device("cuda:0"))}), flush=True)
@@ -165,8 +217,6 @@ def main():
         print(json.dumps({"train": bench_train(lz, torch, torch.device("cuda:0"), args)}),
               flush=True)
         return
-    name = "prefill_bf16_b2_h32_t4096_d128"
-    wl = WORKLOADS[name]
     B, H, T, d, w, M, C = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta, wl.chunk
     dev = torch.device("cuda:0")
     inp = make_inputs(B, H, T, d, d, M, dtype=wl.dtype, seed=0)
@@ -192,9 +242,7 @@ def main():
             raise RuntimeError(f"lizard_hybrid_fwd: status {st}")
 
     # ---- timed region: exactly K steps between two synchronisations
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup_run = warm_up(step, args.warmup, args.min_warmup_seconds)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(args.steps):
@@ -222,7 +270,7 @@ def main():
     out = {
         "metric": "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_steps_run": warmup_run, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "B": B, "H": H, "T": T, "dk": d, "dv": d, "chunk": C,
                    "window": w, "n_meta": M, "parallelism": "single GPU"},
@@ -247,12 +295,15 @@ def main():
         out["long_prefill"] = bench_long_prefill(lz, torch, dev, args, ms / (B * T))
         out["prefill_varlen"] = bench_prefill_varlen(lz, torch, dev, args)
         out["decode"] = bench_decode(lz, torch, dev)
+        # twice the batch: a 512 MiB working set (state + window cache), twice the
+        # 256 MB last-level cache, so bytes / time cannot be served from it
+        out["decode_b128"] = bench_decode(lz, torch, dev, B=128, steps=256)
         try:
             out["train"] = bench_train(lz, torch, dev, args)
         except lz.LizardError as e:
             out["train"] = {"error": str(e)}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
@@ -361,12 +412,15 @@ def bench_prefill_varlen(lz, torch, dev, args):
             "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
-def bench_decode(lz, torch, dev):
-    """1024 decode steps (B=64, H=32, d=128, w=128, M=4) after a 2048-token hybrid
-    prefill; inputs drawn on the device with a seeded generator (same recipe)."""
+def bench_decode(lz, torch, dev, B=None, steps=None):
+    """Decode steps (B=64, H=32, d=128, w=128, M=4; 1024 steps by default) after
+    a 2048-token hybrid prefill; inputs drawn on the device with a seeded
+    generator (same recipe)."""
     from workloads import WORKLOADS
     wl = WORKLOADS["decode_bf16_b64_h32_d128"]
-    B, H, T, d, w, M, steps = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta, wl.steps
+    H, T, d, w, M = wl.H, wl.T, wl.dk, wl.window, wl.n_meta
+    B = wl.B if B is None else B
+    steps = wl.steps if steps is None else steps
     g = torch.Generator(device=dev).manual_seed(0)
 
     def rnd(*shape, mean=0.0, scale=1.0, dt=torch.bfloat16):
@@ -393,17 +447,35 @@ def bench_decode(lz, torch, dev):
     ms = e0.elapsed_time(e1)
     nbytes = sum(decode_bytes_per_step(B, H, d, w, M, T + i) for i in range(steps))
     gbs = nbytes / (ms / 1e3) / 1e9
-    return {"workload": "decode_bf16_b64_h32_d128", "steps": steps, "ms_total": ms,
+    ws_mib = B * H * (d * d * 4 + 2 * w * d * 2) / 2**20
+    return {"workload": f"decode_bf16_b{B}_h{H}_d{d}", "B": B, "steps": steps,
+            "working_set_MiB": ws_mib, "ms_total": ms,
             "us_per_step": ms * 1e3 / steps, "tokens_per_s": B * steps / (ms / 1e3),
             "algorithmic_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-            "note": "algorithmic bytes equal the counter-measured bytes per step "
-                    "(profiles/decode_b64_h32_d128.md)"}
+            "note": "algorithmic bytes: each state, ring and token byte moved once per step; "
+                    "a working set near the 256 MB last-level cache may be served partly "
+                    "from it, one of twice that size cannot"}
+
+
+def train_bytes(B, H, T, d):
+    """Algorithmic HBM bytes of one training step (bf16 tensors, fp32 gates):
+    forward reads q, k, v, log_alpha and writes o, o_swa, lse; backward reads
+    q, k, v, log_alpha, dO, o_swa, lse and writes dq, dk, dv, dlog_alpha (meta
+    tensors are negligible)."""
+    fwd = 3 * d * 2 + d * 4 + d * 2 + d * 2 + 4
+    bwd = 5 * d * 2 + d * 4 + 4 + 3 * d * 2 + d * 4
+    return B * H * T * (fwd + bwd)
+
+
+TRAIN_SOURCES = ("common.hpp", "gla_fwd.hip", "swa_fwd.hip", "gla_bwd.hip", "swa_bwd.hip",
+                 "hybrid_bwd.hip", "hybrid_fwd.hip")
 
 
 def bench_train(lz, torch, dev, args):
     """Forward (saving lse and o_swa) + backward of B=8, H=16, T=2048, d=64, w=64, M=4."""
     from workloads import WORKLOADS, make_inputs
-    wl = WORKLOADS["train_bf16_b8_h16_t2048_d64"]
+    name = "train_bf16_b8_h16_t2048_d64"
+    wl = WORKLOADS[name]
     B, H, T, d, w, M = wl.B, wl.H, wl.T, wl.dk, wl.window, wl.n_meta
     x = {n: t.to(dev) for n, t in make_inputs(B, H, T, d, d, M, dtype=wl.dtype, seed=0,
                                               with_grad_out=True).items()}
@@ -415,8 +487,13 @@ def bench_train(lz, torch, dev, args):
                       f["o_swa"], f["lse"], x["dO"])
 
     ms = event_time_ms(step, max(3, args.steps // 2), max(2, args.warmup // 2))
-    return {"workload": "train_bf16_b8_h16_t2048_d64", "ms_per_step": ms,
-            "tokens_per_s": B * T / (ms / 1e3)}
+    nbytes = train_bytes(B, H, T, d)
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {"workload": name, "ms_per_step": ms, "tokens_per_s": B * T / (ms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "algorithmic_bytes": nbytes,
+                         "traffic": counter_traffic(name, source_digest(*TRAIN_SOURCES))}}
 
 
 if __name__ == "__main__":

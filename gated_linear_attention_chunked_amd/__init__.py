@@ -165,13 +165,17 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
     return out
 
 
-def hybrid_fwd_varlen(q, k, v, log_alpha, meta_k, meta_v, window, cu_seqlens, max_seqlen,
+def hybrid_fwd_varlen(q, k, v, log_alpha, meta_k, meta_v, window, cu_seqlens, max_seqlen=None,
                       scale=None, mix=1.0, h0=None, return_state=False, return_ring=False,
-                      q_w=None, k_w=None):
+                      q_w=None, k_w=None, check_lengths=True):
     """Hybrid forward over a packed batch: q, k, log_alpha (and q_w, k_w) [H, N, dk],
     v [H, N, dv]; sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (int32
-    device tensor [B+1]); max_seqlen bounds every length.  Returns a dict with "o"
-    [H, N, dv] and, on request, the per-sequence "hT" [B,H,dk,dv] and
+    device tensor [B+1]); max_seqlen bounds every length (None: taken from
+    cu_seqlens).  With check_lengths (the default) cu_seqlens is read back to the
+    host once and must start at 0, be non-decreasing, end at N and have no length
+    above max_seqlen, else ValueError; a caller that guarantees this may pass
+    check_lengths=False and a max_seqlen to avoid the read-back.  Returns a dict
+    with "o" [H, N, dv] and, on request, the per-sequence "hT" [B,H,dk,dv] and
     "ring_k"/"ring_v" [B,H,w,d]."""
     H, N, dk = q.shape
     dv = v.shape[-1]
@@ -181,6 +185,17 @@ def hybrid_fwd_varlen(q, k, v, log_alpha, meta_k, meta_v, window, cu_seqlens, ma
     _need(k, "k", (H, N, dk), dt)
     _need(v, "v", (H, N, dv), dt)
     _need(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32)
+    if check_lengths or max_seqlen is None:
+        cu = cu_seqlens.cpu().tolist()
+        lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+        longest = max(lens, default=0)
+        if check_lengths:
+            if cu[0] != 0 or cu[-1] != N or any(n < 0 for n in lens):
+                raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at N")
+            if max_seqlen is not None and longest > max_seqlen:
+                raise ValueError(f"a sequence of {longest} tokens exceeds max_seqlen={max_seqlen}")
+        if max_seqlen is None:
+            max_seqlen = max(longest, 1)
     _window_pair(q_w, k_w, (H, N, dk), dt)
     gate = _gate(log_alpha, "log_alpha", (H, N, dk))
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
@@ -266,7 +281,8 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, 
     _need(ring_v, "ring_v", (B, H, window, dv), dt)
     _need(pos, "pos", (B,), torch.int64)
     meta_k, meta_v, M = _meta_pair(meta_k, meta_v, H, dk, dv, dt)
-    o = torch.empty(B, H, dv, device=q.device, dtype=dt) if out is None else out
+    o = torch.empty(B, H, dv, device=q.device, dtype=dt) if out is None else _need(
+        out, "out", (B, H, dv), dt)
     d = make_desc(B, H, 0, dk, dv, window, M, scale, mix, dt, gate=gate)
     _abi.check("lizard_decode_step", lib().lizard_decode_step(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(state), _p(ring_k), _p(ring_v),

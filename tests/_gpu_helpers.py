@@ -1,4 +1,6 @@
 """Shared helpers for the GPU parity tests (oracle comparisons)."""
+import os
+
 import numpy as np
 import torch
 
@@ -8,9 +10,35 @@ from workloads import to_f64_numpy
 # max|gpu - oracle| / max|oracle| per output tensor.
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 
+# Elementwise companion metric: the 99.9th percentile over elements of
+# |gpu - oracle| / (|oracle| + 1e-3 max|oracle|).  The floor keeps it defined
+# near zero; unlike the normwise error it sees a wrong small-magnitude row
+# (early tokens, strongly decayed channels) even when the largest entries are
+# right.  It is reported for every output (when P999_LOG names a file, each
+# value is also appended there: test, output, normwise, p99.9) and held to a
+# bar per precision: fp32 1e-3, bf16 1.0 (99.9% of the elements within their
+# own magnitude plus the floor: bf16 outputs near cancellation keep the
+# absolute error of the large terms they were summed from).  The gate
+# gradient (d log alpha or d logit) is in bf16 problems a chunk sum of products
+# that cancel (q dq - k dk form), so its bar is 5.0.  Largest values seen over
+# the GPU suite: fp32 1.3e-4, bf16 0.50, bf16 gate gradient 2.8.
+P999_LOG = os.environ.get("P999_LOG")
+P999_BAR = {torch.float32: 1e-3, torch.bfloat16: 1.0}
+P999_GATE_GRAD_BAR = 5.0
+
+
+def _p999_bar(name, dtype):
+    if dtype == torch.bfloat16 and name.startswith(("dlog_alpha", "d gate_x")):
+        return P999_GATE_GRAD_BAR
+    return P999_BAR[dtype]
+
+
+def _host(gpu):
+    return gpu.detach().to("cpu", torch.float64).numpy() if torch.is_tensor(gpu) else np.asarray(gpu)
+
 
 def rel_err(gpu, ref):
-    g = gpu.detach().to("cpu", torch.float64).numpy() if torch.is_tensor(gpu) else np.asarray(gpu)
+    g = _host(gpu)
     ref = np.asarray(ref, dtype=np.float64)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     if not np.all(np.isfinite(g)):
@@ -18,11 +46,31 @@ def rel_err(gpu, ref):
     return float(np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
+def p999_err(gpu, ref):
+    g = _host(gpu)
+    ref = np.asarray(ref, dtype=np.float64)
+    if g.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    floor = 1e-3 * max(float(np.max(np.abs(ref))), 1e-30)
+    e = np.abs(g - ref) / (np.abs(ref) + floor)
+    return float(np.quantile(e.ravel(), 0.999))
+
+
 def assert_close(name, gpu, ref, dtype, tol=None):
     e = rel_err(gpu, ref)
+    p = p999_err(gpu, ref)
     bar = TOL[dtype] if tol is None else tol
-    print(f"  {name}: max-rel {e:.3e} (bar {bar:.0e})", flush=True)
+    print(f"  {name}: max-rel {e:.3e} (bar {bar:.0e}), p99.9 elementwise {p:.3e}", flush=True)
+    if P999_LOG:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+        with open(P999_LOG, "a") as f:
+            f.write(f"{test}\t{name}\t{'f32' if dtype == torch.float32 else 'bf16'}\t"
+                    f"{e:.3e}\t{p:.3e}\n")
     assert e <= bar, f"{name}: max-rel error {e:.3e} > {bar:.0e}"
+    pbar = 0.0 if tol == 0.0 else _p999_bar(name, dtype)
+    assert p <= pbar, f"{name}: 99.9th-percentile elementwise error {p:.3e} > {pbar:.0e}"
     return e
 
 

@@ -91,9 +91,14 @@ def test_decode_ragged_positions():
     assert torch.equal(g[3].cpu(), torch.tensor([1, 6, 101]))
 
 
-def test_full_size_decode_sampled_heads():
+def test_full_size_decode_workload_sampled_heads():
+    # the decode workload as defined: B=64 H=32 d=128 w=128 M=4, a 2048-token
+    # prefill, then all 1024 sequential steps; two sampled heads are compared
+    # with the oracle's 3072-token prefill (every step's output, the final state
+    # and the window cache), so state drift and ring wrap-around over the whole
+    # run are covered
     wl = WORKLOADS["decode_bf16_b64_h32_d128"]
-    prefill_then_decode(wl.B, wl.H, wl.T, 4, wl.dk, wl.window, wl.n_meta, wl.dtype,
+    prefill_then_decode(wl.B, wl.H, wl.T, wl.steps, wl.dk, wl.window, wl.n_meta, wl.dtype,
                         heads=[(0, 0), (63, 31)])
 
 

@@ -129,3 +129,35 @@ def test_serving_mix_workload_sampled():
     out = run(inp, 128, s, 1.0, max(lengths))
     longest = int(np.argmax(lengths))
     check_all(inp, out, 128, s, 1.0, seqs=[0, longest, 15], heads=[0, 17, 31])
+
+
+def test_binding_rejects_bad_lengths_and_out_buffers():
+    # a sequence longer than max_seqlen, and cu_seqlens that do not end at N, are
+    # refused before anything is enqueued; without max_seqlen the bound is taken
+    # from cu_seqlens
+    inp = make_packed_inputs([100, 300], 2, 64, 64, 2, dtype="bf16", seed=1)
+    x = to_dev(inp)
+    args = (x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"], 64)
+    with pytest.raises(ValueError, match="max_seqlen"):
+        lz.hybrid_fwd_varlen(*args, x["cu_seqlens"], 200)
+    bad = torch.tensor([0, 100, 399], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        lz.hybrid_fwd_varlen(*args, bad, 300)
+    a = lz.hybrid_fwd_varlen(*args, x["cu_seqlens"])
+    b = lz.hybrid_fwd_varlen(*args, x["cu_seqlens"], 300)
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"])
+    # decode_step's out buffer must match [B, H, dv] in the problem's dtype
+    B, H, d, w = 2, 2, 64, 8
+    st = torch.zeros(B, H, d, d, device="cuda")
+    rk = torch.zeros(B, H, w, d, device="cuda", dtype=BF)
+    rv = torch.zeros_like(rk)
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    dec = make_decode_inputs(1, B, H, d, d, dtype="bf16", seed=2)
+    t = [dec[n][0].cuda() for n in ("q", "k", "v", "log_alpha")]
+    for out in (torch.empty(B, H, d // 2, device="cuda", dtype=BF),
+                torch.empty(B, H, d, device="cuda", dtype=torch.float32)):
+        with pytest.raises(ValueError, match="out"):
+            lz.decode_step(*t, st, rk, rv, pos, None, None, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(pos.cpu(), torch.zeros(B, dtype=torch.int64))

@@ -56,7 +56,7 @@ def test_forward_separate_window_inputs(B, H, T, d, w, M, dtype):
         assert_close(f"{tag}.ring_k", out["ring_k"], ref["ring_k"], dt, tol=0.0)
         assert_close(f"{tag}.ring_v", out["ring_v"], ref["ring_v"], dt, tol=0.0)
     assert_close("saved.o_swa", sav["o_swa"], ref["o_swa"], dt)
-    assert_close("saved.lse", sav["lse"], ref["lse"], dt)
+    assert_close("saved.lse", sav["lse"], ref["lse"], dt, tol=1e-4)  # fp32 output
 
 
 @pytest.mark.parametrize("d", [64, 128])
