@@ -15,8 +15,10 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "lizard.h")
 LIZARD_F32, LIZARD_BF16 = 0, 1
 LIZARD_GATE_LOG_ALPHA, LIZARD_GATE_LOGIT = 0, 1
 OP_GLA_FWD, OP_SWA_FWD, OP_HYBRID_FWD, OP_HYBRID_BWD, OP_DECODE = range(5)
+STATIC_SCRATCH_BYTES = 17 << 20  # LIZARD_STATIC_SCRATCH_BYTES
 STATUS = {0: "LIZARD_OK", 1: "LIZARD_E_NULL", 2: "LIZARD_E_SHAPE", 3: "LIZARD_E_DTYPE",
-          4: "LIZARD_E_UNSUPPORTED", 5: "LIZARD_E_WORKSPACE", 6: "LIZARD_E_HIP"}
+          4: "LIZARD_E_UNSUPPORTED", 5: "LIZARD_E_WORKSPACE", 6: "LIZARD_E_HIP",
+          7: "LIZARD_E_SCRATCH"}
 
 
 class Desc(ctypes.Structure):
@@ -39,6 +41,7 @@ _SIGS = {
     "lizard_gla_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P, ctypes.c_size_t, P]),
     "lizard_swa_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 7 + [P]),
     "lizard_hybrid_fwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 15 + [P, ctypes.c_size_t, P]),
+    "lizard_hybrid_fwd_static": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 15 + [P]),
     "lizard_hybrid_fwd_varlen": (ctypes.c_int, [ctypes.POINTER(Desc), P, ctypes.c_int32]
                                  + [P] * 13 + [P, ctypes.c_size_t, P]),
     "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 23 + [P, ctypes.c_size_t, P]),

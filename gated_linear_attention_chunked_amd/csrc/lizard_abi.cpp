@@ -66,6 +66,7 @@ const char* lizard_status_str(lizard_status_t s) {
     case LIZARD_E_UNSUPPORTED: return "configuration not supported in this version";
     case LIZARD_E_WORKSPACE: return "workspace too small";
     case LIZARD_E_HIP: return "HIP launch failed";
+    case LIZARD_E_SCRATCH: return "problem needs more than the static scratch array holds";
   }
   return "unknown status";
 }
@@ -107,21 +108,38 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
                          nullptr, nullptr, stream));
 }
 
+}  // extern "C"
+
+namespace lz {
+// Host checks of lizard_hybrid_fwd other than the workspace's.
+lizard_status_t hybrid_fwd_args(const lizard_desc_t* desc, const void* q, const void* k,
+                                const void* v, const void* gate, const void* meta_k,
+                                const void* meta_v, const void* o, const void* ring_k,
+                                const void* ring_v, const void* q_w, const void* k_w) {
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (has_tokens(desc) && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
+  if ((q_w == nullptr) != (k_w == nullptr)) return LIZARD_E_NULL;
+  if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
+  if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
+  return LIZARD_OK;
+}
+}  // namespace lz
+
+extern "C" {
+
 lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, void* o, float* lse,
                                   void* o_swa, float* hT, void* ring_k, void* ring_v,
                                   const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
-  lizard_status_t st = check_desc(desc, true);
+  lizard_status_t st =
+      lz::hybrid_fwd_args(desc, q, k, v, gate, meta_k, meta_v, o, ring_k, ring_v, q_w, k_w);
   if (st != LIZARD_OK) return st;
-  if (has_tokens(desc) && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
-  if ((q_w == nullptr) != (k_w == nullptr)) return LIZARD_E_NULL;
   // the window branch's queries and keys (the same as the GLA branch's by default)
   const void* qw = q_w ? q_w : q;
   const void* kw = k_w ? k_w : k;
-  if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
-  if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
   const Shape s = to_shape(desc);
   const size_t need = lz::gla_fwd_workspace_bytes(s);
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;

@@ -68,7 +68,8 @@ typedef enum {
   LIZARD_E_DTYPE = 3,       /* unknown dtype code                                 */
   LIZARD_E_UNSUPPORTED = 4, /* valid but not built (e.g. dk = 96, F32 at dk = 128)  */
   LIZARD_E_WORKSPACE = 5,   /* ws_bytes smaller than lizard_workspace_bytes()     */
-  LIZARD_E_HIP = 6          /* a HIP launch or query failed                       */
+  LIZARD_E_HIP = 6,         /* a HIP launch or query failed                       */
+  LIZARD_E_SCRATCH = 7      /* needs more scratch than LIZARD_STATIC_SCRATCH_BYTES */
 } lizard_status_t;
 
 typedef enum { LIZARD_F32 = 0, LIZARD_BF16 = 1 } lizard_dtype_t;
@@ -208,6 +209,29 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
                                    void* ring_k, void* ring_v, int64_t* pos,
                                    const void* meta_k, const void* meta_v, const void* q_w,
                                    const void* k_w, void* o, hipStream_t stream);
+
+/* Size of the fixed per-device scratch array behind lizard_hybrid_fwd_static. */
+#define LIZARD_STATIC_SCRATCH_BYTES ((size_t)17 << 20)
+
+/* lizard_hybrid_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Arguments, outputs and errors are those of
+ * lizard_hybrid_fwd; the scratch memory is a fixed array of
+ * LIZARD_STATIC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends, so the call itself allocates and frees nothing.  A
+ * problem whose lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) exceeds that
+ * size returns LIZARD_E_SCRATCH (no shape this version accepts does).  The array
+ * of the current device (hipGetDevice) is used; its device address is looked up
+ * on the first call on each device (LIZARD_E_HIP if that fails).  All calls on
+ * one device share the array and nothing in it carries over between calls (no
+ * part of it must start at zero), but two such calls that overlap in time on one
+ * device, on different streams or threads, race on it: serialise them. */
+lizard_status_t lizard_hybrid_fwd_static(const lizard_desc_t* desc, const void* q, const void* k,
+                                         const void* v, const void* gate, const void* meta_k,
+                                         const void* meta_v, const float* h0, void* o,
+                                         float* lse, void* o_swa, float* hT, void* ring_k,
+                                         void* ring_v, const void* q_w, const void* k_w,
+                                         hipStream_t stream);
 
 /* Static description of a status code. */
 const char* lizard_status_str(lizard_status_t status);

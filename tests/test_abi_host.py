@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = _abi.lib()
-    for code in range(7):
+    for code in range(8):
         assert lib.lizard_status_str(code)
     assert lib.lizard_status_str(99) == b"unknown status"
     assert lib.lizard_version() == 10100
@@ -163,3 +163,22 @@ def test_backward_workspace_and_support():
         d2 = desc(**kw)
         assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
         assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 23), FAKE, 1 << 30, None) == 4
+
+
+def test_static_scratch_entry_checks_arguments_first():
+    # the allocation-free forward runs lizard_hybrid_fwd's checks before any HIP
+    # call (here: no GPU at all), and declares the size of its fixed array
+    lib = _abi.lib()
+    with open(_abi.HEADER) as f:
+        assert "#define LIZARD_STATIC_SCRATCH_BYTES ((size_t)17 << 20)" in f.read()
+    assert _abi.STATIC_SCRATCH_BYTES == 17 << 20
+    call = lambda dd, *p: lib.lizard_hybrid_fwd_static(dd, *p, None)
+    assert call(None, *([FAKE] * 15)) == 1
+    assert call(ctypes.byref(desc(dk=96, dv=96)), *([FAKE] * 15)) == 4
+    assert call(ctypes.byref(desc(dtype=7)), *([FAKE] * 15)) == 3
+    assert call(ctypes.byref(desc()), FAKE, None, *([FAKE] * 13)) == 1
+    assert call(ctypes.byref(desc(B=0, n_meta=0)), *([None] * 15)) == 0
+    # the largest forward workspace of any accepted shape fits the array
+    worst = max(lib.lizard_workspace_bytes(ctypes.byref(desc(B=1, H=h, T=65536, dk=128, dv=128)), 2)
+                for h in range(1, 300))
+    assert 0 < worst <= _abi.STATIC_SCRATCH_BYTES
