@@ -229,6 +229,9 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* k, const voi
     return launch_decode_typed<bf16, 64, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
                                                  pos, mk, mv, o, st);
   }
+  if (s.dk == 128)
+    return launch_decode_typed<float, 128, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v,
+                                                  pos, mk, mv, o, st);
   return launch_decode_typed<float, 64, float>(s, q, k, qw, kw, v, la, state, ring_k, ring_v, pos,
                                                mk, mv, o, st);
 }

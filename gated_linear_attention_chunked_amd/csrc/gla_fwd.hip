@@ -64,16 +64,20 @@ Plan make_plan(const Shape& s) {
 
 template <typename T, int DK>
 struct OutSmem {
-  static constexpr int DKP = DK + 8;
-  static constexpr int CP = kC + 8;
-  T qg[kC][DKP];     // q_t 2^{b_t - R_i}
-  T kg[kC][DKP];     // k_s 2^{R_j - b_s}
-  T qh[kC][DKP];     // q_t 2^{b_t}
+  // fp32 at DK = 128 keeps its tiles within the 160 KiB of LDS with less row
+  // padding (some fragment reads of khT / vT then share banks)
+  static constexpr bool kTight = sizeof(T) == 4 && DK == 128;
+  static constexpr int DKP = DK + (kTight ? 4 : 8);
+  static constexpr int CP = kC + (kTight ? 0 : 8);
+  static constexpr int AP = kC + (kTight ? 4 : 8);
+  T qg[kC][DKP];     // single reference: q_t 2^{b_t}; sub-blocks: q_t 2^{b_t - R_i}
+  T kg[kC][DKP];     // k_s 2^{R_j - b_s} (R = 0 with a single reference)
   T khT[DK][CP];     // (k_s 2^{b_last - b_s})^T
   T vT[DK][CP];      // v^T
-  T a[kC][CP];       // masked intra scores A[t][s]
+  T a[kC][AP];       // masked intra scores A[t][s]
   float tot[8][DK];  // per-8-row-group sums of log2 gates
   float vij[6][DK];  // 2^{R_i - R_j} for the off-diagonal pairs
+  alignas(16) float eR[4][DK];  // 2^{R_i} (sub-block references; unused with a single one)
   alignas(16) float decay[DK];  // 2^{b_last}
 };
 
@@ -356,11 +360,11 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int t = 8 * rg + rr;
-        st_pair<T>(&sm.qh[t][2 * cp], qhv[rr][0], qhv[rr][1]);
+        st_pair<T>(&sm.qg[t][2 * cp], qhv[rr][0], qhv[rr][1]);
         st_pair<T>(&sm.kg[t][2 * cp], kiv[rr][0], kiv[rr][1]);
       }
     } else {
-      float qgv[8][2], kgv[8][2], qhv[8][2];
+      float qgv[8][2], kgv[8][2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int c = 2 * cp + x;
@@ -372,7 +376,6 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
           const float d = b[rr][x] + pre[x] - Ri[x];
           qgv[rr][x] = unpack2(qq[rr], T())[x] * exp2_fast(d);
           kgv[rr][x] = unpack2(kk[rr], T())[x] * exp2_fast(-d);
-          qhv[rr][x] = qgv[rr][x] * eRi;
           kh[rr] = kgv[rr][x] * eKh;
           vc[rr] = unpack2(vv[rr], T())[x];
         }
@@ -383,13 +386,13 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
         } else if (rg == 7) {
           sm.decay[c] = exp2_fast(blast[x]);
         }
+        if ((rg & 1) == 0) sm.eR[i_sub][c] = eRi;
       }
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int t = 8 * rg + rr;
         st_pair<T>(&sm.qg[t][2 * cp], qgv[rr][0], qgv[rr][1]);
         st_pair<T>(&sm.kg[t][2 * cp], kgv[rr][0], kgv[rr][1]);
-        st_pair<T>(&sm.qh[t][2 * cp], qhv[rr][0], qhv[rr][1]);
       }
     }
     lds_barrier();  // (B) operands ready
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     // All fragments of a phase are read before its first product so that the
     // LDS latency is paid once per phase, not once per product.
     {
-      const T* qsrc = fast ? &sm.qh[0][0] : &sm.qg[0][0];
+      const T* qsrc = &sm.qg[0][0];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const int blk = wave + n * NW;
@@ -431,26 +434,35 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     // phases are kept apart so that each one's fragments are not live at once
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- inter: O^T[n][t] = sum_c S[c][n] qh[t][c], with the state entering the chunk
+    // ---- inter: O^T[n][t] = sum_c S[c][n] 2^{R_i}[c] qg[t][c] (query block i of t;
+    // 2^{R_i} = 1 with a single reference), with the state entering the chunk
     f32x4 O[4];
     {
-      F qf[4][KS];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-        for (int p = 0; p < KS; ++p) qf[qb][p] = ld4x2<T>(&sm.qh[16 * qb + r16][32 * p + 4 * g]);
       F sf[KS];
 #pragma unroll
       for (int p = 0; p < KS; ++p) sf[p] = pack_acc<T>(S[2 * p], S[2 * p + 1]);
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
+        F qf[KS], sfs[KS];
+#pragma unroll
+        for (int p = 0; p < KS; ++p) {
+          qf[p] = ld4x2<T>(&sm.qg[16 * qb + r16][32 * p + 4 * g]);
+          sfs[p] = sf[p];
+          if (!fast) {
+            // fragment element e holds channel 32p + 4g + e (e < 4) or 32p + 12 + 4g + e
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm.eR[qb][32 * p + 4 * g]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&sm.eR[qb][32 * p + 16 + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sfs[p][e] = to_t<T>(to_f(sf[p][e]) * lo[e]);
+              sfs[p][e + 4] = to_t<T>(to_f(sf[p][e + 4]) * hi[e]);
+            }
+          }
+        }
         O[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < KS; ++p) mma(O[qb], sf[p], qf[qb][p]);
+        for (int p = 0; p < KS; ++p) mma(O[qb], sfs[p], qf[p]);
       }
-      // issue order: every LDS read of the phase, then the products
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS * (sizeof(T) == 2 ? 1 : 8), 0);
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -459,23 +471,15 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     F vf[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) vf[p] = ld8<T>(&sm.vT[ncol + r16][32 * p + 8 * g]);
-    {
-      F kf[NCB][2];
-      f32x4 dec[NCB];
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        dec[cb] = *reinterpret_cast<const f32x4*>(&sm.decay[16 * cb + 4 * g]);
+    for (int cb = 0; cb < NCB; ++cb) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(&sm.decay[16 * cb + 4 * g]);
+      F kf[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) kf[cb][p] = ld8<T>(&sm.khT[16 * cb + r16][32 * p + 8 * g]);
-      }
+      for (int p = 0; p < 2; ++p) kf[p] = ld8<T>(&sm.khT[16 * cb + r16][32 * p + 8 * g]);
+      S[cb] *= dec;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        S[cb] *= dec[cb];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) mma(S[cb], kf[cb][p], vf[p]);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 3 * NCB + 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCB * (sizeof(T) == 2 ? 1 : 8), 0);
+      for (int p = 0; p < 2; ++p) mma(S[cb], kf[p], vf[p]);
     }
     lds_barrier();  // (C) scores ready
 
@@ -1057,6 +1061,7 @@ hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const vo
     if (s.dk == 128) return launch_typed<bf16, 128, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
     return launch_typed<bf16, 64, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
   }
+  if (s.dk == 128) return launch_typed<float, 128, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
   return launch_typed<float, 64, float>(s, pl, q, k, v, la, h0, o, hT, ws, st);
 }
 

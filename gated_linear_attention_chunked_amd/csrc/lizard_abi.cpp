@@ -23,7 +23,6 @@ lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
   if (d->chunk != 64) return LIZARD_E_UNSUPPORTED;
   if (d->dk != d->dv) return LIZARD_E_UNSUPPORTED;
   if (d->dk != 64 && d->dk != 128) return LIZARD_E_UNSUPPORTED;
-  if (d->dtype == LIZARD_F32 && d->dk != 64) return LIZARD_E_UNSUPPORTED;
   if (d->gate == LIZARD_GATE_LOGIT && d->dtype != LIZARD_BF16) return LIZARD_E_UNSUPPORTED;
   if (d->n_meta > 16) return LIZARD_E_UNSUPPORTED;
   const long long bh = (long long)d->B * d->H;

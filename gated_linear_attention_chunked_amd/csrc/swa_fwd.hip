@@ -528,6 +528,10 @@ template <typename T, int D>
 hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v,
                         const void* mk, const void* mv, void* o, float out_scale, int acc,
                         void* o_swa, float* lse, void* rk, void* rv, hipStream_t st) {
+  // the streaming ring holds up to four 64-key chunks of K and V^T: too large
+  // for LDS in fp32 at D = 128, which takes the tiled kernel for every window
+  constexpr bool kRing = !(sizeof(T) == 4 && D == 128);
+  if constexpr (kRing) {
   if (s.window <= 2 * kKT + 1) {
     // streaming form: runs of query tiles, enough work-groups to fill the chip
     const int nc = (s.T + kKT - 1) / kKT;
@@ -550,6 +554,7 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
                          s.cu, s.n_tokens);
     }
     return hipGetLastError();
+  }
   }
   dim3 grid((s.T + kQT - 1) / kQT, s.B * s.H);
   hipLaunchKernelGGL((swa_fwd_kernel<T, D, D>), grid, dim3(256), 0, st, (const T*)q, (const T*)k,
@@ -575,6 +580,9 @@ hipError_t launch_swa_fwd(const Shape& s, const void* q, const void* k, const vo
     return launch_typed<bf16, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
                                   ring_k, ring_v, st);
   }
+  if (s.dk == 128)
+    return launch_typed<float, 128>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
+                                    ring_k, ring_v, st);
   return launch_typed<float, 64>(s, q, k, v, mk, mv, o, out_scale, accumulate, o_swa, lse,
                                  ring_k, ring_v, st);
 }

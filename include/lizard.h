@@ -47,8 +47,8 @@
  *     returns LIZARD_E_HIP.  NaN/Inf inputs propagate to the outputs.
  *   - Supported in this version: dk == dv, dk in {64, 128}, chunk == 64,
  *     window >= 1, 0 <= M <= 16, T >= 0 with T*dk*4 < 2^31, B*H <= 65535;
- *     dtype BF16 for dk in {64, 128}, F32 for dk == 64.  Output gradients dq, dk, dv use desc->dtype; every
- *     other output is float32.
+ *     dtype BF16 or F32 for dk in {64, 128}.  Output gradients dq, dk, dv use
+ *     desc->dtype; every other output is float32.
  */
 #ifndef LIZARD_H
 #define LIZARD_H
@@ -66,7 +66,7 @@ typedef enum {
   LIZARD_E_NULL = 1,        /* a required pointer is NULL                         */
   LIZARD_E_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
   LIZARD_E_DTYPE = 3,       /* unknown dtype code                                 */
-  LIZARD_E_UNSUPPORTED = 4, /* valid but not built (e.g. dk = 96, F32 at dk = 128)  */
+  LIZARD_E_UNSUPPORTED = 4, /* valid but not built (e.g. dk = 96)                   */
   LIZARD_E_WORKSPACE = 5,   /* ws_bytes smaller than lizard_workspace_bytes()     */
   LIZARD_E_HIP = 6,         /* a HIP launch or query failed                       */
   LIZARD_E_SCRATCH = 7      /* needs more scratch than LIZARD_STATIC_SCRATCH_BYTES */

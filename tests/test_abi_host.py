@@ -65,7 +65,7 @@ def test_status_strings_and_version():
     (dict(B=-1), 2), (dict(T=-5), 2), (dict(dk=0), 2), (dict(window=0), 2), (dict(n_meta=-1), 2),
     (dict(chunk=0), 2), (dict(scale=float("nan")), 2), (dict(mix=float("inf")), 2),
     (dict(chunk=32), 4), (dict(dk=96, dv=96), 4), (dict(dk=64, dv=128), 4),
-    (dict(dk=128, dv=128, dtype=_abi.LIZARD_F32), 4), (dict(n_meta=17), 4),
+    (dict(n_meta=17), 4),
     (dict(B=300, H=300), 4),
 ])
 def test_bad_descriptor_is_rejected_before_launch(kw, status):

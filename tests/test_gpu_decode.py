@@ -56,7 +56,7 @@ def prefill_then_decode(B, H, T0, n, d, w, M, dtype, mix=1.0, heads=None, seed=0
         assert_close(f"ring_v[b{b},h{h}]", sl(rv), ref["ring_v"], dt, tol=0.0)
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 def test_decode_matches_longer_prefill(dtype, d):
     prefill_then_decode(2, 2, 40, 20, d, 16, 4, dtype, mix=0.8)
 

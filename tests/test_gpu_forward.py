@@ -91,6 +91,20 @@ def test_fp32_ragged_lengths(T):
     run_and_check(1, 2, T, 64, 64, 4, "f32", seed=T)
 
 
+@pytest.mark.parametrize("T,w,M", [(1, 64, 4), (63, 128, 0), (130, 129, 16), (300, 64, 4),
+                                   (333, 200, 3), (1100, 128, 4)])
+def test_fp32_d128(T, w, M):
+    # fp32 at d = 128: the fp32 output pass with its tighter LDS layout and the
+    # tiled window kernel for every window
+    run_and_check(1, 2, T, 128, w, M, "f32", seed=T + w, h0=True, mix=0.6)
+
+
+def test_fp32_d128_gate_ranges():
+    run_and_check(1, 2, 300, 128, 64, 4, "f32", gate_mean=-3.0)
+    run_and_check(2, 1, 700, 128, 128, 4, "f32", steep_chunks=True, h0=True)
+    run_and_check(1, 2, 200, 128, 32, 2, "f32", zero_gate=True)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T,w,M", [(300, 128, 4), (200, 1, 0), (129, 7, 16), (70, 500, 0),
                                    (257, 64, 3), (400, 65, 4), (400, 129, 4), (400, 130, 2)])
