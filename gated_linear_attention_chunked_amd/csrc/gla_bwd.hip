@@ -20,9 +20,12 @@
 // where "intra,s<t" leaves out the diagonal pair s = t (it cancels exactly and
 // is never formed).
 //
-// Kernels:
+// Kernels (bf16, d = 64), run per block of chunks c0..c1-1 (the caller walks a
+// sequence block by block, last block first, so the chunk states of one block
+// at a time are held):
 //   1. scans (one launch): per head, the state scan forward writes S_c for every
-//      chunk and the reverse scan writes dS_{c+1}
+//      chunk of the block from the state entering it, and the reverse scan
+//      writes dS_{c+1} from the gradient leaving it
 //   2. per chunk: dq, dk, dv and dlog_alpha from the chunk's inputs and the two
 //      states of its boundaries
 // Intra-chunk factors use 16-token sub-block midpoints R_i as references.
@@ -79,12 +82,17 @@ __device__ __forceinline__ float wave_scan64(float x) {
   return x;
 }
 
+// Chunks c0..c1-1 only: the forward scan starts from fstart (per-head stride
+// fstride floats; null = zero), the reverse scan from rstart (null = zero) and
+// leaves the gradient entering chunk c0 in rend (null = not stored); chunk c's
+// states go to slot c - c0 of the L per head.
 template <typename GT>
 __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const GT* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ h0,
-    const float* __restrict__ dhT, float* __restrict__ dh0, bf16* __restrict__ S_all,
-    bf16* __restrict__ dS_all, int BH, int T_len) {
+    const GT* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ fstart,
+    size_t fstride, const float* __restrict__ rstart, float* __restrict__ rend,
+    bf16* __restrict__ S_all, bf16* __restrict__ dS_all, int BH, int T_len, int c0, int c1,
+    int L) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4, odd = lane & 1;
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
   const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb),
       bla(la + off, nb / 2 * (u32)sizeof(GT));
-  const int nc = (T_len + kC - 1) / kC;
+  const int nc = c1 - c0;                 // chunks of this block
   const int cw = 16 * w;                  // this wave's first channel
   const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
 
@@ -102,11 +110,13 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   f32x4 a1[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the forward scan starts from h0, the reverse scan from dhT (the gradient of
-  // the final state), both [c][j] row-major; absent ones are zero
-  const float* start = rev ? dhT : h0;
+  // the forward scan starts from fstart (h0 or the block's entry state), the
+  // reverse scan from rstart (dhT, the gradient of the final state, or the
+  // gradient leaving the block), all [c][j] row-major; absent ones are zero
+  const float* start = rev ? rstart : fstart;
   if (start) {
-    const float* hp = start + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
+    const float* hp = start + (size_t)bh * (rev ? (size_t)kD * kD : fstride) +
+                      (size_t)(cw + r16) * kD + 4 * g;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) a1[jb] = *reinterpret_cast<const f32x4*>(hp + 16 * jb);
   }
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
       *reinterpret_cast<u32*>(&dstT[swz64(c + 1, te)]) = hi2(fst, snd);
     }
   };
-  auto chunk_at = [&](int n) { return rev ? nc - 1 - n : n; };
+  auto chunk_at = [&](int n) { return rev ? c1 - 1 - n : c0 + n; };
   auto step = [&](In& d, int n) {
     const int ch = chunk_at(n), buf = n & 1;
     // gate cumsum over the chunk, per channel
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     // (all words packed before the first store, so no store's data register is
     // rewritten while earlier stores are in flight)
     {
-      const size_t so = ((size_t)bh * nc + ch) * kTile;
+      const size_t so = ((size_t)bh * L + (ch - c0)) * kTile;
       bf16* dst = (rev ? dS_all : S_all) + so;
       u32x2 w1[4];
 #pragma unroll
@@ -206,9 +216,9 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     step(A, n);
     if (n + 1 < nc) step(B, n + 1);
   }
-  // after chunk 0 the reverse scan holds dS_0, the gradient of the initial state
-  if (rev && dh0) {
-    float* hp = dh0 + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
+  // after chunk c0 the reverse scan holds dS_{c0}, the gradient entering the block
+  if (rev && rend) {
+    float* hp = rend + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) *reinterpret_cast<f32x4*>(hp + 16 * jb) = a1[jb];
   }
@@ -253,17 +263,18 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const GT* __restrict__ la, const bf16* __restrict__ dO, const bf16* __restrict__ S_all,
     const bf16* __restrict__ dS_all, bf16* __restrict__ dq,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dla, int T_len) {
+    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dla, int T_len, int c0,
+    int L) {
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int ch = blockIdx.x, bh = blockIdx.y;
-  const int nc = gridDim.x, t0 = ch * kC;
+  const int ch = c0 + blockIdx.x, bh = blockIdx.y;
+  const int t0 = ch * kC;
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
   const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
   const Buf bla(la + off, nb / 2 * (u32)sizeof(GT));
-  const size_t soff = ((size_t)bh * nc + ch) * kTile;
+  const size_t soff = ((size_t)bh * L + blockIdx.x) * kTile;
   const u32 sb = (u32)(kTile * sizeof(bf16));
   const Buf bS(S_all + soff, sb), bdS(dS_all + soff, sb);
   const int t = 16 * w + r16;
@@ -679,51 +690,24 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
 
 }  // namespace
 
-size_t gla_bwd_workspace_bytes(const Shape& s) {
-  const size_t nc = (size_t)(s.T + kC - 1) / kC;
-  const size_t bh = (size_t)s.B * s.H;
-  return 2 * bh * nc * kD * kD * sizeof(bf16);
-}
-
-// Scans: S_c and dS_{c+1} for every chunk, into ws.
-hipError_t launch_gla_bwd_scans(const Shape& s, const void* q, const void* k, const void* v,
-                                const void* la, const float* h0, const float* dhT, float* dh0,
-                                const void* dO, void* ws, hipStream_t st) {
+// Chunks c0..c1-1 of every head (bf16, d = 64): both scans, then the
+// per-chunk gradients (see launch_gla_bwd_block_gen for the arguments).
+hipError_t launch_gla_bwd_block(const Shape& s, const void* q, const void* k, const void* v,
+                                const void* la, const void* dO, const float* fstart,
+                                size_t fstride, const float* rstart, float* rend, void* dq,
+                                void* dk, void* dv, float* dla, void* S_ws, void* dS_ws,
+                                bool add_qk, int c0, int c1, int L, hipStream_t st) {
   typedef bf16 T;
-  const int nc = (s.T + kC - 1) / kC;
   const int BH = s.B * s.H;
-  if (nc == 0 || BH == 0) return hipSuccess;
-  T* S_all = (T*)ws;
-  T* dS_all = S_all + (size_t)BH * nc * kD * kD;
-  if (s.gate == 1)
-    hipLaunchKernelGGL(gla_bwd_scans<bf16>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, (const bf16*)la, (const T*)dO, h0, dhT, dh0,
-                       S_all, dS_all, BH, s.T);
-  else
-    hipLaunchKernelGGL(gla_bwd_scans<float>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, (const float*)la, (const T*)dO, h0, dhT, dh0,
-                       S_all, dS_all, BH, s.T);
-  return hipGetLastError();
-}
-
-// Per-chunk gradients from the scans' states; adds into dv, and into dq, dk
-// when add_qk (else writes them).
-hipError_t launch_gla_bwd_grads(const Shape& s, const void* q, const void* k, const void* v,
-                                const void* la, const void* dO, void* dq, void* dk, void* dv,
-                                float* dla, const void* ws, bool add_qk, hipStream_t st) {
-  typedef bf16 T;
-  const int nc = (s.T + kC - 1) / kC;
-  const int BH = s.B * s.H;
-  if (nc == 0 || BH == 0) return hipSuccess;
-  const T* S_all = (const T*)ws;
-  const T* dS_all = S_all + (size_t)BH * nc * kD * kD;
   auto go = [&](auto gate_type) {
     typedef decltype(gate_type) GT;
+    hipLaunchKernelGGL(gla_bwd_scans<GT>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
+                       (const T*)k, (const T*)v, (const GT*)la, (const T*)dO, fstart, fstride,
+                       rstart, rend, (T*)S_ws, (T*)dS_ws, BH, s.T, c0, c1, L);
     auto kern = add_qk ? gla_bwd_chunk<true, GT> : gla_bwd_chunk<false, GT>;
-    hipLaunchKernelGGL(kern, dim3(nc, BH),
-                       dim3(kThreads), 0, st, (const T*)q, (const T*)k, (const T*)v,
-                       (const GT*)la, (const T*)dO, S_all, dS_all, (T*)dq, (T*)dk, (T*)dv, dla,
-                       s.T);
+    hipLaunchKernelGGL(kern, dim3(c1 - c0, BH), dim3(kThreads), 0, st, (const T*)q, (const T*)k,
+                       (const T*)v, (const GT*)la, (const T*)dO, (const T*)S_ws,
+                       (const T*)dS_ws, (T*)dq, (T*)dk, (T*)dv, dla, s.T, c0, L);
   };
   if (s.gate == 1)
     go(bf16());

@@ -154,7 +154,7 @@ template <typename T, int DK, typename GT>
 __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
     const T* __restrict__ k, const T* __restrict__ v, const GT* __restrict__ la,
     float* __restrict__ ws_state, float* __restrict__ ws_gamma, int T_arg, int cps, int G,
-    const int* __restrict__ cu, int N, int H) {
+    const int* __restrict__ cu, int N, int H, int region_rows = 0) {
   constexpr int NCB = DK / 16;
   typedef typename Frag<T>::type F;
   __shared__ StateSmem<T, DK> sm;
@@ -227,13 +227,18 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
     }
   }
   // stored column-major ([value column][key row]) so that the output pass reads
-  // four consecutive rows of one column as one 16-byte load
-  float* dst = ws_state + ((size_t)bh * (G - 1) + seg) * DK * DK;
+  // four consecutive rows of one column as one 16-byte load.  With region_rows
+  // > 0 (checkpoints of the backward) segment seg's state and decay go to the
+  // start of its own token rows of ws_state instead ([B*H, T, DK] floats; the
+  // segment's region_rows rows hold DK*DK + DK floats).
+  float* dst = region_rows > 0
+                   ? ws_state + ((size_t)bh * T_len + (size_t)seg * region_rows) * DK
+                   : ws_state + ((size_t)bh * (G - 1) + seg) * DK * DK;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
     *reinterpret_cast<f32x4*>(&dst[(16 * wave + r16) * DK + 16 * cb + 4 * g]) = S[cb];
   if (rg == 0) {
-    float* gd = ws_gamma + ((size_t)bh * (G - 1) + seg) * DK;
+    float* gd = region_rows > 0 ? dst + DK * DK : ws_gamma + ((size_t)bh * (G - 1) + seg) * DK;
     gd[2 * cp] = gsum[0];
     gd[2 * cp + 1] = gsum[1];
   }
@@ -982,6 +987,34 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
   }
 }
 
+// Backward checkpoints: the state entering each block b >= 1 of a head,
+//   S_in(b) = diag(2^{Gamma(b-1)}) S_in(b-1) + S_loc(b-1),  S_in(0) = h0 or 0,
+// from the local end states and log2 decays that the state pass left at the
+// start of each block's rows; S_in(b) is written row-major ([c][j]) right after
+// them (rows of block b-1, offset DK*DK + DK).
+template <int DK>
+__global__ __launch_bounds__(256) void gla_checkpoint_compose(const float* __restrict__ h0,
+                                                              float* __restrict__ region,
+                                                              int T_len, int nb, int rows) {
+  constexpr int PER = DK * DK / 256;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* base = region + (size_t)bh * T_len * DK;
+  float S[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) S[i] = h0 ? h0[(size_t)bh * DK * DK + tid + 256 * i] : 0.f;
+  for (int b = 1; b < nb; ++b) {
+    float* prev = base + (size_t)(b - 1) * rows * DK;
+    const float* gam = prev + DK * DK;
+    float* out = prev + DK * DK + DK;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i, c = e / DK, j = e % DK;
+      S[i] = exp2_fast(gam[c]) * S[i] + prev[j * DK + c];
+      out[e] = S[i];
+    }
+  }
+}
+
 __global__ void state_copy_kernel(const float* __restrict__ h0, float* __restrict__ hT, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) hT[i] = h0 ? h0[i] : 0.f;
@@ -1015,6 +1048,41 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
 }
 
 }  // namespace
+
+namespace {
+template <typename T, int DK, typename GT>
+void launch_checkpoints_typed(const Shape& s, const void* k, const void* v, const void* la,
+                              const float* h0, float* region, int cps, int nb, hipStream_t st) {
+  const int BH = s.B * s.H;
+  hipLaunchKernelGGL((gla_state_pass<T, DK, GT>), dim3(nb - 1, BH), dim3(4 * DK), 0, st,
+                     (const T*)k, (const T*)v, (const GT*)la, region, region, s.T, cps, nb,
+                     (const int*)nullptr, 0, s.H, cps * kC);
+  hipLaunchKernelGGL(gla_checkpoint_compose<DK>, dim3(BH), dim3(256), 0, st, h0, region, s.T, nb,
+                     cps * kC);
+}
+}  // namespace
+
+// States entering blocks 1..nb-1 of cps chunks (see gla_checkpoint_compose):
+// region is [B*H, T, dk] floats, block b >= 1's entry state at rows
+// (b-1)*cps*64 + offset dk*dk + dk, row-major.
+hipError_t launch_gla_checkpoints(const Shape& s, const void* k, const void* v, const void* la,
+                                  const float* h0, float* region, int cps, int nb,
+                                  hipStream_t st) {
+  if (nb < 2 || s.B * s.H == 0) return hipSuccess;
+  if (s.dtype == 1) {
+    if (s.gate == 1) {
+      if (s.dk == 128) launch_checkpoints_typed<bf16, 128, bf16>(s, k, v, la, h0, region, cps, nb, st);
+      else launch_checkpoints_typed<bf16, 64, bf16>(s, k, v, la, h0, region, cps, nb, st);
+    } else {
+      if (s.dk == 128) launch_checkpoints_typed<bf16, 128, float>(s, k, v, la, h0, region, cps, nb, st);
+      else launch_checkpoints_typed<bf16, 64, float>(s, k, v, la, h0, region, cps, nb, st);
+    }
+  } else {
+    if (s.dk == 128) launch_checkpoints_typed<float, 128, float>(s, k, v, la, h0, region, cps, nb, st);
+    else launch_checkpoints_typed<float, 64, float>(s, k, v, la, h0, region, cps, nb, st);
+  }
+  return hipGetLastError();
+}
 
 size_t gla_fwd_workspace_bytes(const Shape& s) {
   const Plan pl = make_plan(s);

@@ -65,8 +65,8 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* k, const voi
                          void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
                          void* o, hipStream_t st);
 
-// Backward (bf16, dk = dv = 64 in this version).  Workspace layout is owned by
-// gla_bwd / swa_bwd; it grows with T (two states per chunk).  qw, kw, dqw, dkw:
+// Backward (bf16 at dk = dv = 64 or 128, fp32 at 64).  The workspace (owned by
+// hybrid_bwd, gla_bwd and swa_bwd) does not depend on T.  qw, kw, dqw, dkw:
 // separate window queries and keys and their gradients (all null: shared).
 bool bwd_supported(const Shape& s);
 size_t bwd_workspace_bytes(const Shape& s);

@@ -10,14 +10,16 @@
 // tile, so nothing of size T x T is ever formed.
 //
 // Kernels (deterministic, no float atomics):
-//   0. w <= 65: one streaming pass per (head, segment) for dq, dk, dv and the
-//      segment's meta-gradient partial sums
-//   otherwise
-//   1. dq   per (head, 64-query tile): D_t, dq, and the tile's meta-gradient
-//           partial sums
+//   0. bf16, d = 64, w <= 65: one streaming pass per (head, segment) for dq,
+//      dk, dv and the segment's meta-gradient partial sums
+//   otherwise (bf16 or fp32, d = 64 or 128)
+//   1. dq   per (head, segment of 64-query tiles): D_t, dq, and the segment's
+//           meta-gradient partial sums
 //   2. dkdv per (head, 64-key tile):   dk, dv
 // This branch runs first and writes dq, dk, dv; the GLA branch adds to them.
-//   3. meta reduction per head over (batch, tile) in a fixed order
+//   3. meta reduction per head over (batch, segment) in a fixed order
+// Segments, not tiles, carry the meta partials, so the scratch memory does not
+// grow with T; D_t goes to caller memory that is overwritten afterwards.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,212 +29,231 @@ namespace lz {
 namespace {
 
 constexpr int kT = 64;       // tile (queries or keys)
-constexpr int kD = 64;       // head size supported by the backward
-constexpr int kDP = kD + 8;
-constexpr int kTP = kT + 8;
+constexpr int kD = 64;       // head size of the streaming kernel
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------- 1. dq
-template <typename T>
+// One work-group per (head, segment of whole 64-query tiles), walking its
+// tiles in order; D = 64 or 128 channels, T = bf16 or float.  Per tile: the
+// tile's D_t (kept for the dk/dv kernel in Dws), the meta-slot terms of dq and
+// of the meta gradients (summed over the segment's tiles in LDS), then dq over
+// the key tiles that the window reaches.
+template <typename T, int D>
+struct DqSmem {
+  static constexpr int DP = D + 8, TP = kT + 8;
+  T skt[kT][DP];   // key tile, row-major
+  T svt[kT][DP];   // value tile, row-major
+  T skT[D][TP];    // key tile, transposed
+  T smk[16][DP];
+  T smv[16][DP];
+  T smkT[D][40];   // meta keys transposed (slots 16..31 zero)
+  T sqT[D][TP];    // this tile's queries, transposed
+  T sdoT[D][TP];   // this tile's dO, transposed
+  float slse[kT], sD[kT];
+  float red[2 * D][17];  // meta-gradient sums of the segment: [c or D + j][slot]
+};
+
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ mk, const T* __restrict__ mv, const T* __restrict__ o_swa,
     const float* __restrict__ lse, const T* __restrict__ dO, T* __restrict__ dq,
     float* __restrict__ Dws, float* __restrict__ metap, int T_len, int H, int W, int M,
-    float scale, float mix) {
+    float scale, float mix, int per) {
+  constexpr int KP = D / 32, NCT = D / 16;
+  constexpr int DP = DqSmem<T, D>::DP, TP = DqSmem<T, D>::TP;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T skt[kT][kDP];   // key tile, row-major
-  __shared__ __attribute__((aligned(16))) T svt[kT][kDP];   // value tile, row-major
-  __shared__ __attribute__((aligned(16))) T skT[kD][kTP];   // key tile, transposed
-  __shared__ __attribute__((aligned(16))) T smk[16][kDP];
-  __shared__ __attribute__((aligned(16))) T smv[16][kDP];
-  __shared__ __attribute__((aligned(16))) T smkT[kD][40];   // meta keys transposed (slots 16..31 zero)
-  __shared__ __attribute__((aligned(16))) T sqT[kD][kTP];   // this tile's queries, transposed
-  __shared__ __attribute__((aligned(16))) T sdoT[kD][kTP];  // this tile's dO, transposed
-  __shared__ __attribute__((aligned(16))) float slse[kT], sD[kT];
-  __shared__ __attribute__((aligned(16))) float red[kD * 2][17];
+  __shared__ __attribute__((aligned(16))) DqSmem<T, D> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
-  const int ntile = gridDim.x;
-  const int logical = xcd_remap(blockIdx.y * ntile + blockIdx.x, ntile * gridDim.y);
-  const int bh = logical / ntile, h = bh % H;
-  const int tile = logical % ntile;
-  const int t0 = tile * kT;
-  const int tq = t0 + 16 * wave + r16;  // this lane's query (column of S^T tiles)
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
-  const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bo(o_swa + off, nb),
-      bdo(dO + off, nb);
+  const int nseg = gridDim.x;
+  const int logical = xcd_remap(blockIdx.y * nseg + blockIdx.x, nseg * gridDim.y);
+  const int bh = logical / nseg, h = bh % H;
+  const int seg = logical % nseg;
+  const int ntiles = (T_len + kT - 1) / kT;
+  const int i0 = seg * per, i1 = min(ntiles, i0 + per);
+  const size_t off = (size_t)bh * T_len * D;
+  const u32 nb = (u32)((size_t)T_len * D * sizeof(T));
+  const Buf bq(q + off, nb), bk(k + off, nb), bv(v + off, nb), bdo(dO + off, nb);
   const float sl2 = scale * kLog2e;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  // per-wave fragments of q and dO (also used as A fragments: same layout)
-  F qf[2], df[2];
-  float dot = 0.f;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int tl = min(tq, T_len - 1);
-    qf[p] = ld8<T>(q + off + (size_t)tl * kD + 32 * p + 8 * g);
-    df[p] = ld8<T>(dO + off + (size_t)tl * kD + 32 * p + 8 * g);
-    const F of = ld8<T>(o_swa + off + (size_t)tl * kD + 32 * p + 8 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dot += to_f(df[p][e]) * to_f(of[e]);
-  }
-  const float Dt = mix * wave_sum16(dot);
-  const float lse2 = (tq < T_len ? lse[(size_t)bh * T_len + tq] : 0.f) * kLog2e;
-  if (g == 0) {
-    slse[16 * wave + r16] = lse2;
-    sD[16 * wave + r16] = Dt;
-    if (tq < T_len) Dws[(size_t)bh * T_len + tq] = Dt;
-  }
-
-  f32x4 dqT[kD / 16];
-#pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) dqT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- meta slots
   if (M > 0) {
-    const Buf bmk(mk + (size_t)h * M * kD, (u32)(M * kD * sizeof(T)));
-    const Buf bmv(mv + (size_t)h * M * kD, (u32)(M * kD * sizeof(T)));
-    stage_rows<T>(&smk[0][0], kDP, bmk, 0, kD, 16, tid, kThreads);
-    stage_rows<T>(&smv[0][0], kDP, bmv, 0, kD, 16, tid, kThreads);
-    stage_cols<T>(&smkT[0][0], 40, bmk, 0, kD, 32, tid, kThreads);
-    stage_cols<T>(&sqT[0][0], kTP, bq, t0, kD, kT, tid, kThreads);
-    stage_cols<T>(&sdoT[0][0], kTP, bdo, t0, kD, kT, tid, kThreads);
-    __syncthreads();
-    // transposed orientation (lane <-> query) for dq
-    f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    const Buf bmk(mk + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
+    const Buf bmv(mv + (size_t)h * M * D, (u32)(M * D * sizeof(T)));
+    stage_rows<T>(&sm.smk[0][0], DP, bmk, 0, D, 16, tid, kThreads);
+    stage_rows<T>(&sm.smv[0][0], DP, bmv, 0, D, 16, tid, kThreads);
+    stage_cols<T>(&sm.smkT[0][0], 40, bmk, 0, D, 32, tid, kThreads);
+    for (int e = tid; e < 2 * D * 17; e += kThreads) (&sm.red[0][0])[e] = 0.f;
+  }
+
+  for (int tile = i0; tile < i1; ++tile) {
+    const int t0 = tile * kT;
+    const int tq = t0 + 16 * wave + r16;  // this lane's query (column of S^T tiles)
+    // per-wave fragments of q and dO (also used as A fragments: same layout)
+    F qf[KP], df[KP];
+    float dot = 0.f;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      mma(s, ld8<T>(&smk[r16][32 * p + 8 * g]), qf[p]);
-      mma(dp, ld8<T>(&smv[r16][32 * p + 8 * g]), df[p]);
+    for (int p = 0; p < KP; ++p) {
+      const int tl = min(tq, T_len - 1);
+      qf[p] = ld8<T>(q + off + (size_t)tl * D + 32 * p + 8 * g);
+      df[p] = ld8<T>(dO + off + (size_t)tl * D + 32 * p + 8 * g);
+      const F of = ld8<T>(o_swa + off + (size_t)tl * D + 32 * p + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += to_f(df[p][e]) * to_f(of[e]);
     }
-    f32x4 ds;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = 4 * g + r < M;
-      const float pr = ok ? exp2_fast(s[r] * sl2 - lse2) : 0.f;
-      ds[r] = pr * (mix * dp[r] - Dt);
+    const float Dt = mix * wave_sum16(dot);
+    const float lse2 = (tq < T_len ? lse[(size_t)bh * T_len + tq] : 0.f) * kLog2e;
+    __syncthreads();  // the previous tile's LDS reads are done
+    if (g == 0) {
+      sm.slse[16 * wave + r16] = lse2;
+      sm.sD[16 * wave + r16] = Dt;
+      if (tq < T_len) Dws[(size_t)bh * T_len + tq] = Dt;
     }
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    f32x4 dqT[NCT];
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct)
-      mma(dqT[ct], ld4x2<T>(&smkT[16 * ct + r16][4 * g]), pack_acc<T>(ds, zero));
-    // slot orientation (lane <-> slot) for the meta gradients of this wave's queries
-    f32x4 s2 = {0.f, 0.f, 0.f, 0.f}, dp2 = {0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < NCT; ++ct) dqT[ct] = zero;
+
+    // ---- meta slots
+    if (M > 0) {
+      stage_cols<T>(&sm.sqT[0][0], TP, bq, t0, D, kT, tid, kThreads);
+      stage_cols<T>(&sm.sdoT[0][0], TP, bdo, t0, D, kT, tid, kThreads);
+      __syncthreads();
+      // transposed orientation (lane <-> query) for dq
+      f32x4 sc = zero, dp = zero;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      mma(s2, qf[p], ld8<T>(&smk[r16][32 * p + 8 * g]));
-      mma(dp2, df[p], ld8<T>(&smv[r16][32 * p + 8 * g]));
-    }
-    f32x4 p2, ds2;  // rows t = 16 wave + 4g + r, column slot r16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tl = 16 * wave + 4 * g + r;
-      const bool ok = (r16 < M) && (t0 + tl < T_len);
-      p2[r] = ok ? exp2_fast(s2[r] * sl2 - slse[tl]) : 0.f;
-      ds2[r] = p2[r] * (mix * dp2[r] - sD[tl]);
-    }
-    f32x4 mkT[kD / 16], mvT[kD / 16];  // [c = 16ct + 4g + r][slot r16]
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      mkT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mvT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      F aq, ao;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        aq[e] = sqT[16 * ct + r16][16 * wave + 4 * g + e];
-        ao[e] = sdoT[16 * ct + r16][16 * wave + 4 * g + e];
-        aq[e + 4] = to_t<T>(0.f);
-        ao[e + 4] = to_t<T>(0.f);
+      for (int p = 0; p < KP; ++p) {
+        mma(sc, ld8<T>(&sm.smk[r16][32 * p + 8 * g]), qf[p]);
+        mma(dp, ld8<T>(&sm.smv[r16][32 * p + 8 * g]), df[p]);
       }
-      mma(mkT[ct], aq, pack_acc<T>(ds2, zero));
-      mma(mvT[ct], ao, pack_acc<T>(p2, zero));
-    }
-    // reduce the four waves' partials in a fixed order: red[c or D + j][slot]
-    for (int wv = 0; wv < 4; ++wv) {
-      if (wave == wv) {
+      f32x4 ds;
 #pragma unroll
-        for (int ct = 0; ct < kD / 16; ++ct)
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 4 * g + r < M;
+        const float pr = ok ? exp2_fast(sc[r] * sl2 - lse2) : 0.f;
+        ds[r] = pr * (mix * dp[r] - Dt);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        mma(dqT[ct], ld4x2<T>(&sm.smkT[16 * ct + r16][4 * g]), pack_acc<T>(ds, zero));
+      // slot orientation (lane <-> slot) for the meta gradients of this wave's queries
+      f32x4 s2 = zero, dp2 = zero;
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+        mma(s2, qf[p], ld8<T>(&sm.smk[r16][32 * p + 8 * g]));
+        mma(dp2, df[p], ld8<T>(&sm.smv[r16][32 * p + 8 * g]));
+      }
+      f32x4 p2, ds2;  // rows t = 16 wave + 4g + r, column slot r16
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 16 * wave + 4 * g + r;
+        const bool ok = (r16 < M) && (t0 + tl < T_len);
+        p2[r] = ok ? exp2_fast(s2[r] * sl2 - sm.slse[tl]) : 0.f;
+        ds2[r] = p2[r] * (mix * dp2[r] - sm.sD[tl]);
+      }
+      // add the four waves' partials to the segment's sums in a fixed order
+      for (int wv = 0; wv < 4; ++wv) {
+        if (wave == wv) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 mkT = zero, mvT = zero;  // [c = 16ct + 4g + r][slot r16]
+            F aq, ao;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              aq[e] = sm.sqT[16 * ct + r16][16 * wave + 4 * g + e];
+              ao[e] = sm.sdoT[16 * ct + r16][16 * wave + 4 * g + e];
+              aq[e + 4] = to_t<T>(0.f);
+              ao[e + 4] = to_t<T>(0.f);
+            }
+            mma(mkT, aq, pack_acc<T>(ds2, zero));
+            mma(mvT, ao, pack_acc<T>(p2, zero));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int cc = 16 * ct + 4 * g + r;
+              sm.red[cc][r16] += scale * mkT[r];
+              sm.red[D + cc][r16] += mix * mvT[r];
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    // ---- key tiles overlapping [t0 - W + 1, t0 + 63]
+    const int first_key = max(0, t0 - W + 1);
+    const int last_key = min(T_len - 1, t0 + kT - 1);
+    const int tq0 = t0 + 16 * wave;
+    for (int kt0 = (first_key / kT) * kT; kt0 <= last_key; kt0 += kT) {
+      __syncthreads();
+      stage_rows<T>(&sm.skt[0][0], DP, bk, kt0, D, kT, tid, kThreads);
+      stage_rows<T>(&sm.svt[0][0], DP, bv, kt0, D, kT, tid, kThreads);
+      stage_cols<T>(&sm.skT[0][0], TP, bk, kt0, D, kT, tid, kThreads);
+      __syncthreads();
+      f32x4 ds[4];
+      bool act[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int s_lo = kt0 + 16 * b;
+        act[b] = (s_lo + 15 >= tq0 - W + 1) && (s_lo <= tq0 + 15) && (s_lo < T_len);
+        ds[b] = zero;
+        if (act[b]) {
+          f32x4 sc = zero, dp = zero;
+#pragma unroll
+          for (int p = 0; p < KP; ++p) {
+            mma(sc, ld8<T>(&sm.skt[16 * b + r16][32 * p + 8 * g]), qf[p]);
+            mma(dp, ld8<T>(&sm.svt[16 * b + r16][32 * p + 8 * g]), df[p]);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int cc = 16 * ct + 4 * g + r;
-            const float a = scale * mkT[ct][r], b = mix * mvT[ct][r];
-            red[cc][r16] = (wv == 0 ? 0.f : red[cc][r16]) + a;
-            red[kD + cc][r16] = (wv == 0 ? 0.f : red[kD + cc][r16]) + b;
+            const int sk = s_lo + 4 * g + r;
+            const bool ok = (sk <= tq) && (sk > tq - W) && (tq < T_len);
+            const float pr = ok ? exp2_fast(sc[r] * sl2 - lse2) : 0.f;
+            ds[b][r] = pr * (mix * dp[r] - Dt);
           }
-      }
-      __syncthreads();
-    }
-    // partial layout per (bh, tile): [M][kD] for meta_k then [M][kD] for meta_v
-    float* mp = metap + ((size_t)bh * ntile + tile) * (size_t)M * 2 * kD;
-    for (int e = tid; e < M * 2 * kD; e += kThreads) {
-      const int which = e / (M * kD), rem = e % (M * kD), i = rem / kD, cc = rem % kD;
-      mp[e] = red[which * kD + cc][i];
-    }
-  }
-
-  // ---- key tiles overlapping [t0 - W + 1, t0 + 63]
-  const int first_key = max(0, t0 - W + 1);
-  const int last_key = min(T_len - 1, t0 + kT - 1);
-  const int tq0 = t0 + 16 * wave;
-  for (int kt0 = (first_key / kT) * kT; kt0 <= last_key; kt0 += kT) {
-    __syncthreads();
-    stage_rows<T>(&skt[0][0], kDP, bk, kt0, kD, kT, tid, kThreads);
-    stage_rows<T>(&svt[0][0], kDP, bv, kt0, kD, kT, tid, kThreads);
-    stage_cols<T>(&skT[0][0], kTP, bk, kt0, kD, kT, tid, kThreads);
-    __syncthreads();
-    f32x4 ds[4];
-    bool act[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int s_lo = kt0 + 16 * b;
-      act[b] = (s_lo + 15 >= tq0 - W + 1) && (s_lo <= tq0 + 15) && (s_lo < T_len);
-      ds[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (act[b]) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          mma(s, ld8<T>(&skt[16 * b + r16][32 * p + 8 * g]), qf[p]);
-          mma(dp, ld8<T>(&svt[16 * b + r16][32 * p + 8 * g]), df[p]);
         }
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int sk = s_lo + 4 * g + r;
-          const bool ok = (sk <= tq) && (sk > tq - W) && (tq < T_len);
-          const float pr = ok ? exp2_fast(s[r] * sl2 - lse2) : 0.f;
-          ds[b][r] = pr * (mix * dp[r] - Dt);
+      for (int pp = 0; pp < 2; ++pp) {
+        if (act[2 * pp] || act[2 * pp + 1]) {
+          const F bf = pack_acc<T>(ds[2 * pp], ds[2 * pp + 1]);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            mma(dqT[ct], ld4x2<T>(&sm.skT[16 * ct + r16][32 * pp + 4 * g]), bf);
         }
       }
     }
+    // ---- dq[t][c] = scale * dq^T[c][t]
+    if (tq < T_len) {
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      if (act[2 * pp] || act[2 * pp + 1]) {
-        const F bf = pack_acc<T>(ds[2 * pp], ds[2 * pp + 1]);
-#pragma unroll
-        for (int ct = 0; ct < kD / 16; ++ct)
-          mma(dqT[ct], ld4x2<T>(&skT[16 * ct + r16][32 * pp + 4 * g]), bf);
-      }
+      for (int ct = 0; ct < NCT; ++ct)
+        st4<T>(dq + off + (size_t)tq * D + 16 * ct + 4 * g, dqT[ct] * scale);
     }
   }
-  // ---- dq[t][c] = scale * dq^T[c][t]
-  if (tq < T_len) {
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct)
-      st4<T>(dq + off + (size_t)tq * kD + 16 * ct + 4 * g, dqT[ct] * scale);
+  // ---- the segment's meta partials: [M][D] for meta_k then [M][D] for meta_v
+  if (M > 0) {
+    __syncthreads();
+    float* mp = metap + ((size_t)bh * nseg + seg) * (size_t)M * 2 * D;
+    for (int e = tid; e < M * 2 * D; e += kThreads) {
+      const int which = e / (M * D), rem = e % (M * D), i = rem / D, cc = rem % D;
+      mp[e] = sm.red[which * D + cc][i];
+    }
   }
 }
 
 // ----------------------------------------------------------------- 2. dk, dv
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ Dws,
     T* __restrict__ dk, T* __restrict__ dv, int T_len, int W, float scale, float mix) {
+  constexpr int KP = D / 32, NCT = D / 16;
+  constexpr int DP = D + 8, TP = kT + 8;
   typedef typename Frag<T>::type F;
-  __shared__ __attribute__((aligned(16))) T sq[kT][kDP];
-  __shared__ __attribute__((aligned(16))) T sdo[kT][kDP];
-  __shared__ __attribute__((aligned(16))) T sqT[kD][kTP];
-  __shared__ __attribute__((aligned(16))) T sdoT[kD][kTP];
+  __shared__ __attribute__((aligned(16))) T sq[kT][DP];
+  __shared__ __attribute__((aligned(16))) T sdo[kT][DP];
+  __shared__ __attribute__((aligned(16))) T sqT[D][TP];
+  __shared__ __attribute__((aligned(16))) T sdoT[D][TP];
   __shared__ __attribute__((aligned(16))) float slse[kT], sD[kT];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
@@ -242,31 +263,31 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
   const int s0 = (logical % ntile) * kT;
   const int sk0 = s0 + 16 * wave;      // first key of this wave
   const int sk = sk0 + r16;            // this lane's key (column of the S tiles)
-  const size_t off = (size_t)bh * T_len * kD;
-  const u32 nb = (u32)((size_t)T_len * kD * sizeof(T));
+  const size_t off = (size_t)bh * T_len * D;
+  const u32 nb = (u32)((size_t)T_len * D * sizeof(T));
   const Buf bq(q + off, nb), bdo(dO + off, nb);
   const float sl2 = scale * kLog2e;
 
-  F kf[2], vf[2];
+  F kf[KP], vf[KP];
   const int skl = min(sk, T_len - 1);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    kf[p] = ld8<T>(k + off + (size_t)skl * kD + 32 * p + 8 * g);
-    vf[p] = ld8<T>(v + off + (size_t)skl * kD + 32 * p + 8 * g);
+  for (int p = 0; p < KP; ++p) {
+    kf[p] = ld8<T>(k + off + (size_t)skl * D + 32 * p + 8 * g);
+    vf[p] = ld8<T>(v + off + (size_t)skl * D + 32 * p + 8 * g);
   }
-  f32x4 dkT[kD / 16], dvT[kD / 16];  // [c or j = 16ct + 4g + r][key r16]
+  f32x4 dkT[NCT], dvT[NCT];  // [c or j = 16ct + 4g + r][key r16]
 #pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) {
+  for (int ct = 0; ct < NCT; ++ct) {
     dkT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     dvT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int last_q = min(T_len - 1, s0 + kT - 1 + W - 1);
   for (int qt0 = s0; qt0 <= last_q; qt0 += kT) {
     __syncthreads();
-    stage_rows<T>(&sq[0][0], kDP, bq, qt0, kD, kT, tid, kThreads);
-    stage_rows<T>(&sdo[0][0], kDP, bdo, qt0, kD, kT, tid, kThreads);
-    stage_cols<T>(&sqT[0][0], kTP, bq, qt0, kD, kT, tid, kThreads);
-    stage_cols<T>(&sdoT[0][0], kTP, bdo, qt0, kD, kT, tid, kThreads);
+    stage_rows<T>(&sq[0][0], DP, bq, qt0, D, kT, tid, kThreads);
+    stage_rows<T>(&sdo[0][0], DP, bdo, qt0, D, kT, tid, kThreads);
+    stage_cols<T>(&sqT[0][0], TP, bq, qt0, D, kT, tid, kThreads);
+    stage_cols<T>(&sdoT[0][0], TP, bdo, qt0, D, kT, tid, kThreads);
     if (tid < kT) {
       const int t = qt0 + tid;
       slse[tid] = t < T_len ? lse[(size_t)bh * T_len + t] * kLog2e : 0.f;
@@ -282,17 +303,17 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
       P[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       dS[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (act[qb]) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          mma(s, ld8<T>(&sq[16 * qb + r16][32 * p + 8 * g]), kf[p]);
+        for (int p = 0; p < KP; ++p) {
+          mma(sc, ld8<T>(&sq[16 * qb + r16][32 * p + 8 * g]), kf[p]);
           mma(dp, ld8<T>(&sdo[16 * qb + r16][32 * p + 8 * g]), vf[p]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tl = 16 * qb + 4 * g + r, t = qt0 + tl;
           const bool ok = (sk <= t) && (t < sk + W) && (t < T_len) && (sk < T_len);
-          const float pr = ok ? exp2_fast(s[r] * sl2 - slse[tl]) : 0.f;
+          const float pr = ok ? exp2_fast(sc[r] * sl2 - slse[tl]) : 0.f;
           P[qb][r] = pr;
           dS[qb][r] = pr * (mix * dp[r] - sD[tl]);
         }
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
         const F bp = pack_acc<T>(P[2 * pp], P[2 * pp + 1]);
         const F bs = pack_acc<T>(dS[2 * pp], dS[2 * pp + 1]);
 #pragma unroll
-        for (int ct = 0; ct < kD / 16; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
           mma(dvT[ct], ld4x2<T>(&sdoT[16 * ct + r16][32 * pp + 4 * g]), bp);
           mma(dkT[ct], ld4x2<T>(&sqT[16 * ct + r16][32 * pp + 4 * g]), bs);
         }
@@ -313,9 +334,9 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
   }
   if (sk < T_len) {
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      st4<T>(dk + off + (size_t)sk * kD + 16 * ct + 4 * g, dkT[ct] * scale);
-      st4<T>(dv + off + (size_t)sk * kD + 16 * ct + 4 * g, dvT[ct] * mix);
+    for (int ct = 0; ct < NCT; ++ct) {
+      st4<T>(dk + off + (size_t)sk * D + 16 * ct + 4 * g, dkT[ct] * scale);
+      st4<T>(dv + off + (size_t)sk * D + 16 * ct + 4 * g, dvT[ct] * mix);
     }
   }
 }
@@ -711,11 +732,12 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
 // its 16 thread groups sum interleaved sixteenths of the partials (coalesced,
 // up to 16 loads in flight per thread), then a fixed tree adds the 16 sums.
 constexpr int kMetaGroups = 16;
+template <int D>
 __global__ __launch_bounds__(64 * kMetaGroups) void swa_meta_reduce(
     const float* __restrict__ metap, float* __restrict__ dmk, float* __restrict__ dmv, int B,
     int H, int ntiles, int M) {
   const int h = blockIdx.x;
-  const int n = M * kD;
+  const int n = M * D;
   const int i = threadIdx.x & 63;
   const int e = blockIdx.y * 64 + i;
   const int grp = threadIdx.x >> 6;
@@ -751,51 +773,77 @@ __global__ __launch_bounds__(64 * kMetaGroups) void swa_meta_reduce(
   }
 }
 
-}  // namespace
+// Segments per head of the window backward's work-groups (whole 64-query
+// tiles): enough work-groups to fill the chip, at most one per tile.  The
+// workspace is sized for the bound that holds for any T.
+int swa_bwd_segments(int BH, int nqt) { return std::max(1, std::min(nqt, (256 + BH - 1) / BH)); }
 
-size_t swa_bwd_workspace_bytes(const Shape& s) {
-  const size_t bh = (size_t)s.B * s.H;
-  const size_t nqt = (size_t)(s.T + kT - 1) / kT;
-  return bh * s.T * sizeof(float) + bh * nqt * s.n_meta * 2 * kD * sizeof(float);
+template <typename T, int D>
+hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, const void* v,
+                                const void* mk, const void* mv, const void* o_swa,
+                                const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                float* dmk, float* dmv, float* Dws, float* metap, hipStream_t st) {
+  const int BH = s.B * s.H;
+  const int nqt = (s.T + kT - 1) / kT;
+  int G = swa_bwd_segments(BH, nqt);
+  const int per = (nqt + G - 1) / G;
+  G = (nqt + per - 1) / per;
+  if constexpr (sizeof(T) == 2 && D == 64) {
+    if (s.window <= 65) {
+      // streaming form: B*H*G work-groups, G segments of whole tiles per sequence
+      hipLaunchKernelGGL(swa_bwd_stream, dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
+                         (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa,
+                         lse, (const T*)dO, (T*)dq, (T*)dk, (T*)dv, metap, s.T, s.H, s.window,
+                         s.n_meta, s.scale, s.mix, per);
+      if (s.n_meta > 0)
+        hipLaunchKernelGGL(swa_meta_reduce<D>, dim3(s.H, (2 * s.n_meta * D + 63) / 64),
+                           dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((swa_bwd_dq<T, D>), dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa, lse,
+                     (const T*)dO, (T*)dq, Dws, metap, s.T, s.H, s.window, s.n_meta, s.scale,
+                     s.mix, per);
+  hipLaunchKernelGGL((swa_bwd_dkdv<T, D>), dim3(nqt, BH), dim3(kThreads), 0, st, (const T*)q,
+                     (const T*)k, (const T*)v, lse, (const T*)dO, Dws, (T*)dk, (T*)dv, s.T,
+                     s.window, s.scale, s.mix);
+  if (s.n_meta > 0)
+    hipLaunchKernelGGL(swa_meta_reduce<D>, dim3(s.H, (2 * s.n_meta * D + 63) / 64),
+                       dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);
+  return hipGetLastError();
 }
 
+}  // namespace
+
+// Meta-gradient partials per (sequence, head, segment); the segment count is
+// at most ceil(256 / (B*H)) whatever T is.
+size_t swa_bwd_workspace_bytes(const Shape& s) {
+  const size_t bh = (size_t)s.B * s.H;
+  if (bh == 0) return 0;
+  const size_t gmax = (size_t)std::max<size_t>(1, (256 + bh - 1) / bh);
+  return bh * gmax * s.n_meta * 2 * s.dk * sizeof(float);
+}
+
+// Dws: B*H*T floats of scratch for D_t = mix * dO_t . o_swa,t (the caller passes
+// memory it overwrites later, so the workspace does not grow with T).
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv, float* dmk, float* dmv,
-                          void* ws, hipStream_t st) {
-  typedef bf16 T;
+                          float* Dws, void* ws, hipStream_t st) {
   const int BH = s.B * s.H;
   const int nqt = (s.T + kT - 1) / kT;
-  float* Dws = (float*)ws;
-  float* metap = Dws + (size_t)BH * s.T;
-  if (nqt > 0 && BH > 0 && s.window <= 65) {
-    // streaming form: B*H*G work-groups, G segments of whole tiles per sequence
-    int G = std::max(1, std::min(nqt, (256 + BH - 1) / BH));
-    const int per = (nqt + G - 1) / G;
-    G = (nqt + per - 1) / per;
-    hipLaunchKernelGGL(swa_bwd_stream, dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa, lse,
-                       (const T*)dO, (T*)dq, (T*)dk, (T*)dv, metap, s.T, s.H, s.window, s.n_meta,
-                       s.scale, s.mix, per);
-    if (s.n_meta > 0 && s.H > 0)
-      hipLaunchKernelGGL(swa_meta_reduce, dim3(s.H, (2 * s.n_meta * kD + 63) / 64),
-                         dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);
-    return hipGetLastError();
+  if (nqt == 0 || BH == 0) return hipSuccess;
+  float* metap = (float*)ws;
+  if (s.dtype == 1) {
+    if (s.dk == 128)
+      return launch_swa_bwd_typed<bf16, 128>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
+                                             dmv, Dws, metap, st);
+    return launch_swa_bwd_typed<bf16, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
+                                          dmv, Dws, metap, st);
   }
-  if (nqt > 0 && BH > 0) {
-    hipLaunchKernelGGL(swa_bwd_dq<T>, dim3(nqt, BH), dim3(kThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa, lse,
-                       (const T*)dO, (T*)dq, Dws, metap, s.T, s.H, s.window, s.n_meta, s.scale,
-                       s.mix);
-    hipLaunchKernelGGL(swa_bwd_dkdv<T>, dim3(nqt, BH), dim3(kThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, lse, (const T*)dO, Dws, (T*)dk, (T*)dv, s.T,
-                       s.window, s.scale, s.mix);
-  }
-  if (s.n_meta > 0 && s.H > 0)
-    hipLaunchKernelGGL(swa_meta_reduce, dim3(s.H, (2 * s.n_meta * kD + 63) / 64),
-                       dim3(64 * kMetaGroups), 0, st,
-                       metap, dmk, dmv, s.B, s.H, nqt, s.n_meta);
-  return hipGetLastError();
+  return launch_swa_bwd_typed<float, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
+                                         Dws, metap, st);
 }
 
 }  // namespace lz

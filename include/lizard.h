@@ -102,6 +102,9 @@ typedef struct {
  * invalid desc yields 0, and the call itself then reports the problem.
  * LIZARD_OP_GLA_FWD / LIZARD_OP_HYBRID_FWD: per-segment GLA states, at most
  * 15 * B*H * (dk*dv + dk) * 4 bytes and independent of T once T >= 1024.
+ * LIZARD_OP_HYBRID_BWD: 64 chunk states per head in the element type plus one
+ * fp32 state per head, and per-segment meta-gradient partials; it does not
+ * depend on T at all (the backward walks a sequence in blocks of 2048 tokens).
  * The workspace holds no state between calls. */
 size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op);
 
@@ -176,14 +179,18 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
  * differentiated by chaining dh0 of a segment into dhT of the one before, the
  * constant-size state of "Lizard: An Efficient Linearization Framework for Large
  * Language Models" (gist.science summary, sections 2(a) and 4).  ws must hold
- * lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_BWD) bytes: two bf16 dk x dv
- * matrices per 64-token chunk and head (S_c and dS_{c+1}) plus small per-token
- * and per-tile buffers, so it grows linearly with T.  q_w, k_w, dq_w, dk_w
+ * lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_BWD) bytes, which do not grow
+ * with T: the gated branch is differentiated in blocks of 32 chunks, last block
+ * first, recomputing each block's chunk states from the state entering it;
+ * those block-entry states (and per-token scratch of the window branch) are
+ * kept in dgate's own rows until the rows are written, so dgate must not
+ * overlap any input.  q_w, k_w, dq_w, dk_w
  * (all four NULL, or all four given, else LIZARD_E_NULL): the window branch's
  * own queries and keys as passed to lizard_hybrid_fwd, and their gradients
  * [B,H,T,dk] (desc->dtype, overwritten); dq, dk then hold the gated branch's
  * gradients alone.  With them NULL, dq and dk hold both branches' gradients.
- * This version supports BF16 with dk = dv = 64 (LIZARD_E_UNSUPPORTED otherwise). */
+ * This version supports BF16 with dk = dv in {64, 128} and F32 with dk = dv = 64
+ * (LIZARD_E_UNSUPPORTED for F32 at 128). */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,

@@ -158,11 +158,24 @@ def test_backward_workspace_and_support():
     assert need > 0
     st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 23), FAKE, need - 1, None)
     assert st == 5
-    # this version's backward covers bf16 with d = 64
+    # the backward covers bf16 at d = 64 and 128 and fp32 at d = 64
     for kw in (dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32)):
-        d2 = desc(**kw)
-        assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
-        assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 23), FAKE, 1 << 30, None) == 4
+        assert lib.lizard_workspace_bytes(ctypes.byref(desc(**kw)), 3) > 0
+    d2 = desc(dk=128, dv=128, dtype=_abi.LIZARD_F32)
+    assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
+    assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 23), FAKE, 1 << 30, None) == 4
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32),
+                                dict(B=8, H=16, window=200, n_meta=16)])
+def test_backward_workspace_does_not_grow_with_T(kw):
+    # the GLA part holds a fixed number of chunk states per head and the window
+    # part a fixed number of meta partials per head, whatever the sequence length
+    lib = _abi.lib()
+    sizes = {T: lib.lizard_workspace_bytes(ctypes.byref(desc(T=T, **kw)), 3)
+             for T in (1, 64, 1024, 2048, 32768, 262144)}
+    assert len(set(sizes.values())) == 1, sizes
+    assert sizes[1] > 0
 
 
 def test_static_scratch_entry_checks_arguments_first():

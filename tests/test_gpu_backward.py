@@ -46,12 +46,14 @@ def ref_grads(inp, w, s, mix, h0=None, dhT=None):
                                   dhT=None if dhT is None else dhT.double().numpy())
 
 
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
 def check(B, H, T, w, M, seed=0, mix=1.0, gate_mean=2.0, with_h0=False, steep_chunks=False,
-          with_dhT=False):
-    d = 64
-    print(f"[case] bwd B{B} H{H} T{T} w{w} M{M} mix{mix} gate{gate_mean} h0{with_h0} "
-          f"steep{steep_chunks} dhT{with_dhT}", flush=True)
-    inp = make_inputs(B, H, T, d, d, M, dtype="bf16", seed=seed, gate_mean=gate_mean,
+          with_dhT=False, d=64, dtype="bf16"):
+    print(f"[case] bwd B{B} H{H} T{T} d{d} {dtype} w{w} M{M} mix{mix} gate{gate_mean} "
+          f"h0{with_h0} steep{steep_chunks} dhT{with_dhT}", flush=True)
+    inp = make_inputs(B, H, T, d, d, M, dtype=dtype, seed=seed, gate_mean=gate_mean,
                       with_grad_out=True, with_h0=with_h0)
     if steep_chunks:
         # every third 64-token chunk decays 8x faster (about -94 per chunk in
@@ -69,26 +71,56 @@ def check(B, H, T, w, M, seed=0, mix=1.0, gate_mean=2.0, with_h0=False, steep_ch
     for n in NAMES:
         if n.startswith("dmeta") and M == 0:
             continue
-        assert_close(n, g[n], ref[n], BF)
-    check_dmix(g["dmix"], ref["dmix"], inp, w, s)
+        assert_close(n, g[n], ref[n], DT[dtype])
+    check_dmix(g["dmix"], ref["dmix"], inp, w, s, dtype)
 
 
-def check_dmix(got, ref, inp, w, s):
-    # dmix = sum(dO * o_swa): o_swa is saved in bf16 (relative rounding <= 2^-8
-    # per element) and the sum runs in fp32, so |error| <= 2^-8 sum(|dO| |o_swa|);
-    # the bound is on that scale because the sum itself may cancel
+def check_dmix(got, ref, inp, w, s, dtype="bf16"):
+    # dmix = sum(dO * o_swa): o_swa is saved in the input precision (relative
+    # rounding <= 2^-8 in bf16; in fp32 its error is the forward's, held to
+    # 1e-4) and the sum runs in fp32, so |error| <= u sum(|dO| |o_swa|); the
+    # bound is on that scale because the sum itself may cancel
     r = f64(inp)
     o_swa, _ = oracle.window_meta_attention(r["q"], r["k"], r["v"], r["meta_k"], r["meta_v"], w, s)
     scale = float((np.abs(r["dO"]) * np.abs(o_swa)).sum())
     err = abs(float(got.item()) - ref)
+    u = 2.0 ** -8 if dtype == "bf16" else 1e-4
     print(f"  dmix: {float(got.item()):.6e} vs {ref:.6e} (error {err:.2e}, bound scale {scale:.2e})")
-    assert err <= 2.0 ** -8 * scale
+    assert err <= u * scale
 
 
 @pytest.mark.parametrize("T,w,M", [(64, 64, 4), (200, 64, 4), (257, 16, 16), (130, 1, 0),
                                    (100, 300, 2)])
 def test_backward_shapes(T, w, M):
     check(2, 2, T, w, M, seed=T + w)
+
+
+@pytest.mark.parametrize("T,w,M", [(64, 64, 4), (200, 128, 4), (257, 16, 16), (130, 1, 0),
+                                   (300, 200, 2), (400, 65, 4)])
+def test_backward_bf16_d128(T, w, M):
+    # the Llama-like head size: generic GLA gradient kernels, tiled window backward
+    check(2, 2, T, w, M, seed=T + w, d=128)
+
+
+@pytest.mark.parametrize("T,w,M", [(64, 64, 4), (200, 64, 4), (257, 16, 16), (130, 1, 0),
+                                   (100, 300, 2)])
+def test_backward_fp32_d64(T, w, M):
+    check(2, 2, T, w, M, seed=T + w, dtype="f32")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+def test_backward_generic_gate_ranges_and_states(d, dtype):
+    check(1, 2, 192, 64, 4, seed=4, gate_mean=-3.0, d=d, dtype=dtype)
+    check(2, 1, 450, 64, 4, seed=5, steep_chunks=True, d=d, dtype=dtype)
+    check(2, 2, 200, 64, 4, seed=11, with_h0=True, with_dhT=True, mix=0.6, d=d, dtype=dtype)
+
+
+@pytest.mark.parametrize("T,d,dtype", [(4500, 64, "bf16"), (2200, 128, "bf16"), (2100, 64, "f32")])
+def test_backward_several_blocks(T, d, dtype):
+    # longer than one 2048-token block: the block-start states (parked in the
+    # gate-gradient output) and the reverse carry between blocks, with an
+    # initial state and a final-state gradient
+    check(1, 2, T, 64, 4, seed=T, with_h0=True, with_dhT=True, d=d, dtype=dtype)
 
 
 def test_backward_h0_and_mix():
