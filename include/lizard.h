@@ -108,7 +108,10 @@ typedef struct {
  * The workspace holds no state between calls. */
 size_t lizard_workspace_bytes(const lizard_desc_t* desc, int32_t op);
 
-/* Chunked gated linear attention forward (GLA branch alone).
+/* Chunked gated linear attention forward (GLA branch alone): the gated state
+ * update of "Lizard: An Efficient Linearization Framework for Large Language
+ * Models" (gist.science summary, section 2(a)), computed chunk by chunk with the
+ * log-space gate absorption of its section 2(c):
  *   o_t = q_t S_t with S_t = diag(exp(log_alpha_t)) S_{t-1} + k_t^T v_t, S_{-1} = h0.
  * h0 (nullable, NULL = zeros) is read; o is written; hT (nullable) receives S_{T-1}
  * (h0, or zeros, when T == 0).  ws must hold lizard_workspace_bytes(desc,
@@ -118,9 +121,13 @@ lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const v
                                void* o, float* hT, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
-/* Sliding-window + meta-memory softmax attention forward (window branch alone).
- * o receives o_swa (no mix applied); lse (nullable) receives the log-sum-exp of
- * each query's logits. */
+/* Sliding-window + meta-memory softmax attention forward (window branch alone):
+ * the anchor window of "Lizard: An Efficient Linearization Framework for Large
+ * Language Models" (gist.science summary, section 2(a)), one softmax over the
+ * keys t-w+1 .. t and the M learnable meta-memory slots (which the section puts
+ * in the softmax denominator), scaled by desc->scale.  o receives o_swa (no mix
+ * applied); lse (nullable) receives the natural log-sum-exp of each query's
+ * logits.  Needs no workspace. */
 lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
                                const void* v, const void* meta_k, const void* meta_v,
                                void* o, float* lse, hipStream_t stream);
@@ -200,7 +207,12 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
-/* One constant-memory generation step for B sequences (desc->T is ignored).
+/* One constant-memory generation step for B sequences (desc->T is ignored): the
+ * recurrent form of both branches, as the constant-memory inference of "Lizard:
+ * An Efficient Linearization Framework for Large Language Models" (gist.science
+ * summary, sections 2(a) and 4 "Efficiency") needs it: the fp32 state is
+ * updated in place and the window branch reads only a ring of the last w keys
+ * and values, so the memory per sequence does not grow with its length.
  * q, k [B,H,dk], v [B,H,dv] in desc->dtype; gate [B,H,dk] as desc->gate says.
  * pos [B] int64 (device): tokens already seen by each sequence.  The call
  * updates state in place, writes (k, v) to ring slot pos mod w, attends over the
