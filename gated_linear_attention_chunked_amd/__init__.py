@@ -129,12 +129,30 @@ def _window_pair(q_w, k_w, shape, dt):
         _need(k_w, "k_w", shape, dt)
 
 
+def _halo_pair(halo_k, halo_v, B, H, dk, dv, dt, window):
+    """The window halo of a segment: [B, H, L, d] keys and values of the L tokens
+    before it (L <= window - 1).  Returns L (0 without a halo)."""
+    if (halo_k is None) != (halo_v is None):
+        raise ValueError("halo_k and halo_v: give both or neither")
+    if halo_k is None:
+        return 0
+    L = halo_k.shape[2]
+    if L > window - 1:
+        raise ValueError(f"a halo of {L} tokens exceeds window - 1 = {window - 1}")
+    _need(halo_k, "halo_k", (B, H, L, dk), dt)
+    _need(halo_v, "halo_v", (B, H, L, dv), dt)
+    return L
+
+
 def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, h0=None,
                save_for_backward=False, return_state=False, return_ring=False, q_w=None,
-               k_w=None):
+               k_w=None, halo_k=None, halo_v=None):
     """o = o_gla + mix * o_swa.  Returns a dict with "o" and, on request, "lse" and
     "o_swa" (save_for_backward), "hT" (return_state), "ring_k"/"ring_v" (return_ring).
-    q_w, k_w (optional, both or neither): the window branch's own queries and keys."""
+    q_w, k_w (optional, both or neither): the window branch's own queries and keys.
+    halo_k, halo_v (optional, [B, H, L, d], L <= window - 1): the window keys and
+    values of the L tokens before this segment of a longer sequence (segment-wise
+    runs; no window cache output then)."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -155,9 +173,18 @@ def hybrid_fwd(q, k, v, log_alpha, meta_k, meta_v, window, scale=None, mix=1.0, 
     if return_ring:
         out["ring_k"] = torch.empty(B, H, window, dk, device=dev, dtype=dt)
         out["ring_v"] = torch.empty(B, H, window, dv, device=dev, dtype=dt)
+    L = _halo_pair(halo_k, halo_v, B, H, dk, dv, dt, window)
+    if L and return_ring:
+        raise ValueError("a segment with a halo returns no window cache")
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt, gate=gate)
     nws = workspace_bytes(d, _abi.OP_HYBRID_FWD)
     ws = torch.empty(nws, device=dev, dtype=torch.uint8) if nws else None
+    if halo_k is not None:
+        _abi.check("lizard_hybrid_fwd_segment", lib().lizard_hybrid_fwd_segment(
+            ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v),
+            _p(h0), _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
+            _p(q_w), _p(k_w), _p(halo_k), _p(halo_v), L, _p(ws), nws, _stream()))
+        return out
     _abi.check("lizard_hybrid_fwd", lib().lizard_hybrid_fwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(out["o"]), _p(out.get("lse")), _p(out.get("o_swa")), _p(out.get("hT")),
@@ -218,13 +245,17 @@ def hybrid_fwd_varlen(q, k, v, log_alpha, meta_k, meta_v, window, cu_seqlens, ma
 
 
 def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale=None, mix=1.0,
-               h0=None, dhT=None, return_dh0=False, return_dmix=False, q_w=None, k_w=None):
+               h0=None, dhT=None, return_dh0=False, return_dmix=False, q_w=None, k_w=None,
+               halo_k=None, halo_v=None, return_dhalo=False, tail_dk=None, tail_dv=None):
     """Gradients of sum(dO * o) + sum(dhT * hT) (dhT: the gradient of the final
     state, optional).  Returns a dict dq, dk, dv, dlog_alpha, dmeta_k, dmeta_v and,
     with return_dh0, dh0 (the gradient of the initial state), with return_dmix,
     dmix (a one-element float32 tensor, the gradient of the mix weight).  With the
     window branch's own q_w, k_w, dq and dk are the gated branch's gradients and
-    the dict also holds dq_w, dk_w."""
+    the dict also holds dq_w, dk_w.  Segment-wise runs: halo_k, halo_v as given to
+    hybrid_fwd (with return_dhalo the dict holds their float32 gradients dhalo_k,
+    dhalo_v), and tail_dk, tail_dv [B, H, L, d] float32, the next segment's dhalo,
+    added to the gradients of this segment's last L window keys and values."""
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
@@ -251,9 +282,28 @@ def hybrid_bwd(q, k, v, log_alpha, meta_k, meta_v, window, o_swa, lse, dO, scale
     if q_w is not None:
         g["dq_w"] = torch.empty_like(q_w)
         g["dk_w"] = torch.empty_like(k_w)
+    L = _halo_pair(halo_k, halo_v, B, H, dk, dv, dt, window)
+    if (tail_dk is None) != (tail_dv is None):
+        raise ValueError("tail_dk and tail_dv: give both or neither")
+    Lt = 0 if tail_dk is None else tail_dk.shape[2]
+    if tail_dk is not None:
+        _need(tail_dk, "tail_dk", (B, H, Lt, dk), torch.float32)
+        _need(tail_dv, "tail_dv", (B, H, Lt, dv), torch.float32)
+    if return_dhalo and L:
+        g["dhalo_k"] = torch.empty(B, H, L, dk, device=dev, dtype=torch.float32)
+        g["dhalo_v"] = torch.empty(B, H, L, dv, device=dev, dtype=torch.float32)
     d = make_desc(B, H, T, dk, dv, window, M, scale, mix, dt, gate=gate)
     nws = workspace_bytes(d, _abi.OP_HYBRID_BWD)
     ws = torch.empty(max(nws, 1), device=dev, dtype=torch.uint8)
+    if L or Lt:
+        _abi.check("lizard_hybrid_bwd_segment", lib().lizard_hybrid_bwd_segment(
+            ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v),
+            _p(h0), _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]),
+            _p(g["dlog_alpha"]), _p(g["dmeta_k"]), _p(g["dmeta_v"]), _p(dhT), _p(g.get("dh0")),
+            _p(g.get("dmix")), _p(q_w), _p(k_w), _p(g.get("dq_w")), _p(g.get("dk_w")),
+            _p(halo_k), _p(halo_v), L, _p(g.get("dhalo_k")), _p(g.get("dhalo_v")),
+            _p(tail_dk), _p(tail_dv), Lt, _p(ws), nws, _stream()))
+        return g
     _abi.check("lizard_hybrid_bwd", lib().lizard_hybrid_bwd(
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(meta_k), _p(meta_v), _p(h0),
         _p(o_swa), _p(lse), _p(dO), _p(g["dq"]), _p(g["dk"]), _p(g["dv"]), _p(g["dlog_alpha"]),

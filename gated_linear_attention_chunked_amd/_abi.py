@@ -45,6 +45,11 @@ _SIGS = {
     "lizard_hybrid_fwd_varlen": (ctypes.c_int, [ctypes.POINTER(Desc), P, ctypes.c_int32]
                                  + [P] * 13 + [P, ctypes.c_size_t, P]),
     "lizard_hybrid_bwd": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 23 + [P, ctypes.c_size_t, P]),
+    "lizard_hybrid_fwd_segment": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 15
+                                  + [ctypes.c_int32, P, ctypes.c_size_t, P]),
+    "lizard_hybrid_bwd_segment": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 25
+                                  + [ctypes.c_int32] + [P] * 4 + [ctypes.c_int32]
+                                  + [P, ctypes.c_size_t, P]),
     "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P]),
     "lizard_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lizard_version": (ctypes.c_int32, []),

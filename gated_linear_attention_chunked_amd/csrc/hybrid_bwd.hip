@@ -121,6 +121,12 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
       if (e != hipSuccess) return e;
     }
     if (dmix) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, st, dmix, (size_t)1);
+    // no queries see the halo
+    const size_t nh = (size_t)s.B * s.H * s.hlen * s.dk;
+    if (s.dhk && nh > 0) {
+      hipLaunchKernelGGL(zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, s.dhk, nh);
+      hipLaunchKernelGGL(zero_kernel, dim3((nh + 255) / 256), dim3(256), 0, st, s.dhv, nh);
+    }
     return hipGetLastError();
   }
   const size_t bh = (size_t)s.B * s.H, dd = (size_t)s.dk * s.dv;

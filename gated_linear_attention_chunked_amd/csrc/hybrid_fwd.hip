@@ -687,7 +687,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 
 bool hybrid_fused_ok(const Shape& s) {
   return s.dtype == 1 && s.dk == kD && s.dv == kD && s.window >= 1 && s.window <= kMaxW &&
-         s.n_meta <= 16 && s.T > 0;
+         s.n_meta <= 16 && s.T > 0 && s.hlen == 0;
 }
 
 template <bool kSep, typename GT>

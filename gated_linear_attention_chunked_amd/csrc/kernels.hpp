@@ -17,6 +17,19 @@ struct Shape {
   // = tokens cu[b] .. cu[b+1]-1 (device array of B+1), T = the longest length
   const int* cu = nullptr;
   int n_tokens = 0;
+  // window halo (segment-wise runs): the hlen keys and values [B, H, hlen, d]
+  // just before the segment's first token, in order (the window branch's key
+  // space); the backward returns their gradients (dhk, dhv, fp32, nullable) and
+  // adds tdk, tdv [B, H, tlen, d] (fp32: the next segment's halo gradients) to
+  // the gradients of the segment's last tlen keys and values
+  const void* hk = nullptr;
+  const void* hv = nullptr;
+  int hlen = 0;
+  float* dhk = nullptr;
+  float* dhv = nullptr;
+  const float* tdk = nullptr;
+  const float* tdv = nullptr;
+  int tlen = 0;
 };
 
 // GLA branch: o = o_gla; hT (optional) = final state.  ws holds

@@ -125,21 +125,34 @@ lizard_status_t hybrid_fwd_args(const lizard_desc_t* desc, const void* q, const 
 }
 }  // namespace lz
 
-extern "C" {
+namespace {
+// A window halo (segment-wise runs): halo_len in [0, w - 1], both buffers given
+// when it is positive.
+lizard_status_t check_halo(const lizard_desc_t* d, const void* hk, const void* hv, int32_t hlen) {
+  if (hlen < 0 || hlen > d->window - 1) return LIZARD_E_SHAPE;
+  if (hlen > 0 && (!hk || !hv)) return LIZARD_E_NULL;
+  return LIZARD_OK;
+}
 
-lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const void* gate, const void* meta_k,
-                                  const void* meta_v, const float* h0, void* o, float* lse,
-                                  void* o_swa, float* hT, void* ring_k, void* ring_v,
-                                  const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+lizard_status_t hybrid_fwd_impl(const lizard_desc_t* desc, const void* q, const void* k,
+                                const void* v, const void* gate, const void* meta_k,
+                                const void* meta_v, const float* h0, void* o, float* lse,
+                                void* o_swa, float* hT, void* ring_k, void* ring_v,
+                                const void* q_w, const void* k_w, const void* halo_k,
+                                const void* halo_v, int32_t halo_len, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
   lizard_status_t st =
       lz::hybrid_fwd_args(desc, q, k, v, gate, meta_k, meta_v, o, ring_k, ring_v, q_w, k_w);
+  if (st != LIZARD_OK) return st;
+  st = check_halo(desc, halo_k, halo_v, halo_len);
   if (st != LIZARD_OK) return st;
   // the window branch's queries and keys (the same as the GLA branch's by default)
   const void* qw = q_w ? q_w : q;
   const void* kw = k_w ? k_w : k;
-  const Shape s = to_shape(desc);
+  Shape s = to_shape(desc);
+  s.hk = halo_k;
+  s.hv = halo_v;
+  s.hlen = halo_len;
   const size_t need = lz::gla_fwd_workspace_bytes(s);
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
@@ -160,6 +173,31 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
     if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, kw, v, ring_k, ring_v, stream);
   }
   return hip_status(e);
+}
+}  // namespace
+
+extern "C" {
+
+lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const void* gate, const void* meta_k,
+                                  const void* meta_v, const float* h0, void* o, float* lse,
+                                  void* o_swa, float* hT, void* ring_k, void* ring_v,
+                                  const void* q_w, const void* k_w, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return hybrid_fwd_impl(desc, q, k, v, gate, meta_k, meta_v, h0, o, lse, o_swa, hT, ring_k,
+                         ring_v, q_w, k_w, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+lizard_status_t lizard_hybrid_fwd_segment(const lizard_desc_t* desc, const void* q,
+                                          const void* k, const void* v, const void* gate,
+                                          const void* meta_k, const void* meta_v,
+                                          const float* h0, void* o, float* lse, void* o_swa,
+                                          float* hT, const void* q_w, const void* k_w,
+                                          const void* halo_k, const void* halo_v,
+                                          int32_t halo_len, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  return hybrid_fwd_impl(desc, q, k, v, gate, meta_k, meta_v, h0, o, lse, o_swa, hT, nullptr,
+                         nullptr, q_w, k_w, halo_k, halo_v, halo_len, ws, ws_bytes, stream);
 }
 
 lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_t* cu_seqlens,
@@ -199,14 +237,19 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   return hip_status(e);
 }
 
-lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
-                                  const void* v, const void* gate, const void* meta_k,
-                                  const void* meta_v, const float* h0, const void* o_swa,
-                                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                                  float* dgate, float* dmeta_k, float* dmeta_v,
-                                  const float* dhT, float* dh0, float* dmix, const void* q_w,
-                                  const void* k_w, void* dq_w, void* dk_w, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+lizard_status_t hybrid_bwd_impl(const lizard_desc_t* desc, const void* q, const void* k,
+                                const void* v, const void* gate, const void* meta_k,
+                                const void* meta_v, const float* h0, const void* o_swa,
+                                const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                float* dgate, float* dmeta_k, float* dmeta_v, const float* dhT,
+                                float* dh0, float* dmix, const void* q_w, const void* k_w,
+                                void* dq_w, void* dk_w, const void* halo_k, const void* halo_v,
+                                int32_t halo_len, float* dhalo_k, float* dhalo_v,
+                                const float* tail_dk, const float* tail_dv, int32_t tail_len,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
   lizard_status_t st = check_desc(desc, true);
   if (st != LIZARD_OK) return st;
   // separate window queries and keys come with their gradient outputs: all four or none
@@ -217,15 +260,58 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                            !dv || !dgate))
     return LIZARD_E_NULL;
   if (meta && (!meta_k || !meta_v || !dmeta_k || !dmeta_v)) return LIZARD_E_NULL;
-  const Shape s = to_shape(desc);
+  st = check_halo(desc, halo_k, halo_v, halo_len);
+  if (st != LIZARD_OK) return st;
+  if ((dhalo_k == nullptr) != (dhalo_v == nullptr)) return LIZARD_E_NULL;
+  if (tail_len < 0 || tail_len > desc->window - 1 || tail_len > desc->T) return LIZARD_E_SHAPE;
+  if (tail_len > 0 && (!tail_dk || !tail_dv)) return LIZARD_E_NULL;
+  Shape s = to_shape(desc);
   if (!lz::bwd_supported(s)) return LIZARD_E_UNSUPPORTED;
   const size_t need = lz::bwd_workspace_bytes(s);
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  s.hk = halo_k;
+  s.hv = halo_v;
+  s.hlen = halo_len;
+  s.dhk = halo_len > 0 ? dhalo_k : nullptr;
+  s.dhv = halo_len > 0 ? dhalo_v : nullptr;
+  s.tdk = tail_dk;
+  s.tdv = tail_dv;
+  s.tlen = tail_len;
   return hip_status(lz::launch_hybrid_bwd(s, q, k, v, gate, meta_k, meta_v, h0, o_swa, lse,
                                           dO, dq, dk, dv, dgate, dmeta_k, dmeta_v, dhT, dh0,
                                           dmix, q_w, k_w, dq_w, dk_w, ws, stream));
+}
+}  // namespace
+
+extern "C" {
+
+lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
+                                  const void* v, const void* gate, const void* meta_k,
+                                  const void* meta_v, const float* h0, const void* o_swa,
+                                  const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                  float* dgate, float* dmeta_k, float* dmeta_v,
+                                  const float* dhT, float* dh0, float* dmix, const void* q_w,
+                                  const void* k_w, void* dq_w, void* dk_w, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return hybrid_bwd_impl(desc, q, k, v, gate, meta_k, meta_v, h0, o_swa, lse, dO, dq, dk, dv,
+                         dgate, dmeta_k, dmeta_v, dhT, dh0, dmix, q_w, k_w, dq_w, dk_w, nullptr,
+                         nullptr, 0, nullptr, nullptr, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+lizard_status_t lizard_hybrid_bwd_segment(
+    const lizard_desc_t* desc, const void* q, const void* k, const void* v, const void* gate,
+    const void* meta_k, const void* meta_v, const float* h0, const void* o_swa,
+    const float* lse, const void* dO, void* dq, void* dk, void* dv, float* dgate,
+    float* dmeta_k, float* dmeta_v, const float* dhT, float* dh0, float* dmix, const void* q_w,
+    const void* k_w, void* dq_w, void* dk_w, const void* halo_k, const void* halo_v,
+    int32_t halo_len, float* dhalo_k, float* dhalo_v, const float* tail_dk,
+    const float* tail_dv, int32_t tail_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return hybrid_bwd_impl(desc, q, k, v, gate, meta_k, meta_v, h0, o_swa, lse, dO, dq, dk, dv,
+                         dgate, dmeta_k, dmeta_v, dhT, dh0, dmix, q_w, k_w, dq_w, dk_w, halo_k,
+                         halo_v, halo_len, dhalo_k, dhalo_v, tail_dk, tail_dv, tail_len, ws,
+                         ws_bytes, stream);
 }
 
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
     const T* __restrict__ mk, const T* __restrict__ mv, const T* __restrict__ o_swa,
     const float* __restrict__ lse, const T* __restrict__ dO, T* __restrict__ dq,
     float* __restrict__ Dws, float* __restrict__ metap, int T_len, int H, int W, int M,
-    float scale, float mix, int per) {
+    float scale, float mix, int per, const T* __restrict__ hk, const T* __restrict__ hv,
+    int hlen) {
   constexpr int KP = D / 32, NCT = D / 16;
   constexpr int DP = DqSmem<T, D>::DP, TP = DqSmem<T, D>::TP;
   typedef typename Frag<T>::type F;
@@ -180,22 +181,35 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
       }
     }
 
-    // ---- key tiles overlapping [t0 - W + 1, t0 + 63]
+    // ---- key tiles overlapping [t0 - W + 1, t0 + 63]: first the halo's (rows
+    // r at position r - hlen, for queries that reach before the segment), then
+    // the segment's own
+    const int tq0 = t0 + 16 * wave;
+    const int nhalo = (hlen > 0 && t0 < W - 1) ? (hlen - (max(0, t0 - W + 1 + hlen) / kT) * kT + kT - 1) / kT : 0;
     const int first_key = max(0, t0 - W + 1);
     const int last_key = min(T_len - 1, t0 + kT - 1);
-    const int tq0 = t0 + 16 * wave;
-    for (int kt0 = (first_key / kT) * kT; kt0 <= last_key; kt0 += kT) {
+    const int kbeg = (first_key / kT) * kT;
+    const int nmain = last_key >= kbeg ? (last_key - kbeg) / kT + 1 : 0;
+    const Buf bhk(hk + (size_t)bh * hlen * D, (u32)((size_t)hlen * D * sizeof(T)));
+    const Buf bhv(hv + (size_t)bh * hlen * D, (u32)((size_t)hlen * D * sizeof(T)));
+    const int hbeg = (max(0, t0 - W + 1 + hlen) / kT) * kT;
+    for (int it = 0; it < nhalo + nmain; ++it) {
+      const bool halo = it < nhalo;
+      const int kt0 = halo ? hbeg + it * kT : kbeg + (it - nhalo) * kT;
       __syncthreads();
-      stage_rows<T>(&sm.skt[0][0], DP, bk, kt0, D, kT, tid, kThreads);
-      stage_rows<T>(&sm.svt[0][0], DP, bv, kt0, D, kT, tid, kThreads);
-      stage_cols<T>(&sm.skT[0][0], TP, bk, kt0, D, kT, tid, kThreads);
+      stage_rows<T>(&sm.skt[0][0], DP, halo ? bhk : bk, kt0, D, kT, tid, kThreads);
+      stage_rows<T>(&sm.svt[0][0], DP, halo ? bhv : bv, kt0, D, kT, tid, kThreads);
+      stage_cols<T>(&sm.skT[0][0], TP, halo ? bhk : bk, kt0, D, kT, tid, kThreads);
       __syncthreads();
+      // key positions of this tile's rows (halo rows sit before position 0)
+      const int pos0 = halo ? kt0 - hlen : kt0;
+      const int rows = halo ? hlen : T_len;
       f32x4 ds[4];
       bool act[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int s_lo = kt0 + 16 * b;
-        act[b] = (s_lo + 15 >= tq0 - W + 1) && (s_lo <= tq0 + 15) && (s_lo < T_len);
+        const int s_lo = pos0 + 16 * b;
+        act[b] = (s_lo + 15 >= tq0 - W + 1) && (s_lo <= tq0 + 15) && (kt0 + 16 * b < rows);
         ds[b] = zero;
         if (act[b]) {
           f32x4 sc = zero, dp = zero;
@@ -207,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int sk = s_lo + 4 * g + r;
-            const bool ok = (sk <= tq) && (sk > tq - W) && (tq < T_len);
+            const bool ok = (sk <= tq) && (sk > tq - W) && (tq < T_len) &&
+                            (kt0 + 16 * b + 4 * g + r < rows);
             const float pr = ok ? exp2_fast(sc[r] * sl2 - lse2) : 0.f;
             ds[b][r] = pr * (mix * dp[r] - Dt);
           }
@@ -242,11 +257,17 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
 }
 
 // ----------------------------------------------------------------- 2. dk, dv
-template <typename T, int D>
+// Keys are rows of k, v [B*H, nrows, D] at positions row + kpos (kpos = 0 for
+// the segment's own keys, -hlen for the halo); queries are the segment's.  OT is
+// the output type (the problem's for the segment, fp32 for the halo).  tdk, tdv
+// (nullable, [B*H, tlen, D] fp32) are added to the gradients of the last tlen
+// rows.
+template <typename T, int D, typename OT = T>
 __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ Dws,
-    T* __restrict__ dk, T* __restrict__ dv, int T_len, int W, float scale, float mix) {
+    OT* __restrict__ dk, OT* __restrict__ dv, int T_len, int W, float scale, float mix,
+    int nrows, int kpos, const float* __restrict__ tdk, const float* __restrict__ tdv, int tlen) {
   constexpr int KP = D / 32, NCT = D / 16;
   constexpr int DP = D + 8, TP = kT + 8;
   typedef typename Frag<T>::type F;
@@ -260,20 +281,22 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
   const int ntile = gridDim.x;
   const int logical = xcd_remap(blockIdx.y * ntile + blockIdx.x, ntile * gridDim.y);
   const int bh = logical / ntile;
-  const int s0 = (logical % ntile) * kT;
+  const int s0 = (logical % ntile) * kT + kpos;  // position of the tile's first key
   const int sk0 = s0 + 16 * wave;      // first key of this wave
   const int sk = sk0 + r16;            // this lane's key (column of the S tiles)
+  const int krow = sk - kpos;          // its row in k, v
   const size_t off = (size_t)bh * T_len * D;
+  const size_t koff = (size_t)bh * nrows * D;
   const u32 nb = (u32)((size_t)T_len * D * sizeof(T));
   const Buf bq(q + off, nb), bdo(dO + off, nb);
   const float sl2 = scale * kLog2e;
 
   F kf[KP], vf[KP];
-  const int skl = min(sk, T_len - 1);
+  const int skl = min(krow, nrows - 1);
 #pragma unroll
   for (int p = 0; p < KP; ++p) {
-    kf[p] = ld8<T>(k + off + (size_t)skl * D + 32 * p + 8 * g);
-    vf[p] = ld8<T>(v + off + (size_t)skl * D + 32 * p + 8 * g);
+    kf[p] = ld8<T>(k + koff + (size_t)skl * D + 32 * p + 8 * g);
+    vf[p] = ld8<T>(v + koff + (size_t)skl * D + 32 * p + 8 * g);
   }
   f32x4 dkT[NCT], dvT[NCT];  // [c or j = 16ct + 4g + r][key r16]
 #pragma unroll
@@ -282,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
     dvT[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int last_q = min(T_len - 1, s0 + kT - 1 + W - 1);
-  for (int qt0 = s0; qt0 <= last_q; qt0 += kT) {
+  for (int qt0 = max(s0, 0); qt0 <= last_q; qt0 += kT) {
     __syncthreads();
     stage_rows<T>(&sq[0][0], DP, bq, qt0, D, kT, tid, kThreads);
     stage_rows<T>(&sdo[0][0], DP, bdo, qt0, D, kT, tid, kThreads);
@@ -312,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tl = 16 * qb + 4 * g + r, t = qt0 + tl;
-          const bool ok = (sk <= t) && (t < sk + W) && (t < T_len) && (sk < T_len);
+          const bool ok = (sk <= t) && (t < sk + W) && (t < T_len) && (krow < nrows);
           const float pr = ok ? exp2_fast(sc[r] * sl2 - slse[tl]) : 0.f;
           P[qb][r] = pr;
           dS[qb][r] = pr * (mix * dp[r] - sD[tl]);
@@ -332,11 +355,18 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
       }
     }
   }
-  if (sk < T_len) {
+  if (krow < nrows) {
+    const int trow = krow - (nrows - tlen);  // row of the added gradients, if >= 0
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      st4<T>(dk + off + (size_t)sk * D + 16 * ct + 4 * g, dkT[ct] * scale);
-      st4<T>(dv + off + (size_t)sk * D + 16 * ct + 4 * g, dvT[ct] * mix);
+      f32x4 gk = dkT[ct] * scale, gv = dvT[ct] * mix;
+      if (tdk && trow >= 0) {
+        const size_t to = ((size_t)bh * tlen + trow) * D + 16 * ct + 4 * g;
+        gk += *reinterpret_cast<const f32x4*>(tdk + to);
+        gv += *reinterpret_cast<const f32x4*>(tdv + to);
+      }
+      st4<OT>(dk + koff + (size_t)krow * D + 16 * ct + 4 * g, gk);
+      st4<OT>(dv + koff + (size_t)krow * D + 16 * ct + 4 * g, gv);
     }
   }
 }
@@ -789,7 +819,7 @@ hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, co
   const int per = (nqt + G - 1) / G;
   G = (nqt + per - 1) / per;
   if constexpr (sizeof(T) == 2 && D == 64) {
-    if (s.window <= 65) {
+    if (s.window <= 65 && s.hlen == 0 && s.tlen == 0) {
       // streaming form: B*H*G work-groups, G segments of whole tiles per sequence
       hipLaunchKernelGGL(swa_bwd_stream, dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa,
@@ -804,10 +834,15 @@ hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, co
   hipLaunchKernelGGL((swa_bwd_dq<T, D>), dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa, lse,
                      (const T*)dO, (T*)dq, Dws, metap, s.T, s.H, s.window, s.n_meta, s.scale,
-                     s.mix, per);
+                     s.mix, per, (const T*)s.hk, (const T*)s.hv, s.hlen);
   hipLaunchKernelGGL((swa_bwd_dkdv<T, D>), dim3(nqt, BH), dim3(kThreads), 0, st, (const T*)q,
                      (const T*)k, (const T*)v, lse, (const T*)dO, Dws, (T*)dk, (T*)dv, s.T,
-                     s.window, s.scale, s.mix);
+                     s.window, s.scale, s.mix, s.T, 0, s.tdk, s.tdv, s.tlen);
+  if (s.hlen > 0 && s.dhk)
+    hipLaunchKernelGGL((swa_bwd_dkdv<T, D, float>), dim3((s.hlen + kT - 1) / kT, BH),
+                       dim3(kThreads), 0, st, (const T*)q, (const T*)s.hk, (const T*)s.hv, lse,
+                       (const T*)dO, Dws, s.dhk, s.dhv, s.T, s.window, s.scale, s.mix, s.hlen,
+                       -s.hlen, (const float*)nullptr, (const float*)nullptr, 0);
   if (s.n_meta > 0)
     hipLaunchKernelGGL(swa_meta_reduce<D>, dim3(s.H, (2 * s.n_meta * D + 63) / 64),
                        dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);

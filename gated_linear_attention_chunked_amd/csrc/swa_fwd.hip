@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ mk, const T* __restrict__ mv, T* __restrict__ o,
     T* __restrict__ o_swa, float* __restrict__ lse, int T_arg, int H, int W, int M,
-    float scale_log2, float out_scale, int accumulate, const int* __restrict__ cu, int N) {
+    float scale_log2, float out_scale, int accumulate, const int* __restrict__ cu, int N,
+    const T* __restrict__ hk, const T* __restrict__ hv, int hlen) {
   constexpr int KS = DK / 32;
   constexpr int NT = DV / 16;
   typedef typename Frag<T>::type F;
@@ -166,6 +167,42 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(
     for (int r = 0; r < 4; ++r)
       P[0][r] = (4 * g + r < M) ? P[0][r] * scale_log2 : -INFINITY;
     softmax_pv(P, act, 2, &sm.mvT[0][0], 32 + 8);
+  }
+
+  // ---- halo: the hlen keys before the segment, row r at position r - hlen,
+  // visible to query tq when r - hlen > tq - W
+  if (hlen > 0 && t0 < W - 1) {
+    const Buf bhk(hk + (size_t)bh * hlen * DK, (u32)((size_t)hlen * DK * sizeof(T)));
+    const Buf bhv(hv + (size_t)bh * hlen * DV, (u32)((size_t)hlen * DV * sizeof(T)));
+    const int first = max(0, t0 - W + 1 + hlen);
+    for (int kt0 = (first / kKT) * kKT; kt0 < hlen; kt0 += kKT) {
+      __syncthreads();
+      stage_rows(&sm.kt[0][0], SwaSmem<T, DK, DV>::DKP, bhk, kt0, DK, kKT);
+      stage_cols(&sm.vT[0][0], kKT + 8, bhv, kt0, DV, kKT);
+      __syncthreads();
+      f32x4 P[4];
+      bool act[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int s_lo = kt0 + 16 * b;
+        act[b] = (s_lo < hlen) && (s_lo + 15 - hlen > tq0 - W);
+        P[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (act[b]) {
+#pragma unroll
+          for (int p = 0; p < KS; ++p) {
+            F af = ld8<T>(&sm.kt[16 * b + r16][32 * p + 8 * g]);
+            mma(P[b], af, qf[p]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = s_lo + 4 * g + r;
+            const bool ok = (row < hlen) && (row - hlen > tq - W);
+            P[b][r] = ok ? P[b][r] * scale_log2 : -INFINITY;
+          }
+        }
+      }
+      softmax_pv(P, act, 4, &sm.vT[0][0], kKT + 8);
+    }
   }
 
   // ---- key tiles overlapping [t0 - W + 1, t0 + 63]
@@ -532,7 +569,7 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
   // for LDS in fp32 at D = 128, which takes the tiled kernel for every window
   constexpr bool kRing = !(sizeof(T) == 4 && D == 128);
   if constexpr (kRing) {
-  if (s.window <= 2 * kKT + 1) {
+  if (s.window <= 2 * kKT + 1 && s.hlen == 0) {
     // streaming form: runs of query tiles, enough work-groups to fill the chip
     const int nc = (s.T + kKT - 1) / kKT;
     const long long bh = (long long)s.B * s.H;
@@ -559,7 +596,8 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
   dim3 grid((s.T + kQT - 1) / kQT, s.B * s.H);
   hipLaunchKernelGGL((swa_fwd_kernel<T, D, D>), grid, dim3(256), 0, st, (const T*)q, (const T*)k,
                      (const T*)v, (const T*)mk, (const T*)mv, (T*)o, (T*)o_swa, lse, s.T, s.H,
-                     s.window, s.n_meta, s.scale * kLog2e, out_scale, acc, s.cu, s.n_tokens);
+                     s.window, s.n_meta, s.scale * kLog2e, out_scale, acc, s.cu, s.n_tokens,
+                     (const T*)s.hk, (const T*)s.hv, s.hlen);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && rk) e = launch_ring_fill(s, k, v, rk, rv, st);
   return e;

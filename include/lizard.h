@@ -207,6 +207,48 @@ lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, cons
                                   const void* k_w, void* dq_w, void* dk_w, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
+/* Segment-wise runs of a long sequence (training over contexts far longer than
+ * one call should hold, e.g. 32k-64k tokens): the sequence is cut into segments
+ * run one after another, the gated branch chained through its constant-size
+ * state (hT of a segment as h0 of the next, dh0 of a segment as dhT of the one
+ * before), which is what the constant-memory claims of "Lizard: An Efficient
+ * Linearization Framework for Large Language Models" (gist.science summary,
+ * sections 2(a), 3 and 4 "Efficiency") rest on.  The window branch of a segment
+ * also needs the w-1 keys and values before its first token, its halo:
+ *   halo_k, halo_v [B, H, halo_len, d] (desc->dtype): the halo_len tokens just
+ *     before the segment, oldest first (keys in the window branch's key space:
+ *     k_w when given, else k); 0 <= halo_len <= w-1, both non-NULL when
+ *     halo_len > 0 (else LIZARD_E_NULL; a halo_len out of range:
+ *     LIZARD_E_SHAPE).  halo_len = min(w-1, tokens before the segment) makes
+ *     every output equal that of one call on the whole sequence.
+ * lizard_hybrid_fwd_segment: lizard_hybrid_fwd with a halo (no window cache
+ *   output; the other arguments and outputs as there).
+ * lizard_hybrid_bwd_segment: lizard_hybrid_bwd with the same halo, plus
+ *   dhalo_k, dhalo_v [B, H, halo_len, d] float32 (both or neither; nullable):
+ *     receive the loss gradient with respect to the halo keys and values;
+ *   tail_dk, tail_dv [B, H, tail_len, d] float32: gradients with respect to
+ *     this segment's last tail_len window keys and values coming from the next
+ *     segment (that segment's dhalo), added into dk (or dk_w) and dv;
+ *     0 <= tail_len <= min(w-1, T), both non-NULL when tail_len > 0.
+ * Segments run last to first in the backward, passing dh0 -> dhT and
+ * dhalo -> tail; the meta-memory gradients of the segments add up. */
+lizard_status_t lizard_hybrid_fwd_segment(const lizard_desc_t* desc, const void* q,
+                                          const void* k, const void* v, const void* gate,
+                                          const void* meta_k, const void* meta_v,
+                                          const float* h0, void* o, float* lse, void* o_swa,
+                                          float* hT, const void* q_w, const void* k_w,
+                                          const void* halo_k, const void* halo_v,
+                                          int32_t halo_len, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+lizard_status_t lizard_hybrid_bwd_segment(
+    const lizard_desc_t* desc, const void* q, const void* k, const void* v, const void* gate,
+    const void* meta_k, const void* meta_v, const float* h0, const void* o_swa,
+    const float* lse, const void* dO, void* dq, void* dk, void* dv, float* dgate,
+    float* dmeta_k, float* dmeta_v, const float* dhT, float* dh0, float* dmix, const void* q_w,
+    const void* k_w, void* dq_w, void* dk_w, const void* halo_k, const void* halo_v,
+    int32_t halo_len, float* dhalo_k, float* dhalo_v, const float* tail_dk,
+    const float* tail_dv, int32_t tail_len, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* One constant-memory generation step for B sequences (desc->T is ignored): the
  * recurrent form of both branches, as the constant-memory inference of "Lizard:
  * An Efficient Linearization Framework for Large Language Models" (gist.science

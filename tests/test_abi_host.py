@@ -195,3 +195,26 @@ def test_static_scratch_entry_checks_arguments_first():
     worst = max(lib.lizard_workspace_bytes(ctypes.byref(desc(B=1, H=h, T=65536, dk=128, dv=128)), 2)
                 for h in range(1, 300))
     assert 0 < worst <= _abi.STATIC_SCRATCH_BYTES
+
+
+def test_segment_entry_points_check_halo_and_tail():
+    lib = _abi.lib()
+    d = desc(T=128, window=64)
+    need_f = lib.lizard_workspace_bytes(ctypes.byref(d), 2)
+    need_b = lib.lizard_workspace_bytes(ctypes.byref(d), 3)
+    fwd = lambda hk, hv, n: lib.lizard_hybrid_fwd_segment(ctypes.byref(d), *([FAKE] * 11), None,
+                                                          None, hk, hv, n, FAKE, need_f, None)
+    assert fwd(FAKE, FAKE, 64) == 2   # a halo longer than w - 1
+    assert fwd(FAKE, FAKE, -1) == 2
+    assert fwd(None, FAKE, 10) == 1   # halo tokens without keys
+    bwd = lambda hlen, dh, tl, tail: lib.lizard_hybrid_bwd_segment(
+        ctypes.byref(d), *([FAKE] * 19), None, None, None, None, FAKE, FAKE, hlen, dh[0], dh[1],
+        tail, tail, tl, FAKE, need_b, None)
+    assert bwd(64, (None, None), 0, None) == 2
+    assert bwd(10, (FAKE, None), 0, None) == 1      # one halo gradient without the other
+    assert bwd(0, (None, None), 64, FAKE) == 2      # tail longer than w - 1
+    assert bwd(0, (None, None), 10, None) == 1      # tail length without the gradients
+    d2 = desc(T=8, window=64)
+    assert lib.lizard_hybrid_bwd_segment(
+        ctypes.byref(d2), *([FAKE] * 19), None, None, None, None, None, None, 0, None, None,
+        FAKE, FAKE, 9, FAKE, 1 << 30, None) == 2    # tail longer than the segment
