@@ -9,7 +9,9 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblizard.so")
+# LIZARD_LIB may name another build of the same library (e.g. the host-sanitizer
+# build of build_sanitize.py); by default the in-tree liblizard.so is loaded
+LIB_PATH = os.environ.get("LIZARD_LIB") or os.path.join(HERE, "liblizard.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "lizard.h")
 
 LIZARD_F32, LIZARD_BF16 = 0, 1

@@ -3,6 +3,8 @@
 #include "../../include/lizard.h"
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 #include "kernels.hpp"
 
@@ -50,13 +52,35 @@ Shape to_shape(const lizard_desc_t* d) {
 
 bool has_tokens(const lizard_desc_t* d) { return (long long)d->B * d->H * d->T > 0; }
 
-lizard_status_t hip_status(hipError_t e) { return e == hipSuccess ? LIZARD_OK : LIZARD_E_HIP; }
+// LIZARD_SYNC_DEBUG=1 in the environment (read once): every call waits for its
+// work on the stream to finish and reports an asynchronous failure of it as
+// LIZARD_E_HIP, so a fault is tied to the call that caused it.
+bool sync_debug() {
+  static const bool on = [] {
+    const char* v = std::getenv("LIZARD_SYNC_DEBUG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+lizard_status_t hip_status(hipError_t e, hipStream_t stream) {
+  if (e == hipSuccess && sync_debug()) {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  return e == hipSuccess ? LIZARD_OK : LIZARD_E_HIP;
+}
 
 }  // namespace
 
 extern "C" {
 
-const char* lizard_status_str(lizard_status_t s) {
+const char* lizard_status_str(lizard_status_t status) {
+  // A C caller may pass any int; its bytes are read as an int, since loading an
+  // out-of-range value through the enum type is undefined in C++.
+  int s;
+  static_assert(sizeof(s) == sizeof(status), "the status enum is int-sized");
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case LIZARD_OK: return "ok";
     case LIZARD_E_NULL: return "a required pointer is NULL";
@@ -91,7 +115,7 @@ lizard_status_t lizard_gla_fwd(const lizard_desc_t* desc, const void* q, const v
   if (ws_bytes < need) return LIZARD_E_WORKSPACE;
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
-  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, gate, h0, o, hT, ws, stream));
+  return hip_status(lz::launch_gla_fwd(to_shape(desc), q, k, v, gate, h0, o, hT, ws, stream), stream);
 }
 
 lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const void* k,
@@ -104,7 +128,7 @@ lizard_status_t lizard_swa_fwd(const lizard_desc_t* desc, const void* q, const v
   if (!has_tokens(desc)) return LIZARD_OK;
   return hip_status(
       lz::launch_swa_fwd(to_shape(desc), q, k, v, meta_k, meta_v, o, 1.0f, 0, nullptr, lse,
-                         nullptr, nullptr, stream));
+                         nullptr, nullptr, stream), stream);
 }
 
 }  // extern "C"
@@ -172,7 +196,7 @@ lizard_status_t hybrid_fwd_impl(const lizard_desc_t* desc, const void* q, const 
     if (hT) e = lz::launch_state_copy(s, h0, hT, stream);
     if (e == hipSuccess && ring_k) e = lz::launch_ring_fill(s, kw, v, ring_k, ring_v, stream);
   }
-  return hip_status(e);
+  return hip_status(e, stream);
 }
 }  // namespace
 
@@ -228,13 +252,13 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   s.n_tokens = n_tokens;
   if (lz::hybrid_fused_ok(s))
     return hip_status(lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o,
-                                              hT, ring_k, ring_v, ws, stream));
+                                              hT, ring_k, ring_v, ws, stream), stream);
   // other shapes: the GLA branch writes o, the window branch adds mix * o_swa
   hipError_t e = lz::launch_gla_fwd(s, q, k, v, gate, h0, o, hT, ws, stream);
   if (e == hipSuccess)
     e = lz::launch_swa_fwd(s, q_w ? q_w : q, k_w ? k_w : k, v, meta_k, meta_v, o, s.mix, 1,
                            nullptr, nullptr, ring_k, ring_v, stream);
-  return hip_status(e);
+  return hip_status(e, stream);
 }
 
 }  // extern "C"
@@ -281,7 +305,7 @@ lizard_status_t hybrid_bwd_impl(const lizard_desc_t* desc, const void* q, const 
   s.tlen = tail_len;
   return hip_status(lz::launch_hybrid_bwd(s, q, k, v, gate, meta_k, meta_v, h0, o_swa, lse,
                                           dO, dq, dk, dv, dgate, dmeta_k, dmeta_v, dhT, dh0,
-                                          dmix, q_w, k_w, dq_w, dk_w, ws, stream));
+                                          dmix, q_w, k_w, dq_w, dk_w, ws, stream), stream);
 }
 }  // namespace
 
@@ -332,7 +356,7 @@ lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, con
   if (desc->H >= (1 << 22)) return LIZARD_E_UNSUPPORTED;
   return hip_status(lz::launch_decode(to_shape(desc), q, k, q_w ? q_w : q, k_w ? k_w : k, v,
                                       gate, state, ring_k, ring_v, pos, meta_k, meta_v, o,
-                                      stream));
+                                      stream), stream);
 }
 
 }  // extern "C"

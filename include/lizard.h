@@ -45,6 +45,10 @@
  *   - Arguments are checked on the host before anything is enqueued; a failed
  *     check returns a non-zero status and enqueues nothing.  A launch failure
  *     returns LIZARD_E_HIP.  NaN/Inf inputs propagate to the outputs.
+ *   - With LIZARD_SYNC_DEBUG=1 in the environment (read once per process),
+ *     every call waits for its work on `stream` to finish and returns
+ *     LIZARD_E_HIP if that work failed, so an asynchronous fault is reported
+ *     by the call that caused it (for debugging; it serialises the stream).
  *   - Supported in this version: dk == dv, dk in {64, 128}, chunk == 64,
  *     window >= 1, 0 <= M <= 16, T >= 0 with T*dk*4 < 2^31, B*H <= 65535;
  *     dtype BF16 or F32 for dk in {64, 128}.  Output gradients dq, dk, dv use
