@@ -1,5 +1,5 @@
 // Gated linear attention backward, generic form: bf16 at d = 128 and fp32 at
-// d = 64 (bf16 at d = 64 has its own tuned kernels in gla_bwd.hip).
+// d = 64 and 128 (bf16 at d = 64 has its own tuned kernels in gla_bwd.hip).
 //
 // Same mathematics as gla_bwd.hip (reverse mode of the chunked recurrence of
 // "Lizard: An Efficient Linearization Framework for Large Language Models",
@@ -159,17 +159,23 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scan_gen(
 }
 
 // --------------------------------------------------- per-chunk gradients
+// fp32 at D = 128 ("lean"): the ungated operands (dO and v rows, dO^T, dS^T)
+// are read from global memory (L2) instead of LDS, so the gated tiles fit.
+template <typename T, int D>
+constexpr bool kLean = sizeof(T) == 4 && D == 128;
+
 template <typename T, int D>
 struct GenSmem {
   static constexpr int TL = kC * D;  // elements of a [64][D] (or [D][64]) tile
+  static constexpr int TU = kLean<T, D> ? 8 : TL;  // the tiles a lean kernel does not keep
   T qg[TL];    // q~ rows [t][c] = q_t 2^{b_t - R_i}
   T kg[TL];    // k~ rows [s][c] = k_s 2^{R_j - b_s}
-  T dor[TL];   // dO rows [t][j]
-  T vr[TL];    // v rows [s][j]
+  T dor[TU];   // dO rows [t][j]
+  T vr[TU];    // v rows [s][j]
   T qgT[TL];   // q~ transposed [c][split_pos(t)]
   T kgT[TL];   // k~ transposed [c][split_pos(s)]
-  T doT[TL];   // dO transposed [j][split_pos(t)]
-  T dST[D * D];  // dS_{c+1} transposed [j][c]
+  T doT[TU];   // dO transposed [j][split_pos(t)]
+  T dST[kLean<T, D> ? 8 : D * D];  // dS_{c+1} transposed [j][c]
   float tot_sx[4][D];  // per-block gate totals; later the suffix totals of dlog_alpha
   float R_sy[4][D];    // sub-block midpoints; later the prefix totals of dlog_alpha
   float Ru[4][D];      // references in use: the midpoints, or 0 on the single-reference path
@@ -229,6 +235,54 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
   const u32 rowe = (u32)(t0 + t) * D;  // element offset of this lane's token row
   const int ts = split_pos(t);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  constexpr bool lean = kLean<T, D>;
+  // fragments of the ungated operands: from LDS, or (lean) from global memory
+  // through the buffer views (rows past T read as zero)
+  auto gfrag = [&](const Buf& b, int row, int col) {  // 8 fp32 elements of row `row` of the chunk
+    F f{};
+    if constexpr (lean) {
+      const u32 off = (u32)((t0 + row) * D + col) * 4u;
+      const u32x4 a = b.ld128(off), c = b.ld128(off + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = as_f(a[e]);
+        f[e + 4] = as_f(c[e]);
+      }
+    }
+    return f;
+  };
+  auto frag_dor = [&](int row, int col) {
+    if constexpr (lean) return gfrag(bdo, row, col);
+    else return ld8<T>(&sm.dor[at_r<D>(row, col)]);
+  };
+  auto frag_vr = [&](int row, int col) {
+    if constexpr (lean) return gfrag(bv, row, col);
+    else return ld8<T>(&sm.vr[at_r<D>(row, col)]);
+  };
+  // dO^T[j][tokens at split positions col..col+7]
+  auto frag_doT = [&](int j, int col) {
+    if constexpr (lean) {
+      F f{};
+      const int tb = (col & ~31) + 4 * ((col >> 3) & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = as_f(bdo.ld32((u32)((t0 + tb + (e & 3) + 16 * (e >> 2)) * D + j) * 4u));
+      return f;
+    } else {
+      return ld8<T>(&sm.doT[at_t(j, col)]);
+    }
+  };
+  // dS_{c+1}^T[j][c..c+7] = dS_{c+1}[c..c+7][j]
+  auto frag_dST = [&](int j, int c) {
+    if constexpr (lean) {
+      F f{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = to_f(dSg[(size_t)(c + e) * D + j]);
+      return f;
+    } else {
+      return ld8<T>(&sm.dST[at_r<D>(j, c)]);
+    }
+  };
 
   // ---- 0. this lane's token row: gates, q, k; dO and v into their tiles
   float b[NCT][4];
@@ -245,18 +299,22 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
     Row4<T> d4, v4;
     d4.load(bdo, e);
     v4.load(bv, e);
-    const int c = 16 * ct + 4 * g;
-    st4<T>(&sm.dor[at_r<D>(t, c)], row4_f(d4));
-    st4<T>(&sm.vr[at_r<D>(t, c)], row4_f(v4));
+    if constexpr (!lean) {
+      const int c = 16 * ct + 4 * g;
+      st4<T>(&sm.dor[at_r<D>(t, c)], row4_f(d4));
+      st4<T>(&sm.vr[at_r<D>(t, c)], row4_f(v4));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.doT[at_t(c + r, ts)] = to_t<T>(d4.at(r));
+      for (int r = 0; r < 4; ++r) sm.doT[at_t(c + r, ts)] = to_t<T>(d4.at(r));
+    }
   }
   // dS_{c+1} transposed into LDS: row c of the workspace state, 8 columns at a time
-  for (int e = tid; e < D * D / 8; e += kThreads) {
-    const int c = e / (D / 8), j0 = 8 * (e % (D / 8));
-    const F x = ld8<T>(dSg + (size_t)c * D + j0);
+  if constexpr (!lean) {
+    for (int e = tid; e < D * D / 8; e += kThreads) {
+      const int c = e / (D / 8), j0 = 8 * (e % (D / 8));
+      const F x = ld8<T>(dSg + (size_t)c * D + j0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sm.dST[at_r<D>(j0 + i, c)] = x[i];
+      for (int i = 0; i < 8; ++i) sm.dST[at_r<D>(j0 + i, c)] = x[i];
+    }
   }
 
   // ---- 1. gate cumsum within each 16-token block
@@ -341,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
   {
     F dof[KP];
 #pragma unroll
-    for (int p = 0; p < KP; ++p) dof[p] = ld8<T>(&sm.dor[at_r<D>(t, 32 * p + 8 * g)]);
+    for (int p = 0; p < KP; ++p) dof[p] = frag_dor(t, 32 * p + 8 * g);
     f32x4 dAT[4];  // dA^T[s = 16j + 4g + r][t], strictly s < t
     float dAtt = 0.f;
 #pragma unroll
@@ -350,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
       if (j <= w) {
 #pragma unroll
         for (int p = 0; p < KP; ++p)
-          mma(dAT[j], ld8<T>(&sm.vr[at_r<D>(16 * j + r16, 32 * p + 8 * g)]), dof[p]);
+          mma(dAT[j], frag_vr(16 * j + r16, 32 * p + 8 * g), dof[p]);
         if (j == w) {
           dAtt = __shfl(dAT[j][r16 & 3], 16 * (r16 >> 2) + r16);
 #pragma unroll
@@ -413,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
     F vf[KP], kf[KP];
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
-      vf[p] = ld8<T>(&sm.vr[at_r<D>(t, 32 * p + 8 * g)]);
+      vf[p] = frag_vr(t, 32 * p + 8 * g);
       kf[p] = ld8<T>(&sm.kg[at_r<D>(t, 32 * p + 8 * g)]);
     }
     f32x4 dA[4], Ab[4];  // [t = 16i + 4g + r][s]; dA strictly t > s, A with t >= s
@@ -425,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
       if (i >= w) {
 #pragma unroll
         for (int p = 0; p < KP; ++p) {
-          mma(dA[i], ld8<T>(&sm.dor[at_r<D>(16 * i + r16, 32 * p + 8 * g)]), vf[p]);
+          mma(dA[i], frag_dor(16 * i + r16, 32 * p + 8 * g), vf[p]);
           F af = ld8<T>(&sm.qg[at_r<D>(16 * i + r16, 32 * p + 8 * g)]);
           if (i > w && !fast) {
             const float* f = &sm.vij[pair_of(i, w)][32 * p + 8 * g];
@@ -492,9 +550,9 @@ __global__ __launch_bounds__(kThreads, 1) void gla_bwd_chunk_gen(
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
         if (2 * pp + 1 >= w)
-          mma(acc, ld8<T>(&sm.doT[at_t(jl, 32 * pp + 8 * g)]), pack_acc<T>(Ab[2 * pp], Ab[2 * pp + 1]));
+          mma(acc, frag_doT(jl, 32 * pp + 8 * g), pack_acc<T>(Ab[2 * pp], Ab[2 * pp + 1]));
 #pragma unroll
-      for (int p = 0; p < KP; ++p) mma(acc, ld8<T>(&sm.dST[at_r<D>(jl, 32 * p + 8 * g)]), kh[p]);
+      for (int p = 0; p < KP; ++p) mma(acc, frag_dST(jl, 32 * p + 8 * g), kh[p]);
       if (live) {
         T* dst = dv + off + rowe + 16 * jt + 4 * g;
         st4<T>(dst, acc + ld4f<T>(dst));
@@ -576,6 +634,9 @@ hipError_t launch_gla_bwd_block_gen(const Shape& s, const void* q, const void* k
     else
       launch_gen<bf16, 128, float>(s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv,
                                    dla, S_ws, dS_ws, add_qk, c0, c1, L, st);
+  } else if (s.dk == 128) {
+    launch_gen<float, 128, float>(s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv,
+                                  dla, S_ws, dS_ws, add_qk, c0, c1, L, st);
   } else {
     launch_gen<float, 64, float>(s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv,
                                  dla, S_ws, dS_ws, add_qk, c0, c1, L, st);

@@ -94,7 +94,7 @@ size_t gla_bwd_workspace_bytes(const Shape& s) {
 
 bool bwd_supported(const Shape& s) {
   if (s.dk != s.dv) return false;
-  return (s.dtype == 1 && (s.dk == 64 || s.dk == 128)) || (s.dtype == 0 && s.dk == 64);
+  return s.dk == 64 || s.dk == 128;
 }
 
 size_t bwd_workspace_bytes(const Shape& s) {

@@ -78,7 +78,7 @@ hipError_t launch_decode(const Shape& s, const void* q, const void* k, const voi
                          void* ring_k, void* ring_v, int64_t* pos, const void* mk, const void* mv,
                          void* o, hipStream_t st);
 
-// Backward (bf16 at dk = dv = 64 or 128, fp32 at 64).  The workspace (owned by
+// Backward (bf16 or fp32, dk = dv = 64 or 128).  The workspace (owned by
 // hybrid_bwd, gla_bwd and swa_bwd) does not depend on T.  qw, kw, dqw, dkw:
 // separate window queries and keys and their gradients (all null: shared).
 bool bwd_supported(const Shape& s);

@@ -24,6 +24,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lz {
 namespace {
@@ -38,17 +39,34 @@ constexpr int kThreads = 256;
 // tile's D_t (kept for the dk/dv kernel in Dws), the meta-slot terms of dq and
 // of the meta gradients (summed over the segment's tiles in LDS), then dq over
 // the key tiles that the window reaches.
+// fp32 at D = 128 does not fit with every tile apart: there the query tiles
+// (used only by the meta-slot terms, before the key loop) share their LDS with
+// the key and value rows (used only in the key loop), and rows are padded less.
 template <typename T, int D>
 struct DqSmem {
-  static constexpr int DP = D + 8, TP = kT + 8;
-  T skt[kT][DP];   // key tile, row-major
-  T svt[kT][DP];   // value tile, row-major
+  static constexpr bool kShare = sizeof(T) == 4 && D == 128;
+  static constexpr int DP = D + 8, TP = kT + (kShare ? 4 : 8);
+  struct KeyRows {
+    T skt[kT][DP];   // key tile, row-major
+    T svt[kT][DP];   // value tile, row-major
+  };
+  struct QueryCols {
+    T sqT[D][TP];    // this tile's queries, transposed
+    T sdoT[D][TP];   // this tile's dO, transposed
+  };
+  struct Apart {
+    KeyRows kr;
+    QueryCols qc;
+  };
+  union Shared {
+    KeyRows kr;
+    QueryCols qc;
+  };
+  typename std::conditional<kShare, Shared, Apart>::type u;
   T skT[D][TP];    // key tile, transposed
   T smk[16][DP];
   T smv[16][DP];
   T smkT[D][40];   // meta keys transposed (slots 16..31 zero)
-  T sqT[D][TP];    // this tile's queries, transposed
-  T sdoT[D][TP];   // this tile's dO, transposed
   float slse[kT], sD[kT];
   float red[2 * D][17];  // meta-gradient sums of the segment: [c or D + j][slot]
 };
@@ -118,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
 
     // ---- meta slots
     if (M > 0) {
-      stage_cols<T>(&sm.sqT[0][0], TP, bq, t0, D, kT, tid, kThreads);
-      stage_cols<T>(&sm.sdoT[0][0], TP, bdo, t0, D, kT, tid, kThreads);
+      stage_cols<T>(&sm.u.qc.sqT[0][0], TP, bq, t0, D, kT, tid, kThreads);
+      stage_cols<T>(&sm.u.qc.sdoT[0][0], TP, bdo, t0, D, kT, tid, kThreads);
       __syncthreads();
       // transposed orientation (lane <-> query) for dq
       f32x4 sc = zero, dp = zero;
@@ -162,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
             F aq, ao;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              aq[e] = sm.sqT[16 * ct + r16][16 * wave + 4 * g + e];
-              ao[e] = sm.sdoT[16 * ct + r16][16 * wave + 4 * g + e];
+              aq[e] = sm.u.qc.sqT[16 * ct + r16][16 * wave + 4 * g + e];
+              ao[e] = sm.u.qc.sdoT[16 * ct + r16][16 * wave + 4 * g + e];
               aq[e + 4] = to_t<T>(0.f);
               ao[e + 4] = to_t<T>(0.f);
             }
@@ -197,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
       const bool halo = it < nhalo;
       const int kt0 = halo ? hbeg + it * kT : kbeg + (it - nhalo) * kT;
       __syncthreads();
-      stage_rows<T>(&sm.skt[0][0], DP, halo ? bhk : bk, kt0, D, kT, tid, kThreads);
-      stage_rows<T>(&sm.svt[0][0], DP, halo ? bhv : bv, kt0, D, kT, tid, kThreads);
+      stage_rows<T>(&sm.u.kr.skt[0][0], DP, halo ? bhk : bk, kt0, D, kT, tid, kThreads);
+      stage_rows<T>(&sm.u.kr.svt[0][0], DP, halo ? bhv : bv, kt0, D, kT, tid, kThreads);
       stage_cols<T>(&sm.skT[0][0], TP, halo ? bhk : bk, kt0, D, kT, tid, kThreads);
       __syncthreads();
       // key positions of this tile's rows (halo rows sit before position 0)
@@ -215,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dq(
           f32x4 sc = zero, dp = zero;
 #pragma unroll
           for (int p = 0; p < KP; ++p) {
-            mma(sc, ld8<T>(&sm.skt[16 * b + r16][32 * p + 8 * g]), qf[p]);
-            mma(dp, ld8<T>(&sm.svt[16 * b + r16][32 * p + 8 * g]), df[p]);
+            mma(sc, ld8<T>(&sm.u.kr.skt[16 * b + r16][32 * p + 8 * g]), qf[p]);
+            mma(dp, ld8<T>(&sm.u.kr.svt[16 * b + r16][32 * p + 8 * g]), df[p]);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -877,6 +895,9 @@ hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const vo
     return launch_swa_bwd_typed<bf16, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
                                           dmv, Dws, metap, st);
   }
+  if (s.dk == 128)
+    return launch_swa_bwd_typed<float, 128>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
+                                            dmv, Dws, metap, st);
   return launch_swa_bwd_typed<float, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
                                          Dws, metap, st);
 }

@@ -200,8 +200,7 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
  * own queries and keys as passed to lizard_hybrid_fwd, and their gradients
  * [B,H,T,dk] (desc->dtype, overwritten); dq, dk then hold the gated branch's
  * gradients alone.  With them NULL, dq and dk hold both branches' gradients.
- * This version supports BF16 with dk = dv in {64, 128} and F32 with dk = dv = 64
- * (LIZARD_E_UNSUPPORTED for F32 at 128). */
+ * Supported for BF16 and F32 with dk = dv in {64, 128}. */
 lizard_status_t lizard_hybrid_bwd(const lizard_desc_t* desc, const void* q, const void* k,
                                   const void* v, const void* gate, const void* meta_k,
                                   const void* meta_v, const float* h0, const void* o_swa,

@@ -158,15 +158,17 @@ def test_backward_workspace_and_support():
     assert need > 0
     st = lib.lizard_hybrid_bwd(ctypes.byref(d), *([FAKE] * 23), FAKE, need - 1, None)
     assert st == 5
-    # the backward covers bf16 at d = 64 and 128 and fp32 at d = 64
-    for kw in (dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32)):
+    # the backward covers d = 64 and 128 in both precisions
+    for kw in (dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32),
+               dict(dk=128, dv=128, dtype=_abi.LIZARD_F32)):
         assert lib.lizard_workspace_bytes(ctypes.byref(desc(**kw)), 3) > 0
-    d2 = desc(dk=128, dv=128, dtype=_abi.LIZARD_F32)
+    d2 = desc(dk=96, dv=96)
     assert lib.lizard_workspace_bytes(ctypes.byref(d2), 3) == 0
     assert lib.lizard_hybrid_bwd(ctypes.byref(d2), *([FAKE] * 23), FAKE, 1 << 30, None) == 4
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(dk=128, dv=128), dict(dtype=_abi.LIZARD_F32),
+                                dict(dk=128, dv=128, dtype=_abi.LIZARD_F32),
                                 dict(B=8, H=16, window=200, n_meta=16)])
 def test_backward_workspace_does_not_grow_with_T(kw):
     # the GLA part holds a fixed number of chunk states per head and the window

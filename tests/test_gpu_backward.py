@@ -108,14 +108,23 @@ def test_backward_fp32_d64(T, w, M):
     check(2, 2, T, w, M, seed=T + w, dtype="f32")
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32")])
+@pytest.mark.parametrize("T,w,M", [(64, 64, 4), (200, 128, 4), (257, 16, 16), (130, 1, 0),
+                                   (300, 200, 2)])
+def test_backward_fp32_d128(T, w, M):
+    # fp32 at d = 128: the chunk-gradient kernel reads dO, v and dS^T from global
+    # memory; the window dq kernel shares LDS between query and key tiles
+    check(1, 2, T, w, M, seed=T + w, d=128, dtype="f32")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f32"), (128, "f32")])
 def test_backward_generic_gate_ranges_and_states(d, dtype):
     check(1, 2, 192, 64, 4, seed=4, gate_mean=-3.0, d=d, dtype=dtype)
     check(2, 1, 450, 64, 4, seed=5, steep_chunks=True, d=d, dtype=dtype)
     check(2, 2, 200, 64, 4, seed=11, with_h0=True, with_dhT=True, mix=0.6, d=d, dtype=dtype)
 
 
-@pytest.mark.parametrize("T,d,dtype", [(4500, 64, "bf16"), (2200, 128, "bf16"), (2100, 64, "f32")])
+@pytest.mark.parametrize("T,d,dtype", [(4500, 64, "bf16"), (2200, 128, "bf16"), (2100, 64, "f32"),
+                                       (2150, 128, "f32")])
 def test_backward_several_blocks(T, d, dtype):
     # longer than one 2048-token block: the block-start states (parked in the
     # gate-gradient output) and the reverse carry between blocks, with an

@@ -134,6 +134,7 @@ def test_short_first_segment():
 def test_segments_d128_and_fp32():
     check(1, 2, 700, (300,), 128, 128, 4, seed=5)
     check(1, 2, 300, (100, 200), 64, 40, 2, dtype="f32", seed=6)
+    check(1, 1, 400, (150, 260), 128, 100, 3, dtype="f32", seed=10)
 
 
 def test_segments_window_inputs_and_gate_logits():
