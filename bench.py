@@ -180,6 +180,8 @@ def main():
                     help="only time the training step (forward + backward), for profiling")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode steps, for profiling")
+    ap.add_argument("--decode-b", type=int, default=None,
+                    help="batch of the --decode-only run (default 64, 1024 steps; else 256 steps)")
     ap.add_argument("--min-warmup-seconds", type=float, default=1.0,
                     help="keep warming up past --warmup steps until this much time has passed")
     args = ap.parse_args()
@@ -211,7 +213,9 @@ def main():
     from gated_linear_attention_chunked_amd import _abi
 
     if args.decode_only:
-        print(json.dumps({"decode": bench_decode(lz, torch, torch.device("cuda:0"))}), flush=True)
+        steps = None if args.decode_b is None else 256
+        print(json.dumps({"decode": bench_decode(lz, torch, torch.device("cuda:0"), B=args.decode_b,
+                                                 steps=steps)}), flush=True)
         return
     if args.train_only:
         print(json.dumps({"train": bench_train(lz, torch, torch.device("cuda:0"), args)}),
