@@ -1101,18 +1101,20 @@ hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const 
   const Plan pl = make_plan(s);
   *G = pl.G;
   *cps = pl.cps;
-  if (s.T == 0 || pl.G < 2 || s.dtype != 1 || s.dk != 128) return hipSuccess;
+  if (s.T == 0 || pl.G < 2 || s.dtype != 1 || (s.dk != 128 && s.dk != 64)) return hipSuccess;
   const int BH = s.B * s.H;
   float* ws_state = (float*)ws;
-  float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * 128 * 128;
-  if (s.gate == 1)
-    hipLaunchKernelGGL((gla_state_pass<bf16, 128, bf16>), dim3(pl.G - 1, BH), dim3(512), 0, st,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)la, ws_state, ws_gamma, s.T,
-                       pl.cps, pl.G, s.cu, s.n_tokens, s.H);
+  float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * s.dk * s.dk;
+  auto go = [&](auto kernel, auto gt) {
+    typedef decltype(gt) GT;
+    hipLaunchKernelGGL(kernel, dim3(pl.G - 1, BH), dim3(4 * s.dk), 0, st, (const bf16*)k,
+                       (const bf16*)v, (const GT*)la, ws_state, ws_gamma, s.T, pl.cps, pl.G, s.cu,
+                       s.n_tokens, s.H, 0);
+  };
+  if (s.dk == 128)
+    s.gate == 1 ? go(gla_state_pass<bf16, 128, bf16>, bf16()) : go(gla_state_pass<bf16, 128, float>, 0.f);
   else
-    hipLaunchKernelGGL((gla_state_pass<bf16, 128, float>), dim3(pl.G - 1, BH), dim3(512), 0, st,
-                       (const bf16*)k, (const bf16*)v, (const float*)la, ws_state, ws_gamma, s.T,
-                       pl.cps, pl.G, s.cu, s.n_tokens, s.H);
+    s.gate == 1 ? go(gla_state_pass<bf16, 64, bf16>, bf16()) : go(gla_state_pass<bf16, 64, float>, 0.f);
   return hipGetLastError();
 }
 

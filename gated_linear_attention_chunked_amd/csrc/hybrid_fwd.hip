@@ -1,4 +1,5 @@
-// Hybrid forward as one output pass, gfx950, bf16, d_k = d_v = 128, w <= 129.
+// Hybrid forward as one output pass, gfx950, bf16, d_k = d_v = D in {64, 128},
+// w <= 129.
 //
 // "Lizard: An Efficient Linearization Framework for Large Language Models"
 // (gist.science summary, sections 2(a) and 2(b)) sums two branches computed from
@@ -12,23 +13,26 @@
 //
 // One work-group of 8 waves per (head, segment) walks the segment's 32-token
 // chunks in order.  Chunk c (tokens t0..t0+31) in two phases:
-//   phase 1  consumers (waves 0-3; value columns 32w..32w+31, their fp32 state
-//              slice in registers): inter O = (q 2^b) S_c, the state update
+//   phase 1  consumers (waves 0-3; value columns (D/4)w.. (D/4)w + D/4 - 1, their
+//              fp32 state slice in registers): inter O = (q 2^b) S_c, the state update
 //              S_{c+1} = diag(2^{b_last}) S_c + (k 2^{b_last - b})^T V, and
 //              (waves 0-2, one 16x16 block each) the masked intra scores
 //            producers (waves 4-7): window scores of query rows 16(p&1).. over
-//              one half of the keys (ring chunks c-4..c-2, or c-1, c and the
-//              meta slots); exponentials from that half's own row maxima;
-//              maxima, row sums and exponentials -> LDS
+//              one half of the keys (the older ring chunks, or the newer ones
+//              with chunk c and the meta slots); exponentials from that half's
+//              own row maxima; maxima, row sums and exponentials -> LDS
 //   ---- barrier
 //   phase 2  consumers: O += A V (intra) + the two halves' P V (V^T ring, meta
 //              values), each scaled by f_h mix / (f_0 l_0 + f_1 l_1) with
 //              f_h = 2^{(m_h - max(m_0, m_1)) scale}; store o; v of chunk c+1
 //              into the V^T ring
-//            producers: gate chunk c+1 (log2-gate cumsum, gated q and k tiles,
-//              k^T for the state update), raw q and raw k of c+1 into LDS;
-//              issue the loads of chunk c+3
+//            producers (D/32 of them, 32 channels each): gate chunk c+1
+//              (log2-gate cumsum, gated q and k tiles, k^T for the state
+//              update), raw q and raw k of c+1 into LDS; issue the loads of c+3
 //   ---- barrier
+// The ring holds RING chunks, c-RING+1 .. c: 5 for w <= 129, 3 for w <= 65.
+// With D = 64 the pass also writes the training outputs o_swa (the window
+// branch alone) and lse (its natural-log softmax normaliser per query).
 // 32-token chunks keep the GLA tiles and a ring of w + 32 window keys and
 // values inside the 160 KB of LDS at once.  The GLA algebra is that of
 // gla_fwd.hip: one reference (the chunk start) when every channel's chunk decay
@@ -45,45 +49,48 @@ namespace lz {
 namespace {
 
 constexpr int kC = 32;             // tokens per chunk
-constexpr int kD = 128;            // d_k = d_v
-constexpr int kRing = 5;           // window ring slots: chunks c-4 .. c
-constexpr int kMaxW = 4 * kC + 1;  // widest window the ring holds
 constexpr float kFast = 64.f;      // single reference while every chunk decay >= 2^-64
+// widest window a ring of RING chunks holds
+__host__ __device__ constexpr int max_window(int ring) { return (ring - 1) * kC + 1; }
 // Row of the transposed [channel][token] tiles (k-hat^T, the V^T ring, meta V^T):
 // 32 tokens padded to 80 bytes.  Their staging stores write four rows 8 apart
 // per instruction; at 64-byte rows those rows share one set of banks, at 80
 // bytes they fall on two, and the 16-row fragment reads stay conflict-free.
 constexpr int kTP = kC + 8;
 
+template <int D, int RING>
 struct Smem {
-  bf16 qs[kC * kD];              // gated q [t][ch]: q 2^{b_t} (or 2^{b_t - R_i})
-  bf16 ks[kC * kD];              // gated k [s][ch]: k 2^{-b_s} (or 2^{R_j - b_s})
-  bf16 khT[kD * kTP];            // [ch][s]: k 2^{b_last - b_s}
+  static constexpr int kD = D, kRing = RING;
+  bf16 qs[kC * D];               // gated q [t][ch]: q 2^{b_t} (or 2^{b_t - R_i})
+  bf16 ks[kC * D];               // gated k [s][ch]: k 2^{-b_s} (or 2^{R_j - b_s})
+  bf16 khT[D * kTP];             // [ch][s]: k 2^{b_last - b_s}
   bf16 a[kC * kC];               // masked intra scores [t][s]
-  bf16 p[kRing + 1][kC * kC];    // window probabilities [t][s] per ring chunk, meta last
-  bf16 vT[kRing][kD * kTP];      // V^T ring [n][s]
-  bf16 kr[kRing][kC * kD];       // raw K ring [s][ch]
-  bf16 qr[kC * kD];              // raw q [t][ch]
-  bf16 mk[16 * kD];              // meta keys (rows >= M zero)
-  bf16 mvT[kD * kTP];            // meta values transposed (slots >= M zero)
-  alignas(16) float decay[kD];   // 2^{b_last}
-  alignas(16) float eR[2][kD];   // 2^{R_i} (1 for single-reference channels)
-  alignas(16) float vij[kD];     // 2^{R_1 - R_0} (likewise)
+  bf16 p[RING + 1][kC * kC];     // window probabilities [t][s] per ring chunk, meta last
+  bf16 vT[RING][D * kTP];        // V^T ring [n][s]
+  bf16 kr[RING][kC * D];         // raw K ring [s][ch]
+  bf16 qr[kC * D];               // raw q [t][ch]
+  bf16 mk[16 * D];               // meta keys (rows >= M zero)
+  bf16 mvT[D * kTP];             // meta values transposed (slots >= M zero)
+  alignas(16) float decay[D];    // 2^{b_last}
+  alignas(16) float eR[2][D];    // 2^{R_i} (1 for single-reference channels)
+  alignas(16) float vij[D];      // 2^{R_1 - R_0} (likewise)
   float pmax[2][kC];             // window: per key half, row maxima of the raw scores
   float psum[2][kC];             // per key half, row sums of exponentials taken from that maximum
   int fastw[4];                  // per producer wave: its channels take one reference
 };
 
-// [rows][128] and [rows][32] tiles, granules permuted by row
-__device__ __forceinline__ int at16(int row, int col) { return swz_at<16>(row, col); }
+// [rows][D] and [rows][32] tiles, granules permuted by row
+template <int D>
+__device__ __forceinline__ int atd(int row, int col) { return swz_at<D / 8>(row, col); }
 __device__ __forceinline__ int at4(int row, int col) { return swz_at<4>(row, col); }
 // (row, col) of a padded transposed tile
 __device__ __forceinline__ int atp(int row, int col) { return row * kTP + col; }
 
-// Split-map fragment (elements col..col+3 and col+16..col+19) of a [rows][128] tile.
-__device__ __forceinline__ bf16x8 ld_split16(const bf16* t, int row, int col) {
-  const bf16x4 x = *reinterpret_cast<const bf16x4*>(&t[at16(row, col)]);
-  const bf16x4 y = *reinterpret_cast<const bf16x4*>(&t[at16(row, col + 16)]);
+// Split-map fragment (elements col..col+3 and col+16..col+19) of a [rows][D] tile.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_split(const bf16* t, int row, int col) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(&t[atd<D>(row, col)]);
+  const bf16x4 y = *reinterpret_cast<const bf16x4*>(&t[atd<D>(row, col + 16)]);
   return bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 }
 
@@ -96,12 +103,14 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const float* f) {
 }
 
 // Masked intra score block A[16i.., 16j..] (key block j <= i) into the a tile.
-__device__ __forceinline__ void intra_scores(Smem& sm, int i, int j, bool fast, int r16, int g) {
+template <class SM>
+__device__ __forceinline__ void intra_scores(SM& sm, int i, int j, bool fast, int r16, int g) {
+  constexpr int D = SM::kD;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const bf16x8 af = ld8<bf16>(&sm.ks[at16(16 * j + r16, 32 * p + 8 * g)]);
-    bf16x8 bf = ld8<bf16>(&sm.qs[at16(16 * i + r16, 32 * p + 8 * g)]);
+  for (int p = 0; p < D / 32; ++p) {
+    const bf16x8 af = ld8<bf16>(&sm.ks[atd<D>(16 * j + r16, 32 * p + 8 * g)]);
+    bf16x8 bf = ld8<bf16>(&sm.qs[atd<D>(16 * i + r16, 32 * p + 8 * g)]);
     if (!fast && j < i) bf = scale8(bf, &sm.vij[32 * p + 8 * g]);
     mma(acc, af, bf);
   }
@@ -115,17 +124,29 @@ __device__ __forceinline__ void intra_scores(Smem& sm, int i, int j, bool fast, 
 
 // kSep: the window branch reads its own queries and keys qw, kw (otherwise qw,
 // kw alias q, k and are not loaded a second time).  GT: gate input type (float
-// log alpha or bf16 logit).
-template <bool kSep, typename GT>
+// log alpha or bf16 logit).  o_swa and lse (D = 64 only; each nullable) receive
+// the window branch alone and its log normaliser.
+template <int D, int RING, bool kSep, typename GT>
 __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ qw,
     const bf16* __restrict__ kw, const bf16* __restrict__ v,
     const GT* __restrict__ la, const bf16* __restrict__ mk, const bf16* __restrict__ mv,
     const float* __restrict__ h0, const float* __restrict__ ws_state,
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT,
-    bf16* __restrict__ rk, bf16* __restrict__ rv, int T_arg, int H, int W, int M,
-    float scale_log2, float mix, int cps, int G, const int* __restrict__ cu, int N) {
-  __shared__ Smem sm;
+    bf16* __restrict__ rk, bf16* __restrict__ rv, bf16* __restrict__ o_swa,
+    float* __restrict__ lse, int T_arg, int H, int W, int M, float scale_log2, float mix, int cps,
+    int G, const int* __restrict__ cu, int N) {
+  constexpr int kD = D, kRing = RING;
+  constexpr int NT = D / 64;    // 16-column blocks of a consumer wave's state slice
+  constexpr int CW = D / 4;     // value columns per consumer wave
+  constexpr int NCB = D / 16;   // 16-row blocks of the state
+  constexpr int KS = D / 32;    // contraction steps over channels
+  constexpr int NPW = D / 32;   // producer waves that gate (32 channels each)
+  constexpr int NR0 = (RING + 1) / 2;  // ring chunks in the first key half
+  constexpr bool kSave = D == 64;
+  static_assert(D == 64 || D == 128, "head size");
+  static_assert(RING == 3 || RING == 5, "ring");
+  __shared__ Smem<D, RING> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
@@ -144,12 +165,13 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   // tiles that stay zero: the intra block above the diagonal, unused meta columns
   for (int e = tid; e < 16 * 16; e += 512) sm.a[at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
   for (int e = tid; e < kC * 16; e += 512) sm.p[kRing][at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
+  if (tid >= NPW && tid < 4) sm.fastw[tid] = 1;  // producers that do not gate: flag 1
   {
     const bf16* mkh = mk + (size_t)h * M * kD;
     const bf16* mvh = mv + (size_t)h * M * kD;
     for (int e = tid; e < 16 * kD; e += 512) {
       const int r = e / kD, c = e % kD;
-      sm.mk[at16(r, c)] = r < M ? mkh[r * kD + c] : (bf16)0.f;
+      sm.mk[atd<D>(r, c)] = r < M ? mkh[r * kD + c] : (bf16)0.f;
     }
     for (int e = tid; e < kD * kC; e += 512) {
       const int c = e / kC, t = e % kC;
@@ -166,33 +188,35 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const int cw = wave;
     // state entering the segment: h0 carried through the earlier segments'
     // local end states (column-major) and total log2 decays
-    f32x4 S[2][8];  // S[nt][cb]: rows 16cb + 4g + r, column 32cw + 16nt + r16
+    f32x4 S[NT][NCB];  // S[nt][cb]: rows 16cb + 4g + r, column CW cw + 16nt + r16
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[nt][cb][r] = h0 ? h0[s_base + (16 * cb + 4 * g + r) * kD + 32 * cw + 16 * nt + r16] : 0.f;
+          S[nt][cb][r] = h0 ? h0[s_base + (16 * cb + 4 * g + r) * kD + CW * cw + 16 * nt + r16] : 0.f;
     for (int sg = 0; sg < seg; ++sg) {
       const float* loc = ws_state + ((size_t)bh * (G - 1) + sg) * kD * kD;
       const float* gm = ws_gamma + ((size_t)bh * (G - 1) + sg) * kD;
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gm[16 * cb + 4 * g]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const f32x4 l4 =
-              *reinterpret_cast<const f32x4*>(&loc[(32 * cw + 16 * nt + r16) * kD + 16 * cb + 4 * g]);
+              *reinterpret_cast<const f32x4*>(&loc[(CW * cw + 16 * nt + r16) * kD + 16 * cb + 4 * g]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) S[nt][cb][r] = exp2_fast(g4[r]) * S[nt][cb][r] + l4[r];
         }
       }
     }
 
-    // v of a chunk: lane takes rows 2vr, 2vr+1 and columns 32cw + 8vo .. +7
-    const int vo = lane & 3, vr = lane >> 2;
-    const u32 vb = (u32)((2 * vr * kD + 32 * cw + 8 * vo) * 2);
+    // v of a chunk: lane takes rows 2vr, 2vr+1 and columns CW cw + 8vo .. +7
+    // (with D = 64 lanes 32..63 repeat lanes 0..31: same loads, same stores)
+    constexpr int VO = CW / 8;
+    const int vo = lane % VO, vr = (lane / VO) & 15;
+    const u32 vb = (u32)((2 * vr * kD + CW * cw + 8 * vo) * 2);
     auto load_v = [&](int ch, u32x4* x) {
       const Buf cv(v + off + (size_t)ch * kC * kD, (u32)max(0, T_len - ch * kC) * kD * 2);
       x[0] = cv.ld128(vb);
@@ -203,7 +227,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const u32 w0 = x[0][c >> 1], w1 = x[1][c >> 1];
-        *reinterpret_cast<u32*>(&dst[atp(32 * cw + 8 * vo + c, 2 * vr)]) =
+        *reinterpret_cast<u32*>(&dst[atp(CW * cw + 8 * vo + c, 2 * vr)]) =
             (c & 1) ? hi2(w0, w1) : lo2(w0, w1);
       }
     };
@@ -212,15 +236,15 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
     for (int r = 0; r < kRing; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32*>(&sm.vT[r][atp(32 * cw + 8 * vo + c, 2 * vr)]) = 0u;
-    {  // ring: chunks c_begin-4 .. c_begin
+      for (int c = 0; c < 8; ++c) *reinterpret_cast<u32*>(&sm.vT[r][atp(CW * cw + 8 * vo + c, 2 * vr)]) = 0u;
+    {  // ring: chunks c_begin-RING+1 .. c_begin
       u32x4 pro[kRing][2];
 #pragma unroll
       for (int r = 0; r < kRing; ++r)
-        if (c_begin - 4 + r >= 0) load_v(c_begin - 4 + r, pro[r]);
+        if (c_begin - (kRing - 1) + r >= 0) load_v(c_begin - (kRing - 1) + r, pro[r]);
 #pragma unroll
       for (int r = 0; r < kRing; ++r)
-        if (c_begin - 4 + r >= 0) store_vT((c_begin - 4 + r) % kRing, pro[r]);
+        if (c_begin - (kRing - 1) + r >= 0) store_vT((c_begin - (kRing - 1) + r) % kRing, pro[r]);
     }
     // chunk c_begin + j is loaded into V[j & 1]; a set is refilled (chunk + 2)
     // right after its v^T store, so every load has two chunks of time
@@ -234,22 +258,22 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       const int fw = sm.fastw[0] & sm.fastw[1] & sm.fastw[2] & sm.fastw[3];
       const bool fast = __builtin_amdgcn_readfirstlane(fw) != 0;
       // ---- phase 1: inter, O^T[n][t] = sum_ch S[ch][n] qs[t][ch]
-      f32x4 O[2][2];  // [nt][qb]: column (query) 16qb + r16, value columns 32cw + 16nt + 4g ..
+      f32x4 O[NT][2];  // [nt][qb]: column (query) 16qb + r16, value columns CW cw + 16nt + 4g ..
       {
-        bf16x8 qf[2][4];
+        bf16x8 qf[2][KS];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) qf[qb][p] = ld_split16(sm.qs, 16 * qb + r16, 32 * p + 4 * g);
+          for (int p = 0; p < KS; ++p) qf[qb][p] = ld_split<D>(sm.qs, 16 * qb + r16, 32 * p + 4 * g);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) O[nt][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (fast) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < KS; ++p) {
               const bf16x8 sf = pack_acc<bf16>(S[nt][2 * p], S[nt][2 * p + 1]);
 #pragma unroll
               for (int qb = 0; qb < 2; ++qb) mma(O[nt][qb], sf, qf[qb][p]);
@@ -259,25 +283,25 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < KS; ++p) {
               const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.eR[qb][32 * p + 4 * g]);
               const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.eR[qb][32 * p + 16 + 4 * g]);
 #pragma unroll
-              for (int nt = 0; nt < 2; ++nt)
+              for (int nt = 0; nt < NT; ++nt)
                 mma(O[nt][qb], pack_acc<bf16>(S[nt][2 * p] * e0, S[nt][2 * p + 1] * e1), qf[qb][p]);
             }
         }
       }
       // ---- phase 1: state update, S = diag(2^{b_last}) S + khT V
-      bf16x8 vf[2];
+      bf16x8 vf[NT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) vf[nt] = ld8<bf16>(&sm.vT[slot][atp(32 * cw + 16 * nt + r16, 8 * g)]);
+      for (int nt = 0; nt < NT; ++nt) vf[nt] = ld8<bf16>(&sm.vT[slot][atp(CW * cw + 16 * nt + r16, 8 * g)]);
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
         const f32x4 dec = *reinterpret_cast<const f32x4*>(&sm.decay[16 * cb + 4 * g]);
         const bf16x8 kf = ld8<bf16>(&sm.khT[atp(16 * cb + r16, 8 * g)]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           S[nt][cb] *= dec;
           mma(S[nt][cb], kf, vf[nt]);
         }
@@ -291,16 +315,19 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) af[qb] = ld8<bf16>(&sm.a[at4(16 * qb + r16, 8 * g)]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) mma(O[nt][qb], vf[nt], af[qb]);
       }
       // ---- phase 2: window, O^T[n][t] += sum_s vT[n][s] P[t][s] over the ring.
-      // Slot of chunk c-4+r is (c+1+r) mod 5; meta slots >= M and P of keys
-      // outside the window are zero.  The two key halves (ring chunks c-4..c-2;
-      // c-1, c and the meta slots) carry exponentials from their own row
-      // maxima m_h with sums l_h: with m = max(m_0, m_1), f_h = 2^{(m_h - m) s},
-      // half h's product is scaled by f_h mix / (f_0 l_0 + f_1 l_1).
+      // Slot of chunk c-RING+1+r is (c+1+r) mod RING; meta slots >= M and P of
+      // keys outside the window are zero.  The two key halves (ring chunks
+      // r < NR0; the rest with the meta slots) carry exponentials from their own
+      // row maxima m_h with sums l_h: with m = max(m_0, m_1),
+      // f_h = 2^{(m_h - m) s}, half h's product is scaled by
+      // f_h mix / (f_0 l_0 + f_1 l_1).  With the training outputs the window
+      // branch is summed apart (without mix) and added once at the end.
+      f32x4 Owin[kSave ? NT : 1][2];
       {
         float sc[2][2];  // [half][qb]
 #pragma unroll
@@ -309,44 +336,61 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           const float m0 = sm.pmax[0][row], m1 = sm.pmax[1][row];
           const float mm = fmaxf(m0, m1);
           const float f0 = exp2_fast((m0 - mm) * scale_log2), f1 = exp2_fast((m1 - mm) * scale_log2);
-          const float inv = mix / (f0 * sm.psum[0][row] + f1 * sm.psum[1][row]);
+          const float L = f0 * sm.psum[0][row] + f1 * sm.psum[1][row];
+          const float inv = (kSave ? 1.f : mix) / L;
           sc[0][qb] = f0 * inv;
           sc[1][qb] = f1 * inv;
+          if constexpr (kSave) {
+            const int t = c * kC + row;
+            if (lse && cw == 0 && g == 0 && t < T_len)
+              lse[sr.row0 + t] = (mm * scale_log2 + log2_fast(L)) * kLn2;
+          }
         }
         const int s0 = (c + 1) % kRing;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int r0 = h == 0 ? 0 : 3, r1 = h == 0 ? 2 : kRing;  // ring chunks (kRing: meta)
-          bf16x8 wf[3][2], pf[3][2];
+          const int r0 = h == 0 ? 0 : NR0, r1 = h == 0 ? NR0 - 1 : kRing;  // ring chunks (kRing: meta)
+          bf16x8 wf[NR0][NT], pf[NR0][2];
 #pragma unroll
           for (int r = r0; r <= r1; ++r) {
             const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
               wf[r - r0][nt] = r == kRing - 1 ? vf[nt]
-                             : r == kRing     ? ld8<bf16>(&sm.mvT[atp(32 * cw + 16 * nt + r16, 8 * g)])
-                                              : ld8<bf16>(&sm.vT[sl][atp(32 * cw + 16 * nt + r16, 8 * g)]);
+                             : r == kRing     ? ld8<bf16>(&sm.mvT[atp(CW * cw + 16 * nt + r16, 8 * g)])
+                                              : ld8<bf16>(&sm.vT[sl][atp(CW * cw + 16 * nt + r16, 8 * g)]);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) pf[r - r0][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
           }
-          f32x4 Ow[2][2];  // this half of the window branch, unnormalised
+          f32x4 Ow[NT][2];  // this half of the window branch, unnormalised
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) Ow[nt][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int r = r0; r <= r1; ++r)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
               for (int qb = 0; qb < 2; ++qb) mma(Ow[nt][qb], wf[r - r0][nt], pf[r - r0][qb]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) O[nt][qb] += Ow[nt][qb] * sc[h][qb];
+            for (int nt = 0; nt < NT; ++nt) {
+              if constexpr (kSave)
+                Owin[nt][qb] = h == 0 ? Ow[nt][qb] * sc[0][qb] : Owin[nt][qb] + Ow[nt][qb] * sc[1][qb];
+              else
+                O[nt][qb] += Ow[nt][qb] * sc[h][qb];
+            }
+        }
+        if constexpr (kSave) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) O[nt][qb] += Owin[nt][qb] * mix;
         }
       }
-      // v of chunk c+1 into the slot of chunk c-4 (read above by this wave only);
+      // v of chunk c+1 into the slot of chunk c-RING+1 (read above by this wave only);
       // past the segment end this stages an unused copy, so the loop body has no
       // branch around its loads and their waits stay exact
       store_vT((c + 1) % kRing, Vn);
@@ -354,11 +398,15 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       bf16* oc = o + off + (size_t)c * kC * kD;
       const int rows = T_len - c * kC;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          if (16 * qb + r16 < rows)
-            st4<bf16>(oc + (u32)((16 * qb + r16) * kD + 32 * cw + 16 * nt + 4 * g), O[nt][qb]);
+          if (16 * qb + r16 < rows) {
+            const u32 e = (u32)((16 * qb + r16) * kD + CW * cw + 16 * nt + 4 * g);
+            st4<bf16>(oc + e, O[nt][qb]);
+            if constexpr (kSave)
+              if (o_swa) st4<bf16>(o_swa + off + (size_t)c * kC * kD + e, Owin[nt][qb]);
+          }
       lds_barrier();  // (B) chunk c+1 staged
     };
     int c = c_begin;
@@ -369,16 +417,17 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     if (c < c_end) step(c, V1);
     if (hT && seg == Gs - 1) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            hT[s_base + (16 * cb + 4 * g + r) * kD + 32 * cw + 16 * nt + r16] = S[nt][cb][r];
+            hT[s_base + (16 * cb + 4 * g + r) * kD + CW * cw + 16 * nt + r16] = S[nt][cb][r];
     }
   } else {
     // ------------------------------------------------------------ producers
-    const int pw = wave - 4;                    // gating: channels 32pw .. 32pw+31
+    const int pw = wave - 4;                    // gating (pw < NPW): channels 32pw .. 32pw+31
+    const bool gater = pw < NPW;
     const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+7, rows 2rq, 2rq+1
     const int ch0 = 32 * pw + 8 * ol;
     const int isub = rq >> 3;                   // 16-row sub-block of the rows
@@ -515,28 +564,28 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int row = 2 * rq + rr;
-        *reinterpret_cast<u32x4*>(&sm.qs[at16(row, ch0)]) = u32x4{qw[rr][0], qw[rr][1], qw[rr][2], qw[rr][3]};
-        *reinterpret_cast<u32x4*>(&sm.ks[at16(row, ch0)]) = u32x4{kw[rr][0], kw[rr][1], kw[rr][2], kw[rr][3]};
-        *reinterpret_cast<u32x4*>(&sm.qr[at16(row, ch0)]) = kSep ? x.wq[rr] : x.q[rr];
-        *reinterpret_cast<u32x4*>(&kring[at16(row, ch0)]) = kSep ? x.wk[rr] : x.k[rr];
+        *reinterpret_cast<u32x4*>(&sm.qs[atd<D>(row, ch0)]) = u32x4{qw[rr][0], qw[rr][1], qw[rr][2], qw[rr][3]};
+        *reinterpret_cast<u32x4*>(&sm.ks[atd<D>(row, ch0)]) = u32x4{kw[rr][0], kw[rr][1], kw[rr][2], kw[rr][3]};
+        *reinterpret_cast<u32x4*>(&sm.qr[atd<D>(row, ch0)]) = kSep ? x.wq[rr] : x.q[rr];
+        *reinterpret_cast<u32x4*>(&kring[atd<D>(row, ch0)]) = kSep ? x.wk[rr] : x.k[rr];
       }
     };
     // Window scores of query rows 16qb..16qb+15 of chunk c over one half of
-    // the keys: ring chunks c-4..c-2 (half 0) or c-1, c and the meta slots
-    // (half 1), one producer per (query block, half).  Each half's
+    // the keys: the NR0 oldest ring chunks (half 0) or the newer ones, chunk c
+    // and the meta slots (half 1), one producer per (query block, half).  Each half's
     // exponentials are taken from its own row maximum; the row maxima and sums
     // go to LDS, and the consumers combine the two halves.
     auto window = [&](int c, int qb, auto half) {
       constexpr int H = decltype(half)::value;
-      constexpr int R0 = H == 0 ? 0 : 3, NR = H == 0 ? 3 : 2;  // ring chunks r = R0 .. R0+NR-1
+      constexpr int R0 = H == 0 ? 0 : NR0, NR = H == 0 ? NR0 : kRing - NR0;  // ring chunks R0 .. R0+NR-1
       constexpr int NB = 2 * NR + H;                           // 16-key blocks (+ the meta block)
-      bf16x8 qf[4];
+      bf16x8 qf[KS];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) qf[p] = ld8<bf16>(&sm.qr[at16(16 * qb + r16, 32 * p + 8 * g)]);
+      for (int p = 0; p < KS; ++p) qf[p] = ld8<bf16>(&sm.qr[atd<D>(16 * qb + r16, 32 * p + 8 * g)]);
       const int t = c * kC + 16 * qb + r16;
       // every slot is multiplied (slots before the sequence start hold stale
       // data); the mask below selects -inf for every key outside the window
-      const int s0 = (c + 1) % kRing;  // slot of chunk c-4
+      const int s0 = (c + 1) % kRing;  // slot of chunk c-RING+1
       f32x4 L[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) L[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -545,16 +594,16 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         const bool meta = x == NR;
         const int r = R0 + x;
         const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
-        bf16x8 kf[2][4];
+        bf16x8 kf[2][KS];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int p = 0; p < 4; ++p)
+          for (int p = 0; p < KS; ++p)
             if (!meta || kb == 0)
-              kf[kb][p] = ld8<bf16>(meta ? &sm.mk[at16(r16, 32 * p + 8 * g)]
-                                         : &sm.kr[sl][at16(16 * kb + r16, 32 * p + 8 * g)]);
+              kf[kb][p] = ld8<bf16>(meta ? &sm.mk[atd<D>(r16, 32 * p + 8 * g)]
+                                         : &sm.kr[sl][atd<D>(16 * kb + r16, 32 * p + 8 * g)]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < KS; ++p)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
             if (!meta || kb == 0) mma(L[2 * x + kb], kf[kb][p], qf[p]);
@@ -614,13 +663,13 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     // ---- prologue: the raw-K ring before the segment, chunk c_begin gated,
     // c_begin+1 and c_begin+2 in flight
     In I0, I1;
-    issue(c_begin, I0);
-    issue(min(c_begin + 1, c_end - 1), I1);
-    {
+    if (gater) {
+      issue(c_begin, I0);
+      issue(min(c_begin + 1, c_end - 1), I1);
       u32x4 kp[kRing - 1][2];
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) {
-        const int cr = c_begin - 4 + r;
+        const int cr = c_begin - (kRing - 1) + r;
         if (cr >= 0) {
           const Buf bk(kw + off + (size_t)cr * kC * kD, (u32)(kC * kD * 2));
           kp[r][0] = bk.ld128(o2);
@@ -629,15 +678,15 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       }
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) {
-        const int cr = c_begin - 4 + r;
+        const int cr = c_begin - (kRing - 1) + r;
         if (cr >= 0) {
-          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][at16(2 * rq, ch0)]) = kp[r][0];
-          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][at16(2 * rq + 1, ch0)]) = kp[r][1];
+          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][atd<D>(2 * rq, ch0)]) = kp[r][0];
+          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][atd<D>(2 * rq + 1, ch0)]) = kp[r][1];
         }
       }
+      gate(c_begin, I0);
+      issue(min(c_begin + 2, c_end - 1), I0);
     }
-    gate(c_begin, I0);
-    issue(min(c_begin + 2, c_end - 1), I0);
     lds_barrier();
 
     auto pstep = [&](int c, In& Xn) {
@@ -645,11 +694,13 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         window(c, pw & 1, std::integral_constant<int, 0>());
       else
         window(c, pw & 1, std::integral_constant<int, 1>());
-      lds_barrier();  // (A) every read of the gated tiles, raw q and K(c-4) done
+      lds_barrier();  // (A) every read of the gated tiles, raw q and K(c-RING+1) done
       // past the segment end this gates an unused copy of the last chunk (no
       // branch around the loads, so their waits stay exact)
-      gate(c + 1, Xn);
-      issue(min(c + 3, c_end - 1), Xn);
+      if (gater) {
+        gate(c + 1, Xn);
+        issue(min(c + 3, c_end - 1), Xn);
+      }
       lds_barrier();  // (B)
     };
     int c = c_begin;
@@ -667,9 +718,10 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const Buf bk(kw + off, (u32)((size_t)T_len * kD * 2)), bv(v + off, (u32)((size_t)T_len * kD * 2));
     const size_t rbase = (size_t)bh * W * kD;
     const u32x4 z = {0u, 0u, 0u, 0u};
+    constexpr int GR = kD / 8;  // 16-byte granules per row
     const int s_lo = (int)((long long)W * seg / Gs), s_hi = (int)((long long)W * (seg + 1) / Gs);
-    for (int e = s_lo * 16 + tid; e < s_hi * 16; e += 512) {
-      const int slot = e >> 4, c = (e & 15) * 8;
+    for (int e = s_lo * GR + tid; e < s_hi * GR; e += 512) {
+      const int slot = e / GR, c = (e % GR) * 8;
       const int p = slot < T_len % W ? T_len - T_len % W + slot : T_len - T_len % W - W + slot;
       u32x4 xk = z, xv = z;
       if (p >= 0) {
@@ -685,46 +737,66 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 
 }  // namespace
 
-bool hybrid_fused_ok(const Shape& s) {
-  return s.dtype == 1 && s.dk == kD && s.dv == kD && s.window >= 1 && s.window <= kMaxW &&
+// bf16 with d_k = d_v = 128 (inference outputs) or 64 (also o_swa and lse), a
+// window the five-chunk ring holds, at most 16 meta slots, no halo.
+bool hybrid_fused_ok(const Shape& s, bool save) {
+  const bool shape = (s.dk == 128 && !save) || s.dk == 64;
+  return s.dtype == 1 && shape && s.dv == s.dk && s.window >= 1 && s.window <= max_window(5) &&
          s.n_meta <= 16 && s.T > 0 && s.hlen == 0;
 }
 
-template <bool kSep, typename GT>
+template <int D, int RING, bool kSep, typename GT>
 void launch_fused_kernel(const Shape& s, const void* q, const void* k, const void* qw,
                          const void* kw, const void* v, const void* la, const void* mk,
                          const void* mv, const float* h0, const float* ws_state,
                          const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
-                         int cps, int G_, hipStream_t st) {
-  hipLaunchKernelGGL((hybrid_fwd_fused<kSep, GT>), dim3(G_, s.B * s.H), dim3(512), 0, st,
+                         void* o_swa, float* lse, int cps, int G_, hipStream_t st) {
+  hipLaunchKernelGGL((hybrid_fwd_fused<D, RING, kSep, GT>), dim3(G_, s.B * s.H), dim3(512), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)qw, (const bf16*)kw,
                      (const bf16*)v, (const GT*)la, (const bf16*)mk, (const bf16*)mv, h0, ws_state,
-                     ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, s.T, s.H, s.window,
-                     s.n_meta, s.scale * kLog2e, s.mix, cps, G_, s.cu, s.n_tokens);
+                     ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, (bf16*)o_swa, lse, s.T,
+                     s.H, s.window, s.n_meta, s.scale * kLog2e, s.mix, cps, G_, s.cu, s.n_tokens);
+}
+
+template <int D, int RING>
+void launch_fused_ring(const Shape& s, bool sep, const void* q, const void* k, const void* qw,
+                       const void* kw, const void* v, const void* la, const void* mk,
+                       const void* mv, const float* h0, const float* ws_state,
+                       const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
+                       void* o_swa, float* lse, int cps, int G, hipStream_t st) {
+  auto go = [&](auto kernel_launch) {
+    kernel_launch(s, q, k, qw, kw, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT, ring_k, ring_v,
+                  o_swa, lse, cps, G, st);
+  };
+  if (s.gate == 1)
+    sep ? go(launch_fused_kernel<D, RING, true, bf16>) : go(launch_fused_kernel<D, RING, false, bf16>);
+  else
+    sep ? go(launch_fused_kernel<D, RING, true, float>) : go(launch_fused_kernel<D, RING, false, float>);
 }
 
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
                                const void* kw, const void* v, const void* la, const void* mk,
                                const void* mv, const float* h0, void* o, float* hT, void* ring_k,
-                               void* ring_v, void* ws, hipStream_t st) {
+                               void* ring_v, void* o_swa, float* lse, void* ws, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
   int G = 1, cps = 1;
   hipError_t e = launch_gla_state(s, k, v, la, ws, &G, &cps, st);
   if (e != hipSuccess) return e;
   const int BH = s.B * s.H;
   const float* ws_state = (const float*)ws;
-  const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * kD * kD : nullptr;
+  const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * s.dk * s.dk : nullptr;
   const bool sep = qw != nullptr;
   const void* qw_ = sep ? qw : q;
   const void* kw_ = sep ? kw : k;
-  auto go = [&](auto kernel_launch) {
-    kernel_launch(s, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT, ring_k,
-                  ring_v, cps, G, st);
-  };
-  if (s.gate == 1)
-    sep ? go(launch_fused_kernel<true, bf16>) : go(launch_fused_kernel<false, bf16>);
+  if (s.dk == 128)
+    launch_fused_ring<128, 5>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
+                              ring_k, ring_v, nullptr, nullptr, cps, G, st);
+  else if (s.window <= max_window(3))
+    launch_fused_ring<64, 3>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
+                             ring_k, ring_v, o_swa, lse, cps, G, st);
   else
-    sep ? go(launch_fused_kernel<true, float>) : go(launch_fused_kernel<false, float>);
+    launch_fused_ring<64, 5>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
+                             ring_k, ring_v, o_swa, lse, cps, G, st);
   return hipGetLastError();
 }
 

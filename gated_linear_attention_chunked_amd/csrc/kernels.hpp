@@ -40,21 +40,22 @@ hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const vo
                           const void* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st);
 
-// State pass of the GLA branch alone (bf16, dk = dv = 128): the local end states
+// State pass of the GLA branch alone (bf16, dk = dv in {64, 128}): the local end states
 // and decays of segments 0..G-2 into ws (same layout as launch_gla_fwd's
 // workspace); G segments of cps 64-token chunks each.
 hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const void* la,
                             void* ws, int* G, int* cps, hipStream_t st);
 
 // Both branches' outputs in one pass after launch_gla_state: o = o_gla + mix *
-// o_swa, hT (optional) and the decode window cache (optional).  Only for the
-// shapes hybrid_fused_ok accepts.
-bool hybrid_fused_ok(const Shape& s);
+// o_swa, hT (optional), the decode window cache (optional) and, with save, the
+// training outputs o_swa and lse (each optional).  Only for the shapes
+// hybrid_fused_ok accepts.
+bool hybrid_fused_ok(const Shape& s, bool save);
 // qw, kw: the window branch's queries and keys (both null: q, k).
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
                                const void* kw, const void* v, const void* la, const void* mk,
                                const void* mv, const float* h0, void* o, float* hT, void* ring_k,
-                               void* ring_v, void* ws, hipStream_t st);
+                               void* ring_v, void* o_swa, float* lse, void* ws, hipStream_t st);
 
 // Window + meta branch.  o = out_scale * o_swa (or o += out_scale * o_swa when
 // accumulate != 0); o_swa and lse are optional extra outputs.

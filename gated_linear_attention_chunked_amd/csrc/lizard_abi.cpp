@@ -182,10 +182,10 @@ lizard_status_t hybrid_fwd_impl(const lizard_desc_t* desc, const void* q, const 
   if (need > 0 && !ws) return LIZARD_E_NULL;
   if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
   hipError_t e = hipSuccess;
-  if (desc->T > 0 && !lse && !o_swa && lz::hybrid_fused_ok(s)) {
+  if (desc->T > 0 && lz::hybrid_fused_ok(s, lse || o_swa)) {
     // state pass, then both branches in one output pass (o written once)
     e = lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o, hT,
-                                ring_k, ring_v, ws, stream);
+                                ring_k, ring_v, o_swa, lse, ws, stream);
   } else if (desc->T > 0) {
     // GLA branch writes o = o_gla; the window branch then adds mix * o_swa in place
     e = lz::launch_gla_fwd(s, q, k, v, gate, h0, o, hT, ws, stream);
@@ -250,9 +250,10 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   if (n_tokens > 0 && (!q || !k || !v || !gate || !o)) return LIZARD_E_NULL;
   s.cu = cu_seqlens;
   s.n_tokens = n_tokens;
-  if (lz::hybrid_fused_ok(s))
+  if (lz::hybrid_fused_ok(s, false))
     return hip_status(lz::launch_hybrid_fused(s, q, k, q_w, k_w, v, gate, meta_k, meta_v, h0, o,
-                                              hT, ring_k, ring_v, ws, stream), stream);
+                                              hT, ring_k, ring_v, nullptr, nullptr, ws, stream),
+                      stream);
   // other shapes: the GLA branch writes o, the window branch adds mix * o_swa
   hipError_t e = lz::launch_gla_fwd(s, q, k, v, gate, h0, o, hT, ws, stream);
   if (e == hipSuccess)

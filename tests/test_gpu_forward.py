@@ -168,26 +168,33 @@ def test_sharp_softmax():
     run_and_check(1, 2, 200, 128, 128, 4, "bf16", scale=1.0, qk_mult=math.sqrt(128))
 
 
-# Single-pass hybrid (bf16, d = 128): one head per launch gives the most
+# Single-pass hybrid (bf16, d = 128 and 64): one head per launch gives the most
 # segments (one per 64-token chunk up to 16), so ring prologues at segment
-# starts, ragged tails and windows up to the ring's 129 keys are all crossed.
+# starts, ragged tails and windows up to the ring's 129 keys are all crossed;
+# at d = 64, w <= 65 takes the three-chunk ring and the pass also writes o_swa
+# and lse.
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("B,H,T,w,M", [(1, 1, 1, 128, 4), (1, 1, 31, 128, 0), (1, 1, 32, 33, 1),
                                        (1, 1, 33, 32, 16), (1, 1, 64, 31, 4), (1, 1, 95, 129, 4),
                                        (1, 1, 200, 1, 0), (1, 1, 300, 64, 4), (1, 1, 383, 100, 16),
+                                       (1, 1, 250, 65, 4), (1, 1, 250, 66, 4),
                                        (2, 3, 520, 128, 4), (1, 1, 2200, 128, 4)])
-def test_single_pass_hybrid_shapes(B, H, T, w, M):
-    run_and_check(B, H, T, 128, w, M, "bf16", h0=True, mix=0.7)
+def test_single_pass_hybrid_shapes(d, B, H, T, w, M):
+    run_and_check(B, H, T, d, w, M, "bf16", h0=True, mix=0.7)
 
 
-def test_single_pass_hybrid_steep_chunks():
+@pytest.mark.parametrize("d", [128, 64])
+def test_single_pass_hybrid_steep_chunks(d):
     # chunks of both gate ranges (single reference and sub-block) in one segment
-    run_and_check(1, 1, 1100, 128, 128, 4, "bf16", steep_chunks=True, h0=True)
-    run_and_check(1, 2, 700, 128, 129, 16, "bf16", gate_mean=-3.0)
+    run_and_check(1, 1, 1100, d, 128, 4, "bf16", steep_chunks=True, h0=True)
+    run_and_check(1, 2, 700, d, 129, 16, "bf16", gate_mean=-3.0)
+    run_and_check(1, 1, 600, d, 64, 4, "bf16", steep_chunks=True, h0=True, mix=-0.8)
 
 
-def test_outputs_fully_written_and_deterministic():
+@pytest.mark.parametrize("d,w", [(128, 128), (64, 64), (64, 100)])
+def test_outputs_fully_written_and_deterministic(d, w):
     # NaN-poisoned outputs must be overwritten; repeated calls agree bit for bit
-    B, H, T, d, w, M = 2, 3, 333, 128, 128, 4
+    B, H, T, M = 2, 3, 333, 4
     inp = to_dev(make_inputs(B, H, T, d, d, M, dtype="bf16", seed=5))
     dsc = lz.make_desc(B, H, T, d, d, w, M, None, 1.0, torch.bfloat16)
     nws = lz.workspace_bytes(dsc, _abi.OP_HYBRID_FWD)
@@ -233,3 +240,27 @@ def test_full_size_prefill_sampled_heads(name, heads):
                                     r["meta_v"], wl.window, wl.scale, mix=wl.mix)
         assert_close(f"o[b{b},h{h}]", out["o"][b:b + 1, h:h + 1], ref["o"], torch.bfloat16)
         assert_close(f"hT[b{b},h{h}]", out["hT"][b:b + 1, h:h + 1], ref["hT"], torch.bfloat16)
+
+
+def test_full_size_training_forward_sampled_heads():
+    # the training step's forward (B=8, H=16, T=2048, d=64, w=64, M=4) in the
+    # configuration the benchmark times: o, o_swa and lse saved for the backward
+    wl = WORKLOADS["train_bf16_b8_h16_t2048_d64"]
+    print("[case] train_bf16_b8_h16_t2048_d64 forward, heads (0,0) (7,15)", flush=True)
+    inp = make_inputs(wl.B, wl.H, wl.T, wl.dk, wl.dv, wl.n_meta, dtype=wl.dtype, seed=0)
+    x = to_dev(inp)
+    out = lz.hybrid_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["meta_k"], x["meta_v"],
+                        wl.window, scale=wl.scale, mix=wl.mix, save_for_backward=True)
+    torch.cuda.synchronize()
+    for n in ("o", "o_swa", "lse"):
+        assert torch.isfinite(out[n].float()).all(), n
+    for b, h in [(0, 0), (7, 15)]:
+        sl = {n: (t[b:b + 1, h:h + 1] if n not in ("meta_k", "meta_v") else t[h:h + 1])
+              for n, t in inp.items()}
+        r = f64(sl)
+        ref = oracle.hybrid_forward(r["q"], r["k"], r["v"], r["log_alpha"], r["meta_k"],
+                                    r["meta_v"], wl.window, wl.scale, mix=wl.mix)
+        hs = lambda t: t[b:b + 1, h:h + 1]
+        assert_close(f"o[b{b},h{h}]", hs(out["o"]), ref["o"], torch.bfloat16)
+        assert_close(f"o_swa[b{b},h{h}]", hs(out["o_swa"]), ref["o_swa"], torch.bfloat16)
+        assert_close(f"lse[b{b},h{h}]", hs(out["lse"]), ref["lse"], torch.bfloat16, tol=LSE_TOL)
