@@ -395,12 +395,20 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_dkdv(
 // (query, key) pair of the band exactly once.  Step i takes key tile i against
 // query tiles i (block A, on and below the diagonal) and i+1 (block B, above
 // it): dk_i and dv_i are then complete; dq_i is complete once block A is added
-// to what block B of step i-1 left; block B's dq part carries to step i+1.  A
-// segment starting at tile i0 > 0 first runs key tile i0-1 for that carry only.
+// to what block B of step i-1 left.  A segment starting at tile i0 > 0 first
+// runs key tile i0-1 for that carry only.
+// Eight waves: wave w owns keys 16(w & 3).. of the key tile (rows in registers,
+// one key per lane) against query rows 32(w >> 2).. of both blocks, so every
+// wave meets at most three of the 16x16 (query, key) blocks that reach the
+// band.  The two waves of a key block swap partial sums through LDS: the first
+// completes dk, the second dv.  dS of both blocks passes through LDS for dq,
+// which wave w computes for query rows 16(w & 3).. of tile i (waves of group
+// i & 1) or tile i+1 (the other group): query tile j's dq is thus made by group
+// j & 1 in both steps that touch it, and its block-B part stays in registers.
 // Query tiles sit in a two-slot LDS ring (tile j in slot j & 1), loaded one
-// step ahead; the key tile's rows stay in registers (one key per lane) and its
-// transpose goes to LDS.  dS of both blocks passes through LDS for dq.
+// step ahead; K^T goes to LDS.
 constexpr int kTE = kT * kD;  // elements of one 64 x 64 tile
+constexpr int kStreamThreads = 512;
 
 // Tiles use swz64 (64-element rows); a fragment of rows 16a..16a+15 at
 // columns 32p + 8g.. is read at 1024 a + fb[p] with fb the lane's base.
@@ -417,11 +425,13 @@ struct StreamSmem {
   bf16 mkr[16 * kD];  // meta keys [m][c] (rows >= M zero)
   bf16 mvr[16 * kD];  // meta values [m][j]
   bf16 mkT[kD * 16];  // meta keys transposed [c][m], plain
-  f32x4 macc[4][8][64];  // per wave: meta-gradient partials, quad j of lane l at [j][l]
-  float red[2 * kD][17];
+  union {
+    f32x4 x[2][4][4][64];  // dk (0) / dv (1) partials: [key block][channel block][lane]
+    float red[2 * kD][17];  // final meta-gradient sums
+  } u;
 };
 
-__global__ __launch_bounds__(kThreads) void swa_bwd_stream(
+__global__ __launch_bounds__(kStreamThreads) void swa_bwd_stream(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ mk, const bf16* __restrict__ mv, const bf16* __restrict__ o_swa,
     const float* __restrict__ lse, const bf16* __restrict__ dO, bf16* __restrict__ dq,
@@ -429,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
     int W, int M, float scale, float mix, int per) {
   __shared__ __attribute__((aligned(16))) StreamSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int grp = w >> 2, wl = w & 3;  // query half and key block of this wave
   const int r16 = lane & 15, g = lane >> 4, odd = tid & 1;
   const int seg = blockIdx.x, nseg = gridDim.x, bh = blockIdx.y, h = bh % H;
   const int ntiles = (T_len + kT - 1) / kT;
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
 
   // meta slots (zero past M)
   if (M > 0) {
-    for (int e = tid; e < 16 * kD; e += kThreads) {
+    for (int e = tid; e < 16 * kD; e += kStreamThreads) {
       const int m = e / kD, c = e % kD;
       const bf16 kk = m < M ? mk[((size_t)h * M + m) * kD + c] : (bf16)0.f;
       const bf16 vv = m < M ? mv[((size_t)h * M + m) * kD + c] : (bf16)0.f;
@@ -455,73 +466,61 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
     }
   }
 
-  // query tile j: rows, transposes, lse and D.  Piece p of the 512 16-byte
-  // pieces is token (p & 1) | 2 (p >> 4), granule (p >> 1) & 7, so neighbouring
+  // query tile j: rows, transposes, lse and D.  Thread p takes the 16-byte
+  // piece of token (p & 1) | 2 (p >> 4), granule (p >> 1) & 7, so neighbouring
   // lanes hold neighbouring tokens of one granule.
-  int pt[2], po[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int p = tid + kThreads * hh;
-    pt[hh] = (p & 1) | ((p >> 4) << 1);
-    po[hh] = (p >> 1) & 7;
-  }
+  const int pt = (tid & 1) | ((tid >> 4) << 1), po = (tid >> 1) & 7;
   struct QIn {
-    u32x4 q[2], d[2], o[2];
+    u32x4 q, d, o;
     u32 lse;
   };
   auto qload = [&](QIn& x, int j) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const u32 e = ((u32)(j * kT + pt[hh]) * kD + 8 * po[hh]) * 2;
-      x.q[hh] = bq.ld128(e);
-      x.d[hh] = bdo.ld128(e);
-      x.o[hh] = bo.ld128(e);
-    }
+    const u32 e = ((u32)(j * kT + pt) * kD + 8 * po) * 2;
+    x.q = bq.ld128(e);
+    x.d = bdo.ld128(e);
+    x.o = bo.ld128(e);
     x.lse = blse.ld32((u32)(j * kT + (tid & 63)) * 4);
   };
-  auto transpose_store = [&](bf16* dstT, const u32x4& x, int hh) {
+  auto transpose_store = [&](bf16* dstT, const u32x4& x) {
     const u32 w0 = x[0], w1 = x[1], w2 = x[2], w3 = x[3];
     const u32 r0 = dpp_swap1(odd ? w0 : w2), r1 = dpp_swap1(odd ? w1 : w3);
     const u32 f0 = odd ? r0 : w0, f1 = odd ? r1 : w1;  // words of the even token
     const u32 s0 = odd ? w2 : r0, s1 = odd ? w3 : r1;  // words of the odd token
-    const int j0 = 8 * po[hh] + 4 * odd, tc = split_pos(pt[hh] & ~1);
+    const int j0 = 8 * po + 4 * odd, tc = split_pos(pt & ~1);
     *reinterpret_cast<u32*>(&dstT[swz64(j0 + 0, tc)]) = lo2(f0, s0);
     *reinterpret_cast<u32*>(&dstT[swz64(j0 + 1, tc)]) = hi2(f0, s0);
     *reinterpret_cast<u32*>(&dstT[swz64(j0 + 2, tc)]) = lo2(f1, s1);
     *reinterpret_cast<u32*>(&dstT[swz64(j0 + 3, tc)]) = hi2(f1, s1);
   };
   auto qstore = [&](const QIn& x, int slot) {
+    *reinterpret_cast<u32x4*>(&sm.qr[slot][swz64(pt, 8 * po)]) = x.q;
+    *reinterpret_cast<u32x4*>(&sm.dor[slot][swz64(pt, 8 * po)]) = x.d;
+    transpose_store(sm.qT[slot], x.q);
+    transpose_store(sm.doT[slot], x.d);
+    float dot = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      *reinterpret_cast<u32x4*>(&sm.qr[slot][swz64(pt[hh], 8 * po[hh])]) = x.q[hh];
-      *reinterpret_cast<u32x4*>(&sm.dor[slot][swz64(pt[hh], 8 * po[hh])]) = x.d[hh];
-      transpose_store(sm.qT[slot], x.q[hh], hh);
-      transpose_store(sm.doT[slot], x.d[hh], hh);
-      float dot = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += bf_at(x.d[hh], e) * bf_at(x.o[hh], e);
-      // the 8 lanes of one token differ in lane bits 1..3
-      dot += __shfl_xor(dot, 2);
-      dot += __shfl_xor(dot, 4);
-      dot += __shfl_xor(dot, 8);
-      if (po[hh] == 0) sm.Dt[slot][pt[hh]] = mix * dot;
-    }
+    for (int e = 0; e < 8; ++e) dot += bf_at(x.d, e) * bf_at(x.o, e);
+    // the 8 lanes of one token differ in lane bits 1..3
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    dot += __shfl_xor(dot, 8);
+    if (po == 0) sm.Dt[slot][pt] = mix * dot;
     if (tid < kT) sm.lse2[slot][tid] = as_f(x.lse) * kLog2e;
   };
-  // key tile i: lane (r16, g) of wave w holds key 16w + r16, channels 32p + 8g..
+  // key tile i: lane (r16, g) of wave w holds key 16(w & 3) + r16, channels 32p + 8g..
   struct KIn {
     u32x4 k[2], v[2];
   };
   auto kload = [&](KIn& x, int i) {
-    const u32 e = (u32)(i * kT + 16 * w + r16) * kD;
+    const u32 e = (u32)(i * kT + 16 * wl + r16) * kD;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       x.k[p] = bk.ld128((e + 32 * p + 8 * g) * 2);
       x.v[p] = bv.ld128((e + 32 * p + 8 * g) * 2);
     }
   };
-  const int se = 16 * w + (r16 & ~1);  // even key of this lane's pair
-  auto kstore = [&](const KIn& x) {    // K^T [c][s] from key pairs in neighbouring lanes
+  const int se = 16 * wl + (r16 & ~1);  // even key of this lane's pair
+  auto kstore = [&](const KIn& x) {     // K^T [c][s] from key pairs in neighbouring lanes
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const u32 w0 = x.k[p][0], w1 = x.k[p][1], w2 = x.k[p][2], w3 = x.k[p][3];
@@ -535,27 +534,28 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
       *reinterpret_cast<u32*>(&sm.kT[swz64(j0 + 3, se)]) = hi2(f1, s1);
     }
   };
-  // dS of four 16-row tiles ([t = 16qb + 4g + r][s = 16w + r16]) into a [t][s]
-  // tile: neighbouring lanes (keys s, s+1) write (s, s+1) pairs, the even lane
-  // rows 4g, 4g+1 and the odd lane rows 4g+2, 4g+3
-  auto ds_store = [&](bf16* dst, const f32x4 (&x)[4]) {
+  // dS of this wave's two 16-row tiles ([t = 16(2grp + u) + 4g + r][s = 16wl +
+  // r16]) into a [t][s] tile: neighbouring lanes (keys s, s+1) write (s, s+1)
+  // pairs, the even lane rows 4g, 4g+1 and the odd lane rows 4g+2, 4g+3
+  auto ds_store = [&](bf16* dst, const f32x4 (&x)[2]) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const u32 a01 = pack_bf2(x[qb][0], x[qb][1]), a23 = pack_bf2(x[qb][2], x[qb][3]);
+    for (int u = 0; u < 2; ++u) {
+      const u32 a01 = pack_bf2(x[u][0], x[u][1]), a23 = pack_bf2(x[u][2], x[u][3]);
       const u32 R = dpp_swap1(odd ? a01 : a23);
       const u32 fst = odd ? R : a01, snd = odd ? a23 : R;
-      const int row = 16 * qb + 4 * g + 2 * odd;
+      const int row = 16 * (2 * grp + u) + 4 * g + 2 * odd;
       *reinterpret_cast<u32*>(&dst[swz64(row, se)]) = lo2(fst, snd);
       *reinterpret_cast<u32*>(&dst[swz64(row + 1, se)]) = hi2(fst, snd);
     }
   };
 
-  f32x4 dqc[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) dqc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sm.macc[w][j][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dqc[4];   // block-B part of dq for query rows 16wl.. of this group's next tile
+  f32x4 macc[8];  // meta-gradient partials (dk part 0..3, dv part 4..7), quad per lane
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) dqc[ct] = zero;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) macc[j] = zero;
   const int start = i0 > 0 ? i0 - 1 : i0;
   QIn qx;
   KIn kx;
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
   qstore(qx, start & 1);
   qload(qx, start + 1);
   qstore(qx, (start + 1) & 1);
-  kstore(kx);
+  if (grp == 0) kstore(kx);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     kf[p] = as_bf8(kx.k[p]);
@@ -579,9 +579,10 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
     const bool pq = i + 2 <= i1, pk = i + 1 < i1;
     if (pq) qload(qx, i + 2);
     if (pk) kload(kx, i + 1);
-    const int s_lo = i * kT + 16 * w, sg = s_lo + r16;  // this lane's key
-    // ---- block A (queries of tile i, slot a), then block B (tile i+1, slot b):
-    // scores with the key per lane, dS to LDS for dq, and dk, dv of key tile i
+    const int s_lo = i * kT + 16 * wl, sg = s_lo + r16;  // this lane's key
+    // ---- blocks A (queries of tile i, slot a) and B (tile i+1, slot b), query
+    // rows 32grp..32grp+31: scores with the key per lane, dS to LDS for dq, and
+    // this wave's part of dk, dv of key tile i
     f32x4 dkT[4], dvT[4];  // [c or j = 16ct + 4g + r][key]
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) dkT[ct] = dvT[ct] = zero;
@@ -589,17 +590,18 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
     for (int blk = 0; blk < 2; ++blk) {
       if (blk == 0 && pre) continue;
       const int sl = blk == 0 ? a : b;
-      f32x4 P[4], dS[4];
-      bool act[4];
+      f32x4 P[2], dS[2];
+      bool act[2];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        P[qb] = dS[qb] = zero;
+      for (int u = 0; u < 2; ++u) {
+        const int qb = 2 * grp + u;
+        P[u] = dS[u] = zero;
         const int t_lo = (i + blk) * kT + 16 * qb;
-        act[qb] = (blk == 1 || t_lo + 15 >= s_lo) && t_lo - (s_lo + 15) < W && t_lo < T_len &&
-                  s_lo < T_len;
+        act[u] = (blk == 1 || t_lo + 15 >= s_lo) && t_lo - (s_lo + 15) < W && t_lo < T_len &&
+                 s_lo < T_len;
         const bool full = (blk == 1 || t_lo > s_lo + 15) && t_lo + 15 - s_lo < W &&
                           t_lo + 15 < T_len && s_lo + 15 < T_len;
-        if (act[qb]) {
+        if (act[u]) {
           f32x4 sc = zero, dp = zero;
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -612,8 +614,8 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float pr = exp2_fast(sc[r] * sl2 - l4[r]);
-              P[qb][r] = pr;
-              dS[qb][r] = pr * (mix * dp[r] - d4[r]);
+              P[u][r] = pr;
+              dS[u][r] = pr * (mix * dp[r] - d4[r]);
             }
           } else {
 #pragma unroll
@@ -621,60 +623,65 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
               const int t = t_lo + 4 * g + r;
               const bool ok = sg <= t && t - sg < W && t < T_len && sg < T_len;
               const float pr = ok ? exp2_fast(sc[r] * sl2 - l4[r]) : 0.f;
-              P[qb][r] = pr;
-              dS[qb][r] = pr * (mix * dp[r] - d4[r]);
+              P[u][r] = pr;
+              dS[u][r] = pr * (mix * dp[r] - d4[r]);
             }
           }
         }
       }
       ds_store(blk == 0 ? sm.dsA : sm.dsB, dS);
-      if (!pre) {
+      if (!pre && (act[0] || act[1])) {
+        const bf16x8 bs = pack_acc<bf16>(dS[0], dS[1]);
+        const bf16x8 bp = pack_acc<bf16>(P[0], P[1]);
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          if (act[2 * pp] || act[2 * pp + 1]) {
-            const bf16x8 bs = pack_acc<bf16>(dS[2 * pp], dS[2 * pp + 1]);
-            const bf16x8 bp = pack_acc<bf16>(P[2 * pp], P[2 * pp + 1]);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              mma(dkT[ct], frag(sm.qT[sl], ct, pp), bs);
-              mma(dvT[ct], frag(sm.doT[sl], ct, pp), bp);
-            }
-          }
+        for (int ct = 0; ct < 4; ++ct) {
+          mma(dkT[ct], frag(sm.qT[sl], ct, grp), bs);
+          mma(dvT[ct], frag(sm.doT[sl], ct, grp), bp);
         }
       }
     }
+    // the first query half hands over its dv part, the second its dk part
+    if (!pre) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) sm.u.x[grp == 0 ? 1 : 0][wl][ct][lane] = grp == 0 ? dvT[ct] : dkT[ct];
+    }
+    lds_barrier();
+    // ---- dk (first query half) or dv (second) of key tile i complete
     if (!pre && sg < T_len) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        st4<bf16>(dk + off + (size_t)sg * kD + 16 * ct + 4 * g, dkT[ct] * scale);
-        st4<bf16>(dv + off + (size_t)sg * kD + 16 * ct + 4 * g, dvT[ct] * mix);
+        if (grp == 0)
+          st4<bf16>(dk + off + (size_t)sg * kD + 16 * ct + 4 * g, (dkT[ct] + sm.u.x[0][wl][ct][lane]) * scale);
+        else
+          st4<bf16>(dv + off + (size_t)sg * kD + 16 * ct + 4 * g, (dvT[ct] + sm.u.x[1][wl][ct][lane]) * mix);
       }
     }
-    lds_barrier();
-    // ---- dq: wave w takes queries 16w + r16 of tiles i (block A) and i+1 (block B)
-    {
-      f32x4 dqi[4], dqn[4];  // [c = 16ct + 4g + r][query]
+    // ---- dq: group a takes query rows 16wl.. of tile i (block A), the other
+    // group those of tile i+1 (block B)
+    const bool dqA = grp == a;
+    if (!(dqA && pre)) {
+      f32x4 dqx[4];  // [c = 16ct + 4g + r][query]
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dqi[ct] = dqn[ct] = zero;
+      for (int ct = 0; ct < 4; ++ct) dqx[ct] = zero;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const bf16x8 fa = frag(sm.dsA, w, p), fbb = frag(sm.dsB, w, p);
+        const bf16x8 fd = frag(dqA ? sm.dsA : sm.dsB, wl, p);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const bf16x8 kt = frag(sm.kT, ct, p);
-          if (!pre) mma(dqi[ct], kt, fa);
-          mma(dqn[ct], kt, fbb);
-        }
+        for (int ct = 0; ct < 4; ++ct) mma(dqx[ct], frag(sm.kT, ct, p), fd);
       }
-      if (!pre) {
-        const int tl = 16 * w + r16, tg = i * kT + tl;
+      if (!dqA) {
+        // block B: the part of dq that tile i+1 gets from key tile i
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) dqc[ct] = dqx[ct];
+      } else {
+        const int tl = 16 * wl + r16, tg = i * kT + tl;
         if (M > 0) {
           // meta slots, query per lane: dq term
           bf16x8 qf[2], df[2];
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            qf[p] = frag(sm.qr[a], w, p);
-            df[p] = frag(sm.dor[a], w, p);
+            qf[p] = frag(sm.qr[a], wl, p);
+            df[p] = frag(sm.dor[a], wl, p);
           }
           f32x4 sc = zero, dp = zero;  // [slot 4g + r][query]
 #pragma unroll
@@ -695,52 +702,47 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
             const bf16x4 m4 = *reinterpret_cast<const bf16x4*>(&sm.mkT[(16 * ct + r16) * 16 + 4 * g]);
-            mma(dqi[ct], bf16x8{m4[0], m4[1], m4[2], m4[3], z, z, z, z}, bds);
+            mma(dqx[ct], bf16x8{m4[0], m4[1], m4[2], m4[3], z, z, z, z}, bds);
           }
           // slot per lane: this wave's 16 queries' share of the meta gradients
-          f32x4 s2 = zero, dp2 = zero;  // [query 16w + 4g + r][slot r16]
+          f32x4 s2 = zero, dp2 = zero;  // [query 16wl + 4g + r][slot r16]
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             mma(s2, qf[p], frag(sm.mkr, 0, p));
             mma(dp2, df[p], frag(sm.mvr, 0, p));
           }
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[a][16 * w + 4 * g]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.Dt[a][16 * w + 4 * g]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[a][16 * wl + 4 * g]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.Dt[a][16 * wl + 4 * g]);
           f32x4 p2, ds2;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const bool ok = r16 < M && i * kT + 16 * w + 4 * g + r < T_len;
+            const bool ok = r16 < M && i * kT + 16 * wl + 4 * g + r < T_len;
             p2[r] = ok ? exp2_fast(s2[r] * sl2 - l4[r]) : 0.f;
             ds2[r] = p2[r] * (mix * dp2[r] - d4[r]);
           }
           const bf16x8 b2 = pack_acc<bf16>(ds2, zero), bp2 = pack_acc<bf16>(p2, zero);
-          // queries 16w + 4g + e sit at split position 32(w >> 1) + 8g + 4(w & 1) + e
-          const int fm = swz64(r16, 32 * (w >> 1) + 8 * g + 4 * (w & 1));
+          // queries 16wl + 4g + e sit at split position 32(wl >> 1) + 8g + 4(wl & 1) + e
+          const int fm = swz64(r16, 32 * (wl >> 1) + 8 * g + 4 * (wl & 1));
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
             const bf16x4 aq = *reinterpret_cast<const bf16x4*>(&sm.qT[a][1024 * ct + fm]);
             const bf16x4 ao = *reinterpret_cast<const bf16x4*>(&sm.doT[a][1024 * ct + fm]);
-            f32x4 ak = sm.macc[w][ct][lane], av = sm.macc[w][4 + ct][lane];
-            mma(ak, bf16x8{aq[0], aq[1], aq[2], aq[3], z, z, z, z}, b2);
-            mma(av, bf16x8{ao[0], ao[1], ao[2], ao[3], z, z, z, z}, bp2);
-            sm.macc[w][ct][lane] = ak;
-            sm.macc[w][4 + ct][lane] = av;
+            mma(macc[ct], bf16x8{aq[0], aq[1], aq[2], aq[3], z, z, z, z}, b2);
+            mma(macc[4 + ct], bf16x8{ao[0], ao[1], ao[2], ao[3], z, z, z, z}, bp2);
           }
         }
         if (tg < T_len) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            st4<bf16>(dq + off + (size_t)tg * kD + 16 * ct + 4 * g, (dqc[ct] + dqi[ct]) * scale);
+            st4<bf16>(dq + off + (size_t)tg * kD + 16 * ct + 4 * g, (dqc[ct] + dqx[ct]) * scale);
         }
       }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dqc[ct] = dqn[ct];
     }
     lds_barrier();
     // ---- the prefetched tiles into the freed slots
     if (pq) qstore(qx, a);  // query tile i + 2
     if (pk) {
-      kstore(kx);
+      if (grp == 0) kstore(kx);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         kf[p] = as_bf8(kx.k[p]);
@@ -752,24 +754,24 @@ __global__ __launch_bounds__(kThreads) void swa_bwd_stream(
 
   // ---- meta partials of this (sequence, segment), waves added in a fixed order
   if (M > 0) {
-    for (int wv = 0; wv < 4; ++wv) {
+    for (int wv = 0; wv < 8; ++wv) {
       if (w == wv) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int cc = 16 * ct + 4 * g + r;
-            const float x0 = scale * sm.macc[w][ct][lane][r], x1 = mix * sm.macc[w][4 + ct][lane][r];
-            sm.red[cc][r16] = (wv == 0 ? 0.f : sm.red[cc][r16]) + x0;
-            sm.red[kD + cc][r16] = (wv == 0 ? 0.f : sm.red[kD + cc][r16]) + x1;
+            const float x0 = scale * macc[ct][r], x1 = mix * macc[4 + ct][r];
+            sm.u.red[cc][r16] = (wv == 0 ? 0.f : sm.u.red[cc][r16]) + x0;
+            sm.u.red[kD + cc][r16] = (wv == 0 ? 0.f : sm.u.red[kD + cc][r16]) + x1;
           }
       }
       __syncthreads();
     }
     float* mp = metap + ((size_t)bh * nseg + seg) * (size_t)M * 2 * kD;
-    for (int e = tid; e < M * 2 * kD; e += kThreads) {
+    for (int e = tid; e < M * 2 * kD; e += kStreamThreads) {
       const int which = e / (M * kD), rem = e % (M * kD), m = rem / kD, cc = rem % kD;
-      mp[e] = sm.red[which * kD + cc][m];
+      mp[e] = sm.u.red[which * kD + cc][m];
     }
   }
 }
@@ -839,7 +841,7 @@ hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, co
   if constexpr (sizeof(T) == 2 && D == 64) {
     if (s.window <= 65 && s.hlen == 0 && s.tlen == 0) {
       // streaming form: B*H*G work-groups, G segments of whole tiles per sequence
-      hipLaunchKernelGGL(swa_bwd_stream, dim3(G, BH), dim3(kThreads), 0, st, (const T*)q,
+      hipLaunchKernelGGL(swa_bwd_stream, dim3(G, BH), dim3(kStreamThreads), 0, st, (const T*)q,
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa,
                          lse, (const T*)dO, (T*)dq, (T*)dk, (T*)dv, metap, s.T, s.H, s.window,
                          s.n_meta, s.scale, s.mix, per);
