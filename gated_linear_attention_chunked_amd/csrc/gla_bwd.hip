@@ -60,10 +60,13 @@ __device__ __forceinline__ int frag_major(int row, int col) {
 // dS_{c+1}, the state gradient leaving chunk c):
 //   S_{c+1} = D_c S_c + K^_c^T V_c,   dS_c = D_c dS_{c+1} + Q^_c^T dO_c,
 // D_c = diag(2^{b_last}), K^_s = k_s 2^{b_last - b_s}, Q^_t = q_t 2^{b_t}.
-// Gating: wave w owns channels 16w..16w+15 and lane l token l of the chunk, so
-// the cumsum over the chunk is one 64-lane scan (row shifts, then the row
-// broadcasts of lanes 15 and 31) and b_last is lane 63's value.  The next
-// chunk's inputs are loaded two steps ahead into alternating register sets.
+// Eight waves.  Gating: wave w owns channels 8w..8w+7 and lane l token l of the
+// chunk, so the cumsum over the chunk is one 64-lane scan (row shifts, then the
+// row broadcasts of lanes 15 and 31) and b_last is lane 63's value.  Update:
+// wave w owns the 16x16 state tiles of channels 16(w >> 1).. and value columns
+// 32(w & 1)..  The next chunk's inputs are loaded two steps ahead into
+// alternating register sets.
+constexpr int kScanThreads = 512;
 struct ScanSmem {
   bf16 xT[2][kTile];  // gated k (or q) transposed [c][t]
   bf16 yT[2][kTile];  // v (or dO) transposed [j][t]
@@ -87,7 +90,7 @@ __device__ __forceinline__ float wave_scan64(float x) {
 // leaves the gradient entering chunk c0 in rend (null = not stored); chunk c's
 // states go to slot c - c0 of the L per head.
 template <typename GT>
-__global__ __launch_bounds__(kThreads) void gla_bwd_scans(
+__global__ __launch_bounds__(kScanThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const GT* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ fstart,
     size_t fstride, const float* __restrict__ rstart, float* __restrict__ rend,
@@ -103,47 +106,44 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb),
       bla(la + off, nb / 2 * (u32)sizeof(GT));
   const int nc = c1 - c0;                 // chunks of this block
-  const int cw = 16 * w;                  // this wave's first channel
+  const int cw = 8 * w;                   // this wave's first gating channel
+  const int cb = w >> 1, jh = 2 * (w & 1);  // its state tiles: channels 16cb.., value blocks jh, jh+1
   const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
 
-  // a1[jb]: [j = 16jb + 4g + r][c = 16w + r16] (the state, transposed)
-  f32x4 a1[4];
+  // a1[u]: [j = 16(jh + u) + 4g + r][c = 16cb + r16] (the state, transposed)
+  f32x4 a1[2];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) a1[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u) a1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the forward scan starts from fstart (h0 or the block's entry state), the
   // reverse scan from rstart (dhT, the gradient of the final state, or the
   // gradient leaving the block), all [c][j] row-major; absent ones are zero
   const float* start = rev ? rstart : fstart;
   if (start) {
     const float* hp = start + (size_t)bh * (rev ? (size_t)kD * kD : fstride) +
-                      (size_t)(cw + r16) * kD + 4 * g;
+                      (size_t)(16 * cb + r16) * kD + 4 * g;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) a1[jb] = *reinterpret_cast<const f32x4*>(hp + 16 * jb);
+    for (int u = 0; u < 2; ++u) a1[u] = *reinterpret_cast<const f32x4*>(hp + 16 * (jh + u));
   }
-  // lane = token of the chunk; 16 channels from cw
+  // lane = token of the chunk; 8 channels from cw
   struct In {
-    Gate8<GT> la[2];
-    u32x4 x[2], y[2];
+    Gate8<GT> la;
+    u32x4 x, y;
   };
   auto load = [&](In& d, int ch) {
     const u32 e = (u32)(ch * kC + lane) * kD + cw;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) d.la[i].load(bla, e + 8 * i);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      d.x[i] = bx.ld128((e + 8 * i) * 2);
-      d.y[i] = by.ld128((e + 8 * i) * 2);
-    }
+    d.la.load(bla, e);
+    d.x = bx.ld128(e * 2);
+    d.y = by.ld128(e * 2);
   };
   const int te = lane & ~1;
-  // 16 channels of tokens (lane, lane ^ 1) as (even, odd) token pairs: the
-  // even lane writes channels cw..cw+7, the odd lane cw+8..cw+15
-  auto tstore = [&](bf16* dstT, const u32 (&X)[8]) {
+  // 8 channels of tokens (lane, lane ^ 1) as (even, odd) token pairs: the
+  // even lane writes channels cw..cw+3, the odd lane cw+4..cw+7
+  auto tstore = [&](bf16* dstT, const u32 (&X)[4]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const u32 R = dpp_swap1(odd ? X[m] : X[4 + m]);
-      const u32 fst = odd ? R : X[m], snd = odd ? X[4 + m] : R;
-      const int c = cw + 8 * odd + 2 * m;
+    for (int m = 0; m < 2; ++m) {
+      const u32 R = dpp_swap1(odd ? X[m] : X[2 + m]);
+      const u32 fst = odd ? R : X[m], snd = odd ? X[2 + m] : R;
+      const int c = cw + 4 * odd + 2 * m;
       *reinterpret_cast<u32*>(&dstT[swz64(c, te)]) = lo2(fst, snd);
       *reinterpret_cast<u32*>(&dstT[swz64(c + 1, te)]) = hi2(fst, snd);
     }
@@ -152,28 +152,28 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   auto step = [&](In& d, int n) {
     const int ch = chunk_at(n), buf = n & 1;
     // gate cumsum over the chunk, per channel
-    float b[16];
+    float b[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-      b[c] = wave_scan64(gate_row<GT>(d.la[c >> 3].log2_at(c & 7), ch * kC + lane < T_len));
-    float bl[16];
+    for (int c = 0; c < 8; ++c)
+      b[c] = wave_scan64(gate_row<GT>(d.la.log2_at(c), ch * kC + lane < T_len));
+    float bl[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
+    for (int c = 0; c < 8; ++c)
       bl[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b[c]), 63));
-    if (lane < 16) {
+    if (lane < 8) {
       float dl = 0.f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dl = lane == c ? bl[c] : dl;
+      for (int c = 0; c < 8; ++c) dl = lane == c ? bl[c] : dl;
       sm.dec[buf][cw + lane] = exp2_fast(dl);
     }
-    u32 X[8], Y[8];
+    u32 X[4], Y[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const u32 xw = d.x[m >> 2][m & 3];
+    for (int m = 0; m < 4; ++m) {
+      const u32 xw = d.x[m];
       const float f0 = exp2_fast(rev ? b[2 * m] : bl[2 * m] - b[2 * m]);
       const float f1 = exp2_fast(rev ? b[2 * m + 1] : bl[2 * m + 1] - b[2 * m + 1]);
       X[m] = pack_bf2(bf_lo(xw) * f0, bf_hi(xw) * f1);
-      Y[m] = d.y[m >> 2][m & 3];
+      Y[m] = d.y[m];
     }
     tstore(sm.xT[buf], X);
     tstore(sm.yT[buf], Y);
@@ -185,26 +185,26 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
     {
       const size_t so = ((size_t)bh * L + (ch - c0)) * kTile;
       bf16* dst = (rev ? dS_all : S_all) + so;
-      u32x2 w1[4];
+      u32x2 w1[2];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-        w1[jb] = u32x2{pack_bf2(a1[jb][0], a1[jb][1]), pack_bf2(a1[jb][2], a1[jb][3])};
+      for (int u = 0; u < 2; ++u)
+        w1[u] = u32x2{pack_bf2(a1[u][0], a1[u][1]), pack_bf2(a1[u][2], a1[u][3])};
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-        *reinterpret_cast<u32x2*>(dst + frag_major(cw + r16, 16 * jb + 4 * g)) = w1[jb];
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<u32x2*>(dst + frag_major(16 * cb + r16, 16 * (jh + u) + 4 * g)) = w1[u];
     }
     lds_barrier();
     // decay, then add this chunk's outer products
-    const float d1 = sm.dec[buf][cw + r16];
-    const bf16* xb = sm.xT[buf] + 1024 * w;
+    const float d1 = sm.dec[buf][16 * cb + r16];
+    const bf16* xb = sm.xT[buf] + 1024 * cb;
     const bf16x8 xf0 = ld8<bf16>(xb + fb0), xf1 = ld8<bf16>(xb + fb1);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      a1[jb] *= d1;
-      const bf16* yb = sm.yT[buf] + 1024 * jb;
+    for (int u = 0; u < 2; ++u) {
+      a1[u] *= d1;
+      const bf16* yb = sm.yT[buf] + 1024 * (jh + u);
       const bf16x8 y0 = ld8<bf16>(yb + fb0), y1 = ld8<bf16>(yb + fb1);
-      mma(a1[jb], y0, xf0);
-      mma(a1[jb], y1, xf1);
+      mma(a1[u], y0, xf0);
+      mma(a1[u], y1, xf1);
     }
   };
   In A, B;
@@ -218,9 +218,9 @@ __global__ __launch_bounds__(kThreads) void gla_bwd_scans(
   }
   // after chunk c0 the reverse scan holds dS_{c0}, the gradient entering the block
   if (rev && rend) {
-    float* hp = rend + (size_t)bh * kD * kD + (size_t)(cw + r16) * kD + 4 * g;
+    float* hp = rend + (size_t)bh * kD * kD + (size_t)(16 * cb + r16) * kD + 4 * g;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) *reinterpret_cast<f32x4*>(hp + 16 * jb) = a1[jb];
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<f32x4*>(hp + 16 * (jh + u)) = a1[u];
   }
 }
 
@@ -701,7 +701,7 @@ hipError_t launch_gla_bwd_block(const Shape& s, const void* q, const void* k, co
   const int BH = s.B * s.H;
   auto go = [&](auto gate_type) {
     typedef decltype(gate_type) GT;
-    hipLaunchKernelGGL(gla_bwd_scans<GT>, dim3(2 * BH), dim3(kThreads), 0, st, (const T*)q,
+    hipLaunchKernelGGL(gla_bwd_scans<GT>, dim3(2 * BH), dim3(kScanThreads), 0, st, (const T*)q,
                        (const T*)k, (const T*)v, (const GT*)la, (const T*)dO, fstart, fstride,
                        rstart, rend, (T*)S_ws, (T*)dS_ws, BH, s.T, c0, c1, L);
     auto kern = add_qk ? gla_bwd_chunk<true, GT> : gla_bwd_chunk<false, GT>;
