@@ -142,6 +142,12 @@ struct Buf {
 __device__ __forceinline__ float as_f(u32 x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ float bf_lo(u32 x) { return as_f(x << 16); }
 __device__ __forceinline__ float bf_hi(u32 x) { return as_f(x & 0xffff0000u); }
+// acc + lo(x) lo(y) + hi(x) hi(y) for two packed bf16 pairs (one dot instruction)
+__device__ __forceinline__ float dot2_bf16(u32 x, u32 y, float acc) {
+  typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2v, x), __builtin_bit_cast(bf2v, y),
+                                         acc, false);
+}
 // bf16 element c (0..7) of a 16-byte word as fp32
 __device__ __forceinline__ float bf_at(const u32x4& v, int c) {
   const u32 w = v[c >> 1];

@@ -504,19 +504,19 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
       }
     }
   }
-  // state term (wave 0; S_c is not needed after this)
-  if (w == 0) {
+  // state term, rows 16w.. by wave w (S_c is not needed after this)
+  {
+    float pc = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      float pc = 0.f;
+    for (int ct = 0; ct < 4; ++ct)
+      if (ct == w)  // uniform over the wave
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pc += bf_at(Sf[ct][p], e) * bf_at(dSf[ct][p], e);
-      pc += __shfl_xor(pc, 16);
-      pc += __shfl_xor(pc, 32);
-      if (g == 0) sm.st[16 * ct + r16] = pc * exp2_fast(sm.bl[16 * ct + r16]);
-    }
+          for (int e = 0; e < 4; ++e) pc = dot2_bf16(Sf[ct][p][e], dSf[ct][p][e], pc);
+    pc += __shfl_xor(pc, 16);
+    pc += __shfl_xor(pc, 32);
+    if (g == 0) sm.st[16 * w + r16] = pc * exp2_fast(sm.bl[16 * w + r16]);
   }
   // dS_{c+1} transposed into LDS for the dv inter product: neighbouring lanes
   // hold rows c, c+1; the even lane writes (c, c+1) pairs of columns j0..j0+3,

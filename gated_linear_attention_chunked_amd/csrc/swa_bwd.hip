@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kStreamThreads) void swa_bwd_stream(
     transpose_store(sm.doT[slot], x.d);
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dot += bf_at(x.d, e) * bf_at(x.o, e);
+    for (int e = 0; e < 4; ++e) dot = dot2_bf16(x.d[e], x.o[e], dot);
     // the 8 lanes of one token differ in lane bits 1..3
     dot += __shfl_xor(dot, 2);
     dot += __shfl_xor(dot, 4);
