@@ -60,30 +60,21 @@ __device__ __forceinline__ int frag_major(int row, int col) {
 // dS_{c+1}, the state gradient leaving chunk c):
 //   S_{c+1} = D_c S_c + K^_c^T V_c,   dS_c = D_c dS_{c+1} + Q^_c^T dO_c,
 // D_c = diag(2^{b_last}), K^_s = k_s 2^{b_last - b_s}, Q^_t = q_t 2^{b_t}.
-// Eight waves.  Gating: wave w owns channels 8w..8w+7 and lane l token l of the
-// chunk, so the cumsum over the chunk is one 64-lane scan (row shifts, then the
-// row broadcasts of lanes 15 and 31) and b_last is lane 63's value.  Update:
-// wave w owns the 16x16 state tiles of channels 16(w >> 1).. and value columns
-// 32(w & 1)..  The next chunk's inputs are loaded two steps ahead into
-// alternating register sets.
+// Eight waves.  Gating: lane c is channel c and wave w holds tokens 8w..8w+7 of
+// the chunk, so the cumsum is serial over the wave's eight tokens plus the
+// totals of the waves before it, exchanged through LDS; the totals of chunk
+// n+1 are made in step n, before that step's barrier, so a step has one
+// barrier.  Each lane stores its eight gated tokens as one 16-byte granule of
+// the [c][t] tiles.  Update: wave w owns the 16x16 state tiles of channels
+// 16(w >> 1).. and value columns 32(w & 1)..  The next chunk's inputs are
+// loaded two steps ahead into alternating register sets.
 constexpr int kScanThreads = 512;
 struct ScanSmem {
-  bf16 xT[2][kTile];  // gated k (or q) transposed [c][t]
-  bf16 yT[2][kTile];  // v (or dO) transposed [j][t]
-  float dec[2][kD];   // 2^{b_last} per channel
+  bf16 xT[2][kTile];    // gated k (or q) transposed [c][t]
+  bf16 yT[2][kTile];    // v (or dO) transposed [j][t]
+  float tot[2][8][kD];  // per-wave log2-gate totals of a chunk
+  float dec[2][kD];     // 2^{b_last} per channel
 };
-
-// inclusive cumsum over the 64 lanes of a wave
-__device__ __forceinline__ float wave_scan64(float x) {
-  x += dpp_shr<1>(x);
-  x += dpp_shr<2>(x);
-  x += dpp_shr<4>(x);
-  x += dpp_shr<8>(x);
-  // lane 15 of row 0 into row 1, lane 47 of row 2 into row 3; then lane 31 into rows 2, 3
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
-  return x;
-}
 
 // Chunks c0..c1-1 only: the forward scan starts from fstart (per-head stride
 // fstride floats; null = zero), the reverse scan from rstart (null = zero) and
@@ -98,16 +89,15 @@ __global__ __launch_bounds__(kScanThreads) void gla_bwd_scans(
     int L) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-  const int r16 = lane & 15, g = lane >> 4, odd = lane & 1;
+  const int r16 = lane & 15, g = lane >> 4;
   const bool rev = (int)blockIdx.x >= BH;
   const int bh = rev ? blockIdx.x - BH : blockIdx.x;
   const size_t off = (size_t)bh * T_len * kD;
   const u32 nb = (u32)((size_t)T_len * kD * sizeof(bf16));
   const Buf bx((rev ? q : k) + off, nb), by((rev ? dO : v) + off, nb),
       bla(la + off, nb / 2 * (u32)sizeof(GT));
-  const int nc = c1 - c0;                 // chunks of this block
-  const int cw = 8 * w;                   // this wave's first gating channel
-  const int cb = w >> 1, jh = 2 * (w & 1);  // its state tiles: channels 16cb.., value blocks jh, jh+1
+  const int nc = c1 - c0;                   // chunks of this block
+  const int cb = w >> 1, jh = 2 * (w & 1);  // state tiles: channels 16cb.., value blocks jh, jh+1
   const int fb0 = swz64(r16, 8 * g), fb1 = swz64(r16, 32 + 8 * g);
 
   // a1[u]: [j = 16(jh + u) + 4g + r][c = 16cb + r16] (the state, transposed)
@@ -124,59 +114,64 @@ __global__ __launch_bounds__(kScanThreads) void gla_bwd_scans(
 #pragma unroll
     for (int u = 0; u < 2; ++u) a1[u] = *reinterpret_cast<const f32x4*>(hp + 16 * (jh + u));
   }
-  // lane = token of the chunk; 8 channels from cw
+  // channel `lane` of tokens 8w..8w+7: gate (as its raw bits), x and y (bf16)
   struct In {
-    Gate8<GT> la;
-    u32x4 x, y;
+    u32 la[8], x[8], y[8];
   };
   auto load = [&](In& d, int ch) {
-    const u32 e = (u32)(ch * kC + lane) * kD + cw;
-    d.la.load(bla, e);
-    d.x = bx.ld128(e * 2);
-    d.y = by.ld128(e * 2);
-  };
-  const int te = lane & ~1;
-  // 8 channels of tokens (lane, lane ^ 1) as (even, odd) token pairs: the
-  // even lane writes channels cw..cw+3, the odd lane cw+4..cw+7
-  auto tstore = [&](bf16* dstT, const u32 (&X)[4]) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const u32 R = dpp_swap1(odd ? X[m] : X[2 + m]);
-      const u32 fst = odd ? R : X[m], snd = odd ? X[2 + m] : R;
-      const int c = cw + 4 * odd + 2 * m;
-      *reinterpret_cast<u32*>(&dstT[swz64(c, te)]) = lo2(fst, snd);
-      *reinterpret_cast<u32*>(&dstT[swz64(c + 1, te)]) = hi2(fst, snd);
+    for (int i = 0; i < 8; ++i) {
+      const u32 e = (u32)(ch * kC + 8 * w + i) * kD + lane;
+      if constexpr (sizeof(GT) == 4)
+        d.la[i] = bla.ld32(e * 4);
+      else
+        d.la[i] = __builtin_amdgcn_raw_buffer_load_b16(bla.r, e * 2, 0, 0);
+      d.x[i] = __builtin_amdgcn_raw_buffer_load_b16(bx.r, e * 2, 0, 0);
+      d.y[i] = __builtin_amdgcn_raw_buffer_load_b16(by.r, e * 2, 0, 0);
+    }
+  };
+  auto gate_of = [&](u32 bits) {
+    if constexpr (sizeof(GT) == 4)
+      return gate_log2(as_f(bits), GT());
+    else
+      return gate_log2(as_f(bits << 16), GT());
+  };
+  // in-wave inclusive cumsum of chunk ch's gates over this wave's tokens
+  auto local_cumsum = [&](const In& d, int ch, float (&bloc)[8]) {
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      run += gate_row<GT>(gate_of(d.la[i]), ch * kC + 8 * w + i < T_len);
+      bloc[i] = run;
     }
   };
   auto chunk_at = [&](int n) { return rev ? c1 - 1 - n : c0 + n; };
-  auto step = [&](In& d, int n) {
+  float bloc[8];
+  auto step = [&](In& d, In& dn, int n) {
     const int ch = chunk_at(n), buf = n & 1;
-    // gate cumsum over the chunk, per channel
-    float b[8];
+    // chunk-wide cumsum: the totals of the waves before this one, and b_last
+    float pre = 0.f, blast = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      b[c] = wave_scan64(gate_row<GT>(d.la.log2_at(c), ch * kC + lane < T_len));
-    float bl[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      bl[c] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b[c]), 63));
-    if (lane < 8) {
-      float dl = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dl = lane == c ? bl[c] : dl;
-      sm.dec[buf][cw + lane] = exp2_fast(dl);
+    for (int j = 0; j < 8; ++j) {
+      const float tj = sm.tot[buf][j][lane];
+      pre += j < w ? tj : 0.f;
+      blast += tj;
     }
+    if (w == 0) sm.dec[buf][lane] = exp2_fast(blast);
     u32 X[4], Y[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const u32 xw = d.x[m];
-      const float f0 = exp2_fast(rev ? b[2 * m] : bl[2 * m] - b[2 * m]);
-      const float f1 = exp2_fast(rev ? b[2 * m + 1] : bl[2 * m + 1] - b[2 * m + 1]);
-      X[m] = pack_bf2(bf_lo(xw) * f0, bf_hi(xw) * f1);
-      Y[m] = d.y[m];
+      const float b0 = bloc[2 * m] + pre, b1 = bloc[2 * m + 1] + pre;
+      const float f0 = exp2_fast(rev ? b0 : blast - b0);
+      const float f1 = exp2_fast(rev ? b1 : blast - b1);
+      X[m] = pack_bf2(bf_lo(d.x[2 * m]) * f0, bf_lo(d.x[2 * m + 1]) * f1);
+      Y[m] = (d.y[2 * m] & 0xffffu) | (d.y[2 * m + 1] << 16);
     }
-    tstore(sm.xT[buf], X);
-    tstore(sm.yT[buf], Y);
+    *reinterpret_cast<u32x4*>(&sm.xT[buf][swz64(lane, 8 * w)]) = u32x4{X[0], X[1], X[2], X[3]};
+    *reinterpret_cast<u32x4*>(&sm.yT[buf][swz64(lane, 8 * w)]) = u32x4{Y[0], Y[1], Y[2], Y[3]};
+    // the next chunk's in-wave cumsum and total (its inputs are already loaded)
+    local_cumsum(dn, chunk_at(min(n + 1, nc - 1)), bloc);
+    sm.tot[buf ^ 1][w][lane] = bloc[7];
     // unconditional (clamped at the last chunk) so that the wait counts stay exact
     load(d, chunk_at(min(n + 2, nc - 1)));
     // the state at the chunk boundary, before this chunk's update
@@ -212,9 +207,12 @@ __global__ __launch_bounds__(kScanThreads) void gla_bwd_scans(
   __builtin_amdgcn_sched_barrier(0);  // keep set A's loads ahead of set B's
   load(B, chunk_at(min(1, nc - 1)));
   __builtin_amdgcn_sched_barrier(0);
+  local_cumsum(A, chunk_at(0), bloc);
+  sm.tot[0][w][lane] = bloc[7];
+  lds_barrier();
   for (int n = 0; n < nc; n += 2) {
-    step(A, n);
-    if (n + 1 < nc) step(B, n + 1);
+    step(A, B, n);
+    if (n + 1 < nc) step(B, A, n + 1);
   }
   // after chunk c0 the reverse scan holds dS_{c0}, the gradient entering the block
   if (rev && rend) {
