@@ -81,13 +81,15 @@ struct OutSmem {
   alignas(16) float decay[DK];  // 2^{b_last}
 };
 
+// Double-buffered by chunk parity: the state pass gates chunk c into one set
+// while the matrix cores still read the other.
 template <typename T, int DK>
 struct StateSmem {
   static constexpr int CP = kC + 8;
-  T khT[DK][CP];
-  T vT[DK][CP];
-  float tot[8][DK];
-  float decay[DK];
+  T khT[2][DK][CP];
+  T vT[2][DK][CP];
+  float tot[2][8][DK];
+  float decay[2][DK];
 };
 
 // Per-thread gating slice: 8 rows (8*rg ..) x 2 channels (2*cp, 2*cp+1); GT is
@@ -180,51 +182,66 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_state_pass(
   for (int cb = 0; cb < NCB; ++cb) S[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x2 gsum = {0.f, 0.f};
 
-  Slice<T, DK, GT> cur;
-  cur.load(bk, bk, bv, bla, c_begin * kC, rg, cp, false);
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    f32x2 b[8];
-    const f32x2 tot = local_cumsum(cur, b, T_len - ch * kC - 8 * rg);
-    typename Pair<T>::type kk[8], vv[8];
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) { kk[rr] = cur.k[rr]; vv[rr] = cur.v[rr]; }
-    cur.load(bk, bk, bv, bla, min(ch + 1, c_end - 1) * kC, rg, cp, false);
-    sm.tot[rg][2 * cp] = tot[0];
-    sm.tot[rg][2 * cp + 1] = tot[1];
-    lds_barrier();
+  // Chunk c_begin + n is gated in step n from register set n & 1; its row-group
+  // totals were exchanged in step n-1 (or the prologue), so each step has one
+  // barrier, before the matrix-core update.  Inputs are loaded two chunks ahead.
+  Slice<T, DK, GT> A, B;
+  f32x2 b[8];  // in-thread log2 cumsum of the chunk to gate next
+  A.load(bk, bk, bv, bla, c_begin * kC, rg, cp, false);
+  B.load(bk, bk, bv, bla, min(c_begin + 1, c_end - 1) * kC, rg, cp, false);
+  {
+    const f32x2 t0 = local_cumsum(A, b, T_len - c_begin * kC - 8 * rg);
+    sm.tot[0][rg][2 * cp] = t0[0];
+    sm.tot[0][rg][2 * cp + 1] = t0[1];
+  }
+  lds_barrier();
+  auto step = [&](Slice<T, DK, GT>& d, const Slice<T, DK, GT>& dn, int n) {
+    const int ch = c_begin + n, buf = n & 1;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int c = 2 * cp + x;
       float pre = 0.f, blast = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float tr = sm.tot[r][c];
+        const float tr = sm.tot[buf][r][c];
         pre += (r < rg) ? tr : 0.f;
         blast += tr;
       }
       float kh[8], vc[8];
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
-        kh[rr] = unpack2(kk[rr], T())[x] * exp2_fast(blast - (b[rr][x] + pre));
-        vc[rr] = unpack2(vv[rr], T())[x];
+        kh[rr] = unpack2(d.k[rr], T())[x] * exp2_fast(blast - (b[rr][x] + pre));
+        vc[rr] = unpack2(d.v[rr], T())[x];
       }
-      store8<T>(&sm.khT[c][8 * rg], kh);
-      store8<T>(&sm.vT[c][8 * rg], vc);
-      if (rg == 0) sm.decay[c] = exp2_fast(blast);
+      store8<T>(&sm.khT[buf][c][8 * rg], kh);
+      store8<T>(&sm.vT[buf][c][8 * rg], vc);
+      if (rg == 0) sm.decay[buf][c] = exp2_fast(blast);
       gsum[x] += blast;
     }
+    // the next chunk's in-thread cumsum and row-group totals (past the last
+    // chunk this repeats it; those totals are never read)
+    const f32x2 tn = local_cumsum(dn, b, T_len - (ch + 1) * kC - 8 * rg);
+    sm.tot[buf ^ 1][rg][2 * cp] = tn[0];
+    sm.tot[buf ^ 1][rg][2 * cp + 1] = tn[1];
+    // unconditional (clamped at the last chunk) so that the wait counts stay exact
+    d.load(bk, bk, bv, bla, min(ch + 2, c_end - 1) * kC, rg, cp, false);
     lds_barrier();
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[cb][r] *= sm.decay[16 * cb + 4 * g + r];
+      for (int r = 0; r < 4; ++r) S[cb][r] *= sm.decay[buf][16 * cb + 4 * g + r];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        F af = ld8<T>(&sm.khT[16 * cb + r16][32 * p + 8 * g]);
-        F bf = ld8<T>(&sm.vT[16 * wave + r16][32 * p + 8 * g]);
+        F af = ld8<T>(&sm.khT[buf][16 * cb + r16][32 * p + 8 * g]);
+        F bf = ld8<T>(&sm.vT[buf][16 * wave + r16][32 * p + 8 * g]);
         mma(S[cb], af, bf);
       }
     }
+  };
+  const int nch = c_end - c_begin;
+  for (int n = 0; n < nch; n += 2) {
+    step(A, B, n);
+    if (n + 1 < nch) step(B, A, n + 1);
   }
   // stored column-major ([value column][key row]) so that the output pass reads
   // four consecutive rows of one column as one 16-byte load.  With region_rows
