@@ -309,6 +309,13 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
     for (int p = 0; p < 2; ++p) Sf[ct][p] = bS.ld128(frag_off(ct, p));
+  // the window branch's gradients, to which this branch's are added (read
+  // early so that their latency hides behind the gating)
+  const Buf bgq(dq + off, nb), bgk(dk + off, nb), bgv(dv + off, nb);
+  u32x2 dqw[4], dkw[4], dvw[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+    dqw[ct] = kAddQK ? ld64v(bgq, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
 
   // ---- 1. dO and v tiles; gate cumsum within each 16-token block
   {
@@ -430,17 +437,16 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
     for (int p = 0; p < 2; ++p) {
       dSf[ct][p] = bdS.ld128(frag_off(ct, p));
     }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    dkw[ct] = kAddQK ? ld64v(bgk, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
+    dvw[ct] = ld64v(bgv, (rowe + 16 * ct + 4 * g) * 2);
+  }
   lds_barrier();
 
   float X[4][4], Y[4][4];  // dlog_alpha items: suffix-summed X, prefix-summed Y
-  // the window branch's gradients, to which this branch's are added
-  const Buf bgq(dq + off, nb), bgk(dk + off, nb), bgv(dv + off, nb);
   // ---- 4. dq: wave w is query block w
   {
-    u32x2 dqw[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      dqw[ct] = kAddQK ? ld64v(bgq, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
     bf16x8 dof[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) dof[p] = ld8<bf16>(&sm.dor[at(t, 32 * p + 8 * g)]);
@@ -540,12 +546,6 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
   lds_barrier();
   // ---- 5. dk, dv: wave w is key block w
   {
-    u32x2 dkw[4], dvw[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      dkw[ct] = kAddQK ? ld64v(bgk, (rowe + 16 * ct + 4 * g) * 2) : u32x2{0u, 0u};
-      dvw[ct] = ld64v(bgv, (rowe + 16 * ct + 4 * g) * 2);
-    }
     bf16x8 vf[2], kf[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
