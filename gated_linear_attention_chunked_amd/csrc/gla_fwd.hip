@@ -1101,9 +1101,23 @@ hipError_t launch_gla_checkpoints(const Shape& s, const void* k, const void* v, 
   return hipGetLastError();
 }
 
+// Pieces per segment of the hybrid path's state pass: the largest divisor m of
+// the chunks per segment with (G-1) m B H <= 256 work-groups, so that a head
+// count too small to fill the chip with whole segments still does (packed
+// batches keep whole segments).
+int state_pieces(const Shape& s, const Plan& pl) {
+  if (s.cu || pl.G < 2) return 1;
+  const long long used = (long long)(pl.G - 1) * s.B * s.H;
+  int m = 1;
+  for (int c = 2; c <= pl.cps; ++c)
+    if (pl.cps % c == 0 && used * c <= 256) m = c;
+  return m;
+}
+
 size_t gla_fwd_workspace_bytes(const Shape& s) {
   const Plan pl = make_plan(s);
-  return (size_t)s.B * s.H * (pl.G - 1) * ((size_t)s.dk * s.dv + s.dk) * sizeof(float);
+  return (size_t)s.B * s.H * (pl.G - 1) * state_pieces(s, pl) * ((size_t)s.dk * s.dv + s.dk) *
+         sizeof(float);
 }
 
 hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStream_t st) {
@@ -1114,19 +1128,23 @@ hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStre
 }
 
 hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const void* la,
-                            void* ws, int* G, int* cps, hipStream_t st) {
+                            void* ws, int* G, int* cps, int* m, hipStream_t st) {
   const Plan pl = make_plan(s);
   *G = pl.G;
   *cps = pl.cps;
+  *m = state_pieces(s, pl);
   if (s.T == 0 || pl.G < 2 || s.dtype != 1 || (s.dk != 128 && s.dk != 64)) return hipSuccess;
   const int BH = s.B * s.H;
+  // (G-1) m pieces of cps / m chunks: the state pass sees them as the first
+  // segments of a plan with (G-1) m + 1 segments
+  const int P = (pl.G - 1) * *m;
   float* ws_state = (float*)ws;
-  float* ws_gamma = ws_state + (size_t)BH * (pl.G - 1) * s.dk * s.dk;
+  float* ws_gamma = ws_state + (size_t)BH * P * s.dk * s.dk;
   auto go = [&](auto kernel, auto gt) {
     typedef decltype(gt) GT;
-    hipLaunchKernelGGL(kernel, dim3(pl.G - 1, BH), dim3(4 * s.dk), 0, st, (const bf16*)k,
-                       (const bf16*)v, (const GT*)la, ws_state, ws_gamma, s.T, pl.cps, pl.G, s.cu,
-                       s.n_tokens, s.H, 0);
+    hipLaunchKernelGGL(kernel, dim3(P, BH), dim3(4 * s.dk), 0, st, (const bf16*)k,
+                       (const bf16*)v, (const GT*)la, ws_state, ws_gamma, s.T, pl.cps / *m, P + 1,
+                       s.cu, s.n_tokens, s.H, 0);
   };
   if (s.dk == 128)
     s.gate == 1 ? go(gla_state_pass<bf16, 128, bf16>, bf16()) : go(gla_state_pass<bf16, 128, float>, 0.f);

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const float* __restrict__ ws_gamma, bf16* __restrict__ o, float* __restrict__ hT,
     bf16* __restrict__ rk, bf16* __restrict__ rv, bf16* __restrict__ o_swa,
     float* __restrict__ lse, int T_arg, int H, int W, int M, float scale_log2, float mix, int cps,
-    int G, const int* __restrict__ cu, int N) {
+    int G, int m, const int* __restrict__ cu, int N) {
   constexpr int kD = D, kRing = RING;
   constexpr int NT = D / 64;    // 16-column blocks of a consumer wave's state slice
   constexpr int CW = D / 4;     // value columns per consumer wave
@@ -186,8 +186,9 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   } else if (wave < 4) {
     // ------------------------------------------------------------ consumers
     const int cw = wave;
-    // state entering the segment: h0 carried through the earlier segments'
-    // local end states (column-major) and total log2 decays
+    // state entering the segment: h0 carried through the local end states
+    // (column-major) and total log2 decays of the m pieces of each earlier
+    // segment
     f32x4 S[NT][NCB];  // S[nt][cb]: rows 16cb + 4g + r, column CW cw + 16nt + r16
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -196,9 +197,10 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           S[nt][cb][r] = h0 ? h0[s_base + (16 * cb + 4 * g + r) * kD + CW * cw + 16 * nt + r16] : 0.f;
-    for (int sg = 0; sg < seg; ++sg) {
-      const float* loc = ws_state + ((size_t)bh * (G - 1) + sg) * kD * kD;
-      const float* gm = ws_gamma + ((size_t)bh * (G - 1) + sg) * kD;
+    const int P = (G - 1) * m;
+    for (int sg = 0; sg < seg * m; ++sg) {
+      const float* loc = ws_state + ((size_t)bh * P + sg) * kD * kD;
+      const float* gm = ws_gamma + ((size_t)bh * P + sg) * kD;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gm[16 * cb + 4 * g]);
@@ -750,12 +752,12 @@ void launch_fused_kernel(const Shape& s, const void* q, const void* k, const voi
                          const void* kw, const void* v, const void* la, const void* mk,
                          const void* mv, const float* h0, const float* ws_state,
                          const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
-                         void* o_swa, float* lse, int cps, int G_, hipStream_t st) {
+                         void* o_swa, float* lse, int cps, int G_, int m, hipStream_t st) {
   hipLaunchKernelGGL((hybrid_fwd_fused<D, RING, kSep, GT>), dim3(G_, s.B * s.H), dim3(512), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)qw, (const bf16*)kw,
                      (const bf16*)v, (const GT*)la, (const bf16*)mk, (const bf16*)mv, h0, ws_state,
                      ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, (bf16*)o_swa, lse, s.T,
-                     s.H, s.window, s.n_meta, s.scale * kLog2e, s.mix, cps, G_, s.cu, s.n_tokens);
+                     s.H, s.window, s.n_meta, s.scale * kLog2e, s.mix, cps, G_, m, s.cu, s.n_tokens);
 }
 
 template <int D, int RING>
@@ -763,10 +765,10 @@ void launch_fused_ring(const Shape& s, bool sep, const void* q, const void* k, c
                        const void* kw, const void* v, const void* la, const void* mk,
                        const void* mv, const float* h0, const float* ws_state,
                        const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
-                       void* o_swa, float* lse, int cps, int G, hipStream_t st) {
+                       void* o_swa, float* lse, int cps, int G, int m, hipStream_t st) {
   auto go = [&](auto kernel_launch) {
     kernel_launch(s, q, k, qw, kw, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT, ring_k, ring_v,
-                  o_swa, lse, cps, G, st);
+                  o_swa, lse, cps, G, m, st);
   };
   if (s.gate == 1)
     sep ? go(launch_fused_kernel<D, RING, true, bf16>) : go(launch_fused_kernel<D, RING, false, bf16>);
@@ -779,24 +781,24 @@ hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, con
                                const void* mv, const float* h0, void* o, float* hT, void* ring_k,
                                void* ring_v, void* o_swa, float* lse, void* ws, hipStream_t st) {
   if (s.B * s.H == 0) return hipSuccess;
-  int G = 1, cps = 1;
-  hipError_t e = launch_gla_state(s, k, v, la, ws, &G, &cps, st);
+  int G = 1, cps = 1, m = 1;
+  hipError_t e = launch_gla_state(s, k, v, la, ws, &G, &cps, &m, st);
   if (e != hipSuccess) return e;
   const int BH = s.B * s.H;
   const float* ws_state = (const float*)ws;
-  const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * s.dk * s.dk : nullptr;
+  const float* ws_gamma = ws_state ? ws_state + (size_t)BH * (G - 1) * m * s.dk * s.dk : nullptr;
   const bool sep = qw != nullptr;
   const void* qw_ = sep ? qw : q;
   const void* kw_ = sep ? kw : k;
   if (s.dk == 128)
     launch_fused_ring<128, 5>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
-                              ring_k, ring_v, nullptr, nullptr, cps, G, st);
+                              ring_k, ring_v, nullptr, nullptr, cps, G, m, st);
   else if (s.window <= max_window(3))
     launch_fused_ring<64, 3>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
-                             ring_k, ring_v, o_swa, lse, cps, G, st);
+                             ring_k, ring_v, o_swa, lse, cps, G, m, st);
   else
     launch_fused_ring<64, 5>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
-                             ring_k, ring_v, o_swa, lse, cps, G, st);
+                             ring_k, ring_v, o_swa, lse, cps, G, m, st);
   return hipGetLastError();
 }
 

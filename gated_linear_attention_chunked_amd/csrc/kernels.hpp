@@ -40,11 +40,12 @@ hipError_t launch_gla_fwd(const Shape& s, const void* q, const void* k, const vo
                           const void* la, const float* h0, void* o, float* hT, void* ws,
                           hipStream_t st);
 
-// State pass of the GLA branch alone (bf16, dk = dv in {64, 128}): the local end states
-// and decays of segments 0..G-2 into ws (same layout as launch_gla_fwd's
-// workspace); G segments of cps 64-token chunks each.
+// State pass of the GLA branch alone (bf16, dk = dv in {64, 128}): the local end
+// states and decays of the (G-1) m pieces of segments 0..G-2 into ws (pieces of
+// cps / m 64-token chunks, in order; m = 1 gives launch_gla_fwd's layout); G
+// segments of cps 64-token chunks each.
 hipError_t launch_gla_state(const Shape& s, const void* k, const void* v, const void* la,
-                            void* ws, int* G, int* cps, hipStream_t st);
+                            void* ws, int* G, int* cps, int* m, hipStream_t st);
 
 // Both branches' outputs in one pass after launch_gla_state: o = o_gla + mix *
 // o_swa, hT (optional), the decode window cache (optional) and, with save, the
