@@ -620,10 +620,12 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           const int slo = (c - (kRing - 1) + R0 + x) * kC + 16 * kb;
           const bool full = slo >= 0 && slo + 15 <= tlo && slo > tlo + 15 - W;
           if (!full) {
+            // key s inside the window of query t: 0 <= t - s < W (one unsigned
+            // compare); keys before the sequence start only in its first chunks
+            const int dt = t - slo - 4 * g;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int sk = slo + 4 * g + i;
-              const bool ok = sk >= 0 && sk <= t && sk > t - W;
+              const bool ok = (u32)(dt - i) < (u32)W && (slo >= 0 || slo + 4 * g + i >= 0);
               L[2 * x + kb][i] = ok ? L[2 * x + kb][i] : -INFINITY;
             }
           }

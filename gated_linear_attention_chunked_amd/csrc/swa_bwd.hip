@@ -617,6 +617,16 @@ __global__ __launch_bounds__(kStreamThreads) void swa_bwd_stream(
               P[u][r] = pr;
               dS[u][r] = pr * (mix * dp[r] - d4[r]);
             }
+          } else if (t_lo + 15 < T_len && s_lo + 15 < T_len) {
+            // query t sees key s when 0 <= t - s < W (one unsigned compare)
+            const int dt = t_lo + 4 * g - sg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const bool ok = (u32)(dt + r) < (u32)W;
+              const float pr = ok ? exp2_fast(sc[r] * sl2 - l4[r]) : 0.f;
+              P[u][r] = pr;
+              dS[u][r] = pr * (mix * dp[r] - d4[r]);
+            }
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
