@@ -124,9 +124,11 @@ __device__ __forceinline__ void intra_scores(SM& sm, int i, int j, bool fast, in
 
 // kSep: the window branch reads its own queries and keys qw, kw (otherwise qw,
 // kw alias q, k and are not loaded a second time).  GT: gate input type (float
-// log alpha or bf16 logit).  o_swa and lse (D = 64 only; each nullable) receive
-// the window branch alone and its log normaliser.
-template <int D, int RING, bool kSep, typename GT>
+// log alpha or bf16 logit).  kSave: o_swa and lse (each nullable) receive the
+// window branch alone and its log normaliser (always at D = 64; at D = 128 a
+// separate instance, whose extra accumulators spill a few registers, so that
+// the inference instance keeps none).
+template <int D, int RING, bool kSep, typename GT, bool kSave = (D == 64)>
 __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ qw,
     const bf16* __restrict__ kw, const bf16* __restrict__ v,
@@ -143,7 +145,6 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   constexpr int KS = D / 32;    // contraction steps over channels
   constexpr int NPW = D / 32;   // producer waves that gate (32 channels each)
   constexpr int NR0 = (RING + 1) / 2;  // ring chunks in the first key half
-  constexpr bool kSave = D == 64;
   static_assert(D == 64 || D == 128, "head size");
   static_assert(RING == 3 || RING == 5, "ring");
   __shared__ Smem<D, RING> sm;
@@ -741,28 +742,28 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 
 }  // namespace
 
-// bf16 with d_k = d_v = 128 (inference outputs) or 64 (also o_swa and lse), a
-// window the five-chunk ring holds, at most 16 meta slots, no halo.
+// bf16 with d_k = d_v in {64, 128} (with or without the training outputs o_swa
+// and lse), a window the five-chunk ring holds, at most 16 meta slots, no halo.
 bool hybrid_fused_ok(const Shape& s, bool save) {
-  const bool shape = (s.dk == 128 && !save) || s.dk == 64;
-  return s.dtype == 1 && shape && s.dv == s.dk && s.window >= 1 && s.window <= max_window(5) &&
-         s.n_meta <= 16 && s.T > 0 && s.hlen == 0;
+  (void)save;
+  return s.dtype == 1 && (s.dk == 64 || s.dk == 128) && s.dv == s.dk && s.window >= 1 &&
+         s.window <= max_window(5) && s.n_meta <= 16 && s.T > 0 && s.hlen == 0;
 }
 
-template <int D, int RING, bool kSep, typename GT>
+template <int D, int RING, bool kSep, typename GT, bool kSave>
 void launch_fused_kernel(const Shape& s, const void* q, const void* k, const void* qw,
                          const void* kw, const void* v, const void* la, const void* mk,
                          const void* mv, const float* h0, const float* ws_state,
                          const float* ws_gamma, void* o, float* hT, void* ring_k, void* ring_v,
                          void* o_swa, float* lse, int cps, int G_, int m, hipStream_t st) {
-  hipLaunchKernelGGL((hybrid_fwd_fused<D, RING, kSep, GT>), dim3(G_, s.B * s.H), dim3(512), 0, st,
+  hipLaunchKernelGGL((hybrid_fwd_fused<D, RING, kSep, GT, kSave>), dim3(G_, s.B * s.H), dim3(512), 0, st,
                      (const bf16*)q, (const bf16*)k, (const bf16*)qw, (const bf16*)kw,
                      (const bf16*)v, (const GT*)la, (const bf16*)mk, (const bf16*)mv, h0, ws_state,
                      ws_gamma, (bf16*)o, hT, (bf16*)ring_k, (bf16*)ring_v, (bf16*)o_swa, lse, s.T,
                      s.H, s.window, s.n_meta, s.scale * kLog2e, s.mix, cps, G_, m, s.cu, s.n_tokens);
 }
 
-template <int D, int RING>
+template <int D, int RING, bool kSave = (D == 64)>
 void launch_fused_ring(const Shape& s, bool sep, const void* q, const void* k, const void* qw,
                        const void* kw, const void* v, const void* la, const void* mk,
                        const void* mv, const float* h0, const float* ws_state,
@@ -773,9 +774,9 @@ void launch_fused_ring(const Shape& s, bool sep, const void* q, const void* k, c
                   o_swa, lse, cps, G, m, st);
   };
   if (s.gate == 1)
-    sep ? go(launch_fused_kernel<D, RING, true, bf16>) : go(launch_fused_kernel<D, RING, false, bf16>);
+    sep ? go(launch_fused_kernel<D, RING, true, bf16, kSave>) : go(launch_fused_kernel<D, RING, false, bf16, kSave>);
   else
-    sep ? go(launch_fused_kernel<D, RING, true, float>) : go(launch_fused_kernel<D, RING, false, float>);
+    sep ? go(launch_fused_kernel<D, RING, true, float, kSave>) : go(launch_fused_kernel<D, RING, false, float, kSave>);
 }
 
 hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, const void* qw,
@@ -792,7 +793,10 @@ hipError_t launch_hybrid_fused(const Shape& s, const void* q, const void* k, con
   const bool sep = qw != nullptr;
   const void* qw_ = sep ? qw : q;
   const void* kw_ = sep ? kw : k;
-  if (s.dk == 128)
+  if (s.dk == 128 && (o_swa || lse))
+    launch_fused_ring<128, 5, true>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o,
+                                    hT, ring_k, ring_v, o_swa, lse, cps, G, m, st);
+  else if (s.dk == 128)
     launch_fused_ring<128, 5>(s, sep, q, k, qw_, kw_, v, la, mk, mv, h0, ws_state, ws_gamma, o, hT,
                               ring_k, ring_v, nullptr, nullptr, cps, G, m, st);
   else if (s.window <= max_window(3))
