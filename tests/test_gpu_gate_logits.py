@@ -41,7 +41,7 @@ def ref_forward(inp, w, s, mix, sep=False):
     (2, 2, 300, 128, 128, 4, 2.0, False),    # single pass
     (1, 2, 2100, 128, 64, 3, 2.0, False),    # single pass, several state segments
     (2, 2, 257, 128, 100, 2, -3.0, True),    # steep gates (sub-block form), own window q, k
-    (2, 2, 333, 64, 64, 4, 2.0, False),      # two-kernel path
+    (2, 2, 333, 64, 64, 4, 2.0, False),      # single pass at d = 64, three-chunk ring
     (1, 3, 200, 64, 40, 0, -3.0, False),
 ])
 def test_forward_gate_logits(B, H, T, d, w, M, gate_mean, sep):

@@ -33,7 +33,7 @@ def ref_forward(inp, w, s, mix):
 @pytest.mark.parametrize("B,H,T,d,w,M,dtype", [
     (2, 2, 300, 128, 128, 4, "bf16"),   # single pass, ragged tail
     (1, 2, 2100, 128, 64, 3, "bf16"),   # single pass, two state segments
-    (2, 2, 257, 64, 64, 4, "bf16"),     # two-kernel path
+    (2, 2, 257, 64, 64, 4, "bf16"),     # single pass at d = 64, three-chunk ring
     (1, 2, 130, 64, 40, 2, "f32"),
 ])
 def test_forward_separate_window_inputs(B, H, T, d, w, M, dtype):
