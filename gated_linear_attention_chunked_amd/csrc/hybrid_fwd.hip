@@ -429,6 +429,10 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     }
   } else {
     // ------------------------------------------------------------ producers
+    // At d = 64 the producers' gating and window scores are the longer path
+    // (measured: 76.4 against 79.7 us on B8 H16 T2048 with the training outputs);
+    // at d = 128 raising them was slower (0.158 against 0.154 ms on B2 H32 T4096).
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(2);
     const int pw = wave - 4;                    // gating (pw < NPW): channels 32pw .. 32pw+31
     const bool gater = pw < NPW;
     const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+7, rows 2rq, 2rq+1
