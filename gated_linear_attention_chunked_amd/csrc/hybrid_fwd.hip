@@ -429,10 +429,13 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     }
   } else {
     // ------------------------------------------------------------ producers
-    // At d = 64 the producers' gating and window scores are the longer path
-    // (measured: 76.4 against 79.7 us on B8 H16 T2048 with the training outputs);
-    // at d = 128 raising them was slower (0.158 against 0.154 ms on B2 H32 T4096).
-    if constexpr (D == 64) __builtin_amdgcn_s_setprio(2);
+    // Issue priority over the consumer wave on the same SIMD: the window
+    // scores are the longer path at either head size, and at d = 64 the gating
+    // too (measured on B8 H16 T2048 with the training outputs: 76.4 against
+    // 79.7 us); at d = 128 the gating yields to the consumers' outputs (on B2
+    // H32 T4096: 0.1505 ms, against 0.154 with no priority and 0.158 with the
+    // gating raised as well).
+    __builtin_amdgcn_s_setprio(2);
     const int pw = wave - 4;                    // gating (pw < NPW): channels 32pw .. 32pw+31
     const bool gater = pw < NPW;
     const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+7, rows 2rq, 2rq+1
@@ -704,6 +707,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       else
         window(c, pw & 1, std::integral_constant<int, 1>());
       lds_barrier();  // (A) every read of the gated tiles, raw q and K(c-RING+1) done
+      if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
       // past the segment end this gates an unused copy of the last chunk (no
       // branch around the loads, so their waits stay exact)
       if (gater) {
@@ -711,6 +715,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
         issue(min(c + 3, c_end - 1), Xn);
       }
       lds_barrier();  // (B)
+      if constexpr (D == 128) __builtin_amdgcn_s_setprio(2);
     };
     int c = c_begin;
     for (; c + 1 < c_end; c += 2) {
