@@ -432,9 +432,11 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     // Issue priority over the consumer wave on the same SIMD: the window
     // scores are the longer path at either head size, and at d = 64 the gating
     // too (measured on B8 H16 T2048 with the training outputs: 76.4 against
-    // 79.7 us); at d = 128 the gating yields to the consumers' outputs (on B2
-    // H32 T4096: 0.1505 ms, against 0.154 with no priority and 0.158 with the
-    // gating raised as well).
+    // 79.7 us); at d = 128 the gating of fp32 log alpha yields to the
+    // consumers' outputs (on B2 H32 T4096: 0.1505 ms, against 0.154 with no
+    // priority and 0.158 with the gating raised as well), while the gating of
+    // bf16 logits, which adds a log-sigmoid per element, stays raised (0.152
+    // against 0.156 ms lowered).
     __builtin_amdgcn_s_setprio(2);
     const int pw = wave - 4;                    // gating (pw < NPW): channels 32pw .. 32pw+31
     const bool gater = pw < NPW;
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       else
         window(c, pw & 1, std::integral_constant<int, 1>());
       lds_barrier();  // (A) every read of the gated tiles, raw q and K(c-RING+1) done
-      if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
+      if constexpr (D == 128 && sizeof(GT) == 4) __builtin_amdgcn_s_setprio(0);
       // past the segment end this gates an unused copy of the last chunk (no
       // branch around the loads, so their waits stay exact)
       if (gater) {
