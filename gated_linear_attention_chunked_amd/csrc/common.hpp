@@ -185,11 +185,20 @@ template <> __device__ __forceinline__ U2 ld_pair<float>(const Buf& b, u32 off) 
 // section 2(a), the learnable gate).  The kernels work with log2 alpha:
 //   log alpha:  log2 alpha = log_alpha * log2(e)
 //   logit:      log2 sigmoid(x) = min(x, 0) log2(e) - log2(1 + 2^{-|x| log2(e)})
-// (the second form never exponentiates a positive number).
-__device__ __forceinline__ float gate_log2(float la, float) { return la * kLog2e; }
+// (the second form never exponentiates a positive number).  Per token the log2
+// gate is held at or above kMinLog2Gate: the 16-token sub-block references keep
+// every gated operand within 2^{8 |log2 alpha|} of its token, which must stay
+// inside the bf16/fp32 exponent range (2^127) with room for the operand itself.
+// A gate below 2^-15 (alpha < 3.1e-5, a state all but reset at that token) is
+// taken as 2^-15: the older state then enters with a weight of at most 2^-15
+// instead of alpha, a change below the bf16 and fp32 accuracy of the outputs.
+constexpr float kMinLog2Gate = -15.f;
+__device__ __forceinline__ float gate_log2(float la, float) {
+  return fmaxf(la * kLog2e, kMinLog2Gate);
+}
 __device__ __forceinline__ float gate_log2(float x, bf16) {
   const float t = x * kLog2e;
-  return fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t)));
+  return fmaxf(fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t))), kMinLog2Gate);
 }
 // d log(alpha) / dx = sigmoid(-x) = 1 / (1 + 2^{x log2(e)}) for a logit x; 1 for
 // log alpha itself.

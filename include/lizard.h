@@ -28,7 +28,16 @@
  *                                      finite, <= 0;  LIZARD_GATE_LOGIT: bf16
  *                                      logits x, alpha = sigmoid(x) (the
  *                                      section's learnable sigmoid gate), half
- *                                      the bytes, log-sigmoid taken in-kernel
+ *                                      the bytes, log-sigmoid taken in-kernel.
+ *                                      A log alpha below -15 ln 2 (alpha <
+ *                                      2^-15, a state all but reset at that
+ *                                      token) is taken as -15 ln 2 in every
+ *                                      entry point: the gated operands stay
+ *                                      inside the fp32/bf16 exponent range, and
+ *                                      the older state then enters with a
+ *                                      weight of at most 2^-15 instead of
+ *                                      alpha; the gate gradient is that of the
+ *                                      floored gate
  *       meta_k      [H, M, dk]         dtype of desc->dtype (shared by the batch)
  *       meta_v      [H, M, dv]         dtype of desc->dtype
  *       state/h0/hT [B, H, dk, dv]     float32 (row = key channel)
