@@ -193,12 +193,18 @@ template <> __device__ __forceinline__ U2 ld_pair<float>(const Buf& b, u32 off) 
 // taken as 2^-15: the older state then enters with a weight of at most 2^-15
 // instead of alpha, a change below the bf16 and fp32 accuracy of the outputs.
 constexpr float kMinLog2Gate = -15.f;
-__device__ __forceinline__ float gate_log2(float la, float) {
-  return fmaxf(la * kLog2e, kMinLog2Gate);
-}
-__device__ __forceinline__ float gate_log2(float x, bf16) {
+// The same without the floor.  Every log2 gate is <= 0, so a run of tokens
+// whose summed log2 gate stays at or above kMinLog2Gate holds no token below
+// the floor: a kernel may sum these and take the floored form only for a run
+// whose sum falls below it.
+__device__ __forceinline__ float gate_log2_nofloor(float la, float) { return la * kLog2e; }
+__device__ __forceinline__ float gate_log2_nofloor(float x, bf16) {
   const float t = x * kLog2e;
-  return fmaxf(fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t))), kMinLog2Gate);
+  return fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t)));
+}
+template <typename GT>
+__device__ __forceinline__ float gate_log2(float v, GT) {
+  return fmaxf(gate_log2_nofloor(v, GT()), kMinLog2Gate);
 }
 // d log(alpha) / dx = sigmoid(-x) = 1 / (1 + 2^{x log2(e)}) for a logit x; 1 for
 // log alpha itself.
@@ -245,10 +251,10 @@ struct Gate8 {
     for (int i = 0; i < kWords; ++i) w[i] = b.ld128(elem * (u32)sizeof(G) + 16u * i);
   }
   __device__ __forceinline__ float log2_at(int c) const {
-    if constexpr (sizeof(G) == 4)
-      return gate_log2(f_at(w[c >> 2], c & 3), G());
-    else
-      return gate_log2(bf_at(w[0], c), G());
+    return gate_log2(raw_at(c), G());
+  }
+  __device__ __forceinline__ float log2_nofloor_at(int c) const {
+    return gate_log2_nofloor(raw_at(c), G());
   }
   __device__ __forceinline__ float raw_at(int c) const {
     if constexpr (sizeof(G) == 4)

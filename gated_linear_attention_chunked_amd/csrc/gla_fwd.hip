@@ -28,6 +28,8 @@
 // (j < i) take the extra per-channel factor 2^{R_i - R_j} <= 1 on the q operand.
 // Every factor stays within 2^{8 max|log2 alpha|}, so extreme gates neither
 // overflow nor lose the diagonal terms.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -114,17 +116,27 @@ struct Slice {
 };
 
 // Local (row-group) log2 cumsum of the slice's gates; returns the group total.
+// Summed first without the gate floor, and again with it only in a thread
+// whose 8-row total falls below the floor (no row can lie below it otherwise).
 template <typename T, int DK, typename GT>
 // vrows: rows of the slice before the sequence end
 __device__ __forceinline__ f32x2 local_cumsum(const Slice<T, DK, GT>& sl, f32x2* b, int vrows) {
-  f32x2 run = {0.f, 0.f};
+  f32x2 run;
+  auto sum = [&](auto floor) {
+    run = f32x2{0.f, 0.f};
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr) {
-    const f32x2 la = unpack2(sl.la[rr], GT());
-    run[0] += gate_row<GT>(gate_log2(la[0], GT()), rr < vrows);
-    run[1] += gate_row<GT>(gate_log2(la[1], GT()), rr < vrows);
-    b[rr] = run;
-  }
+    for (int rr = 0; rr < 8; ++rr) {
+      const f32x2 la = unpack2(sl.la[rr], GT());
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const float g = decltype(floor)::value ? gate_log2(la[x], GT()) : gate_log2_nofloor(la[x], GT());
+        run[x] += gate_row<GT>(g, rr < vrows);
+      }
+      b[rr] = run;
+    }
+  };
+  sum(std::false_type());
+  if (fminf(run[0], run[1]) < kMinLog2Gate) sum(std::true_type());
   return run;
 }
 

@@ -471,34 +471,41 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     auto gate = [&](int ch, const In& x) {
       // b: inclusive log2 cumsum from the chunk start (in-thread over 2 rows,
       // then a scan over the 16 row pairs inside the 16-lane row)
-      float b[2][8], inc[8];
+      // The sums are first taken without the gate floor; only when some
+      // channel's chunk total falls below the floor (then a token may lie
+      // below it) are they taken again with it.
+      float b[2][8], inc[8], blast[8], bmin = 0.f;
+      auto scan = [&](auto floor) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float run = 0.f;
+        for (int c = 0; c < 8; ++c) {
+          float run = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          run += gate_row<GT>(x.la[rr].log2_at(c), 2 * rq + rr < T_len - ch * kC);
-          b[rr][c] = run;
+          for (int rr = 0; rr < 2; ++rr) {
+            const float g = decltype(floor)::value ? x.la[rr].log2_at(c) : x.la[rr].log2_nofloor_at(c);
+            run += gate_row<GT>(g, 2 * rq + rr < T_len - ch * kC);
+            b[rr][c] = run;
+          }
+          inc[c] = run;
         }
-        inc[c] = run;
-      }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<1>(inc[c]);
+        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<1>(inc[c]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<2>(inc[c]);
+        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<2>(inc[c]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<4>(inc[c]);
+        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<4>(inc[c]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<8>(inc[c]);
-      float blast[8], bmin = 0.f;
+        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<8>(inc[c]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float ex = inc[c] - b[1][c];
-        b[0][c] += ex;
-        b[1][c] += ex;
-        blast[c] = dpp_bcast<15>(inc[c]);  // the last row pair holds the chunk total
-        bmin = c ? fminf(bmin, blast[c]) : blast[c];
-      }
+        for (int c = 0; c < 8; ++c) {
+          const float ex = inc[c] - b[1][c];
+          b[0][c] += ex;
+          b[1][c] += ex;
+          blast[c] = dpp_bcast<15>(inc[c]);  // the last row pair holds the chunk total
+          bmin = c ? fminf(bmin, blast[c]) : blast[c];
+        }
+      };
+      scan(std::false_type());
+      if (__any(bmin < kMinLog2Gate)) scan(std::true_type());  // uniform over the wave
       const bool fast = !__any(bmin < -kFast);  // uniform over the wave
       if (lane == 0) sm.fastw[pw] = fast ? 1 : 0;
       float dl[8];  // 2^{b_last}
