@@ -876,16 +876,28 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
       issue_row(sr, 0);
       // b: inclusive log2 cumsum from the chunk start (in-thread over 4 rows,
       // then a scan over the 16 row quads inside the 16-lane row)
+      // (summed without the gate floor, and again with it only in a thread
+      // where some channel's 4-row total falls below the floor)
       float b[4][8], inc[8], blast[8];
+      auto sum = [&](auto floor) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float run = 0.f;
+        for (int c = 0; c < 8; ++c) {
+          float run = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          run += gate_row<GT>(hla[rr].log2_at(c), 4 * rq + rr < T_len - gch * kC);
-          b[rr][c] = run;
+          for (int rr = 0; rr < 4; ++rr) {
+            const float g = decltype(floor)::value ? hla[rr].log2_at(c) : hla[rr].log2_nofloor_at(c);
+            run += gate_row<GT>(g, 4 * rq + rr < T_len - gch * kC);
+            b[rr][c] = run;
+          }
+          inc[c] = run;
         }
-        inc[c] = run;
+      };
+      sum(std::false_type());
+      {
+        float m = inc[0];
+#pragma unroll
+        for (int c = 1; c < 8; ++c) m = fminf(m, inc[c]);
+        if (m < kMinLog2Gate) sum(std::true_type());
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) inc[c] += row_shr<1>(inc[c]);
