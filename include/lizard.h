@@ -36,8 +36,10 @@
  *                                      inside the fp32/bf16 exponent range, and
  *                                      the older state then enters with a
  *                                      weight of at most 2^-15 instead of
- *                                      alpha; the gate gradient is that of the
- *                                      floored gate
+ *                                      alpha; for such a token the gate
+ *                                      gradient is taken at the floored value
+ *                                      and passed through the floor unchanged
+ *                                      (not zeroed)
  *       meta_k      [H, M, dk]         dtype of desc->dtype (shared by the batch)
  *       meta_v      [H, M, dv]         dtype of desc->dtype
  *       state/h0/hT [B, H, dk, dv]     float32 (row = key channel)
