@@ -122,14 +122,14 @@ template <typename T, int DK, typename GT>
 // vrows: rows of the slice before the sequence end
 __device__ __forceinline__ f32x2 local_cumsum(const Slice<T, DK, GT>& sl, f32x2* b, int vrows) {
   f32x2 run;
-  auto sum = [&](auto floor) {
+  auto sum = [&](auto floored) {
     run = f32x2{0.f, 0.f};
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const f32x2 la = unpack2(sl.la[rr], GT());
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const float g = decltype(floor)::value ? gate_log2(la[x], GT()) : gate_log2_nofloor(la[x], GT());
+        const float g = decltype(floored)::value ? gate_log2(la[x], GT()) : gate_log2_nofloor(la[x], GT());
         run[x] += gate_row<GT>(g, rr < vrows);
       }
       b[rr] = run;
@@ -879,13 +879,13 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_ws(
       // (summed without the gate floor, and again with it only in a thread
       // where some channel's 4-row total falls below the floor)
       float b[4][8], inc[8], blast[8];
-      auto sum = [&](auto floor) {
+      auto sum = [&](auto floored) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float run = 0.f;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const float g = decltype(floor)::value ? hla[rr].log2_at(c) : hla[rr].log2_nofloor_at(c);
+            const float g = decltype(floored)::value ? hla[rr].log2_at(c) : hla[rr].log2_nofloor_at(c);
             run += gate_row<GT>(g, 4 * rq + rr < T_len - gch * kC);
             b[rr][c] = run;
           }

@@ -475,13 +475,13 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       // channel's chunk total falls below the floor (then a token may lie
       // below it) are they taken again with it.
       float b[2][8], inc[8], blast[8], bmin = 0.f;
-      auto scan = [&](auto floor) {
+      auto scan = [&](auto floored) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float run = 0.f;
 #pragma unroll
           for (int rr = 0; rr < 2; ++rr) {
-            const float g = decltype(floor)::value ? x.la[rr].log2_at(c) : x.la[rr].log2_nofloor_at(c);
+            const float g = decltype(floored)::value ? x.la[rr].log2_at(c) : x.la[rr].log2_nofloor_at(c);
             run += gate_row<GT>(g, 2 * rq + rr < T_len - ch * kC);
             b[rr][c] = run;
           }
