@@ -191,7 +191,7 @@ template <> __device__ __forceinline__ U2 ld_pair<float>(const Buf& b, u32 off) 
 // inside the bf16/fp32 exponent range (2^127) with room for the operand itself.
 // A gate below 2^-15 (alpha < 3.1e-5, a state all but reset at that token) is
 // taken as 2^-15: the older state then enters with a weight of at most 2^-15
-// instead of alpha, a change below the bf16 and fp32 accuracy of the outputs.
+// instead of alpha, which moves an output by at most 2^-15 |q|_1 max|S|.
 constexpr float kMinLog2Gate = -15.f;
 // The same without the floor.  Every log2 gate is <= 0, so a run of tokens
 // whose summed log2 gate stays at or above kMinLog2Gate holds no token below
