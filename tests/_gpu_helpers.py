@@ -21,7 +21,8 @@ TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 # absolute error of the large terms they were summed from).  The gate
 # gradient (d log alpha or d logit) is in bf16 problems a chunk sum of products
 # that cancel (q dq - k dk form), so its bar is 5.0.  Largest values seen over
-# the GPU suite: fp32 1.3e-4, bf16 0.50, bf16 gate gradient 2.8.
+# the GPU suite: fp32 1.7e-4, bf16 0.50, bf16 gate gradient 2.8 (a test may pass
+# its own elementwise bar: the fp32 extreme-gate case, 1e-2, measured 1.4e-3).
 P999_LOG = os.environ.get("P999_LOG")
 P999_BAR = {torch.float32: 1e-3, torch.bfloat16: 1.0}
 P999_GATE_GRAD_BAR = 5.0
