@@ -11,7 +11,8 @@ so it is held to an absolute bound on the scale of those products (|q| |dq|);
 the initial-state gradient, which every token's floored gate scales down,
 to one on |dh0| itself.  Cases: uniformly extreme gates (log alpha about -14,
 -30, -90), half the channels extreme and half moderate, bf16 logits of -40,
-at d = 64 and 128, bf16 and fp32.
+at d = 64 and 128, bf16 and fp32; and packed (variable-length) batches with
+gates far below the floor, each sequence against the oracle run on it alone.
 """
 import math
 
@@ -22,7 +23,7 @@ import torch
 import gated_linear_attention_chunked_amd as lz
 import oracle
 from tests._gpu_helpers import assert_close, f64, rel_err, to_dev
-from workloads import make_decode_inputs, make_inputs
+from workloads import make_decode_inputs, make_inputs, make_packed_inputs
 
 pytestmark = pytest.mark.gpu
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -132,3 +133,34 @@ def test_extreme_gates(d, dtype, gate_mean, mixed, logits):
         assert torch.isfinite(o).all()
         assert_close(f"decode[{i}].o", o, o_ref, dt)
     assert_close("decode.state", state, st_ref, dt)
+
+
+@pytest.mark.parametrize("d,w,logits", [
+    (128, 128, False),   # single-pass kernel
+    (64, 64, True),      # d = 64 packed batches: GLA output pass + window kernel
+])
+def test_extreme_gates_packed(d, w, logits):
+    """Packed (variable-length) prefill with gates far below the floor: every
+    sequence against the oracle run on it alone with the same floor."""
+    lengths = [0, 1, 33, 300, 1100, 70]
+    print(f"[case] extreme gates packed d{d} w{w} logits{logits}", flush=True)
+    s, mix = 1.0 / math.sqrt(d), 0.8
+    inp = make_packed_inputs(lengths, 2, d, d, 4, seed=d + 17, gate_mean=-30.0, with_h0=True,
+                             with_gate_logits=logits)
+    x = to_dev(inp)
+    out = lz.hybrid_fwd_varlen(x["q"], x["k"], x["v"], x["gate_x"] if logits else x["log_alpha"],
+                               x["meta_k"], x["meta_v"], w, x["cu_seqlens"], max(lengths), scale=s,
+                               mix=mix, h0=x["h0"], return_state=True, return_ring=True)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].tolist()
+    for b in range(len(lengths)):
+        sl = lambda t: f64({"t": t[:, cu[b]:cu[b + 1]]})["t"][None]
+        la = oracle.log_sigmoid(sl(inp["gate_x"])) if logits else sl(inp["log_alpha"])
+        ref = oracle.hybrid_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), np.maximum(la, FLOOR),
+                                    f64(inp)["meta_k"], f64(inp)["meta_v"], w, s, mix=mix,
+                                    h0=f64(inp)["h0"][b:b + 1])
+        if lengths[b]:
+            assert torch.isfinite(out["o"][:, cu[b]:cu[b + 1]]).all()
+            assert_close(f"o[seq {b}]", out["o"][:, cu[b]:cu[b + 1]][None], ref["o"], torch.bfloat16)
+        assert torch.isfinite(out["hT"][b]).all()
+        assert_close(f"hT[seq {b}]", out["hT"][b:b + 1], ref["hT"], torch.bfloat16)
