@@ -448,4 +448,54 @@ __device__ __forceinline__ float swap_sum16(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// Meta-memory gradients of the window branch: fixed-order sum (deterministic)
+// of per-(sequence, query tile) partials.  metap holds, for partial p = b
+// ntiles + tile of head h, 2 n floats at ((b H + h) ntiles + tile) 2 n:
+// entries e < n belong to dmeta_k [H, n], the rest to dmeta_v (n = M d).
+struct MetaReduceArgs {
+  const float* metap = nullptr;
+  float* dmk = nullptr;
+  float* dmv = nullptr;
+  int B = 0, H = 0, ntiles = 0, n = 0;  // n = 0: nothing to reduce
+};
+
+// One block sums the 64 entries of strip `strip` of head h: its NG groups of
+// 64 threads sum interleaved NG-ths of the B ntiles partials (coalesced, up to
+// 16 loads in flight per thread), then a fixed tree through `part` (NG x 64
+// floats of LDS) adds the NG sums.  Every thread of the block calls it.
+template <int NG>
+__device__ __forceinline__ void meta_reduce_strip(const MetaReduceArgs& a, int h, int strip,
+                                                  float (*part)[64]) {
+  const int i = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int e = strip * 64 + i, n = a.n;
+  const int np = a.B * a.ntiles;
+  float s = 0.f;
+  if (e < 2 * n) {
+    auto at = [&](int p) {
+      const int b = p / a.ntiles, tl = p - b * a.ntiles;
+      return a.metap[(((size_t)(b * a.H + h)) * a.ntiles + tl) * 2 * n + e];
+    };
+    int p = grp;
+    for (; p + 15 * NG < np; p += 16 * NG) {
+      float x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = at(p + NG * u);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += x[u];
+    }
+    for (; p < np; p += NG) s += at(p);
+  }
+  part[grp][i] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = NG / 2; w >= 1; w >>= 1) {
+    if (grp < w) part[grp][i] += part[grp + w][i];
+    __syncthreads();
+  }
+  if (grp == 0 && e < 2 * n) {
+    if (e < n) a.dmk[(size_t)h * n + e] = part[0][i];
+    else a.dmv[(size_t)h * n + e - n] = part[0][i];
+  }
+}
+
 }  // namespace lz

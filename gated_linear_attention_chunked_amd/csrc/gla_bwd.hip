@@ -79,15 +79,25 @@ struct ScanSmem {
 // Chunks c0..c1-1 only: the forward scan starts from fstart (per-head stride
 // fstride floats; null = zero), the reverse scan from rstart (null = zero) and
 // leaves the gradient entering chunk c0 in rend (null = not stored); chunk c's
-// states go to slot c - c0 of the L per head.
+// states go to slot c - c0 of the L per head.  Blocks past the 2 BH of the
+// scans, when the launch has them, sum the window branch's meta-gradient
+// partials (meta): a latency-bound step that runs here beside the scans
+// instead of as a launch of its own.
 template <typename GT>
 __global__ __launch_bounds__(kScanThreads) void gla_bwd_scans(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const GT* __restrict__ la, const bf16* __restrict__ dO, const float* __restrict__ fstart,
     size_t fstride, const float* __restrict__ rstart, float* __restrict__ rend,
     bf16* __restrict__ S_all, bf16* __restrict__ dS_all, int BH, int T_len, int c0, int c1,
-    int L) {
+    int L, MetaReduceArgs meta) {
   __shared__ __attribute__((aligned(16))) ScanSmem sm;
+  static_assert(sizeof(ScanSmem) >= sizeof(float) * (kScanThreads / 64) * 64, "meta strip LDS");
+  if ((int)blockIdx.x >= 2 * BH) {  // uniform over the block
+    const int r = blockIdx.x - 2 * BH;
+    meta_reduce_strip<kScanThreads / 64>(meta, r % meta.H, r / meta.H,
+                                         reinterpret_cast<float(*)[64]>(&sm));
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int r16 = lane & 15, g = lane >> 4;
   const bool rev = (int)blockIdx.x >= BH;
@@ -689,19 +699,23 @@ __global__ __launch_bounds__(kThreads, 2) void gla_bwd_chunk(
 }  // namespace
 
 // Chunks c0..c1-1 of every head (bf16, d = 64): both scans, then the
-// per-chunk gradients (see launch_gla_bwd_block_gen for the arguments).
+// per-chunk gradients (see launch_gla_bwd_block_gen for the arguments); with
+// meta.n > 0 the scans launch also sums the window branch's meta gradients.
 hipError_t launch_gla_bwd_block(const Shape& s, const void* q, const void* k, const void* v,
                                 const void* la, const void* dO, const float* fstart,
                                 size_t fstride, const float* rstart, float* rend, void* dq,
                                 void* dk, void* dv, float* dla, void* S_ws, void* dS_ws,
-                                bool add_qk, int c0, int c1, int L, hipStream_t st) {
+                                bool add_qk, int c0, int c1, int L, const MetaReduceArgs& meta,
+                                hipStream_t st) {
   typedef bf16 T;
   const int BH = s.B * s.H;
+  // meta.n > 0: H strips of 64 entries per 2 n more blocks for the meta reduction
+  const int nmeta = meta.n > 0 ? meta.H * ((2 * meta.n + 63) / 64) : 0;
   auto go = [&](auto gate_type) {
     typedef decltype(gate_type) GT;
-    hipLaunchKernelGGL(gla_bwd_scans<GT>, dim3(2 * BH), dim3(kScanThreads), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, (const GT*)la, (const T*)dO, fstart, fstride,
-                       rstart, rend, (T*)S_ws, (T*)dS_ws, BH, s.T, c0, c1, L);
+    hipLaunchKernelGGL(gla_bwd_scans<GT>, dim3(2 * BH + nmeta), dim3(kScanThreads), 0, st,
+                       (const T*)q, (const T*)k, (const T*)v, (const GT*)la, (const T*)dO, fstart,
+                       fstride, rstart, rend, (T*)S_ws, (T*)dS_ws, BH, s.T, c0, c1, L, meta);
     auto kern = add_qk ? gla_bwd_chunk<true, GT> : gla_bwd_chunk<false, GT>;
     hipLaunchKernelGGL(kern, dim3(c1 - c0, BH), dim3(kThreads), 0, st, (const T*)q, (const T*)k,
                        (const T*)v, (const GT*)la, (const T*)dO, (const T*)S_ws,

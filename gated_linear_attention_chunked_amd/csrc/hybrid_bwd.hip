@@ -16,7 +16,7 @@ size_t swa_bwd_workspace_bytes(const Shape& s);
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv, float* dmk, float* dmv,
-                          float* Dws, void* ws, hipStream_t st);
+                          float* Dws, void* ws, MetaReduceArgs* defer, hipStream_t st);
 hipError_t launch_gla_checkpoints(const Shape& s, const void* k, const void* v, const void* la,
                                   const float* h0, float* region, int cps, int nb,
                                   hipStream_t st);
@@ -24,7 +24,8 @@ hipError_t launch_gla_bwd_block(const Shape& s, const void* q, const void* k, co
                                 const void* la, const void* dO, const float* fstart,
                                 size_t fstride, const float* rstart, float* rend, void* dq,
                                 void* dk, void* dv, float* dla, void* S_ws, void* dS_ws,
-                                bool add_qk, int c0, int c1, int L, hipStream_t st);
+                                bool add_qk, int c0, int c1, int L, const MetaReduceArgs& meta,
+                                hipStream_t st);
 hipError_t launch_gla_bwd_block_gen(const Shape& s, const void* q, const void* k, const void* v,
                                     const void* la, const void* dO, const float* fstart,
                                     size_t fstride, const float* rstart, float* rend, void* dq,
@@ -139,9 +140,15 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
   float* part = (float*)(wswa + align256(swa_bwd_workspace_bytes(s)));
   // 1. the window branch writes dq, dk, dv (its per-token D_t scratch is the
   //    first B*H*T floats of dla, which the GLA branch overwrites below)
+  //    With the tuned GLA kernels (bf16, d = 64) the window branch's
+  //    meta-gradient reduction, if it leaves it, runs inside the first scans
+  //    launch.
   const bool sep = qw != nullptr;
+  const bool tuned = s.dtype == 1 && s.dk == 64;
+  MetaReduceArgs meta;
   hipError_t e = launch_swa_bwd(s, sep ? qw : q, sep ? kw : k, v, mk, mv, o_swa, lse, dO,
-                                sep ? dqw : dq, sep ? dkw : dk, dv, dmk, dmv, dla, wswa, st);
+                                sep ? dqw : dq, sep ? dkw : dk, dv, dmk, dmv, dla, wswa,
+                                tuned ? &meta : nullptr, st);
   if (e != hipSuccess) return e;
   if (dmix) {
     const size_t n8 = (size_t)s.B * s.H * s.T * s.dv / 8;  // dv is a multiple of 8
@@ -164,16 +171,19 @@ hipError_t launch_hybrid_bwd(const Shape& s, const void* q, const void* k, const
   const int nb = (nc + kBlk - 1) / kBlk;
   e = launch_gla_checkpoints(s, k, v, la, h0, dla, kBlk, nb, st);
   if (e != hipSuccess) return e;
-  const bool tuned = s.dtype == 1 && s.dk == 64;
   for (int b = nb - 1; b >= 0; --b) {
     const int c0 = b * kBlk, c1 = std::min(nc, c0 + kBlk);
     const float* fstart = b == 0 ? h0 : dla + (size_t)(b - 1) * kBlk * kC * s.dk + dd + s.dk;
     const size_t fstride = b == 0 ? dd : (size_t)s.T * s.dk;
     const float* rstart = b == nb - 1 ? dhT : carry;
     float* rend = b == 0 ? dh0 : carry;
-    e = (tuned ? launch_gla_bwd_block : launch_gla_bwd_block_gen)(
-        s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv, dla, S_ws, dS_ws, !sep,
-        c0, c1, kBlk, st);
+    if (tuned)
+      e = launch_gla_bwd_block(s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv, dla,
+                               S_ws, dS_ws, !sep, c0, c1, kBlk,
+                               b == nb - 1 ? meta : MetaReduceArgs(), st);
+    else
+      e = launch_gla_bwd_block_gen(s, q, k, v, la, dO, fstart, fstride, rstart, rend, dq, dk, dv,
+                                   dla, S_ws, dS_ws, !sep, c0, c1, kBlk, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -787,50 +787,12 @@ __global__ __launch_bounds__(kStreamThreads) void swa_bwd_stream(
 }
 
 // ----------------------------------------------------------- 3. meta reduce
-// Meta gradients: sum of the per-(sequence, query tile) partials, in a fixed
-// order (deterministic).  A block takes 64 consecutive entries of one head;
-// its 16 thread groups sum interleaved sixteenths of the partials (coalesced,
-// up to 16 loads in flight per thread), then a fixed tree adds the 16 sums.
+// Meta gradients: one block per (head, 64-entry strip), 16 thread groups
+// (meta_reduce_strip).
 constexpr int kMetaGroups = 16;
-template <int D>
-__global__ __launch_bounds__(64 * kMetaGroups) void swa_meta_reduce(
-    const float* __restrict__ metap, float* __restrict__ dmk, float* __restrict__ dmv, int B,
-    int H, int ntiles, int M) {
-  const int h = blockIdx.x;
-  const int n = M * D;
-  const int i = threadIdx.x & 63;
-  const int e = blockIdx.y * 64 + i;
-  const int grp = threadIdx.x >> 6;
-  const int np = B * ntiles;  // partials of this head: p = b * ntiles + tile
-  float s = 0.f;
-  if (e < 2 * n) {
-    auto at = [&](int p) {
-      const int b = p / ntiles, tl = p - b * ntiles;
-      return metap[(((size_t)(b * H + h)) * ntiles + tl) * 2 * n + e];
-    };
-    constexpr int G = kMetaGroups;
-    int p = grp;
-    for (; p + 15 * G < np; p += 16 * G) {
-      float x[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = at(p + G * u);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) s += x[u];
-    }
-    for (; p < np; p += G) s += at(p);
-  }
+__global__ __launch_bounds__(64 * kMetaGroups) void swa_meta_reduce(MetaReduceArgs a) {
   __shared__ float part[kMetaGroups][64];
-  part[grp][i] = s;
-  __syncthreads();
-#pragma unroll
-  for (int w = kMetaGroups / 2; w >= 1; w >>= 1) {
-    if (grp < w) part[grp][i] += part[grp + w][i];
-    __syncthreads();
-  }
-  if (grp == 0 && e < 2 * n) {
-    if (e < n) dmk[(size_t)h * n + e] = part[0][i];
-    else dmv[(size_t)h * n + e - n] = part[0][i];
-  }
+  meta_reduce_strip<kMetaGroups>(a, blockIdx.x, blockIdx.y, part);
 }
 
 // Segments per head of the window backward's work-groups (whole 64-query
@@ -842,12 +804,15 @@ template <typename T, int D>
 hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, const void* v,
                                 const void* mk, const void* mv, const void* o_swa,
                                 const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                                float* dmk, float* dmv, float* Dws, float* metap, hipStream_t st) {
+                                float* dmk, float* dmv, float* Dws, float* metap,
+                                MetaReduceArgs* defer, hipStream_t st) {
   const int BH = s.B * s.H;
   const int nqt = (s.T + kT - 1) / kT;
   int G = swa_bwd_segments(BH, nqt);
   const int per = (nqt + G - 1) / G;
   G = (nqt + per - 1) / per;
+  const MetaReduceArgs meta{metap, dmk, dmv, s.B, s.H, G, s.n_meta * D};
+  const dim3 mgrid(s.H, (2 * s.n_meta * D + 63) / 64);
   if constexpr (sizeof(T) == 2 && D == 64) {
     if (s.window <= 65 && s.hlen == 0 && s.tlen == 0) {
       // streaming form: B*H*G work-groups, G segments of whole tiles per sequence
@@ -855,9 +820,14 @@ hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, co
                          (const T*)k, (const T*)v, (const T*)mk, (const T*)mv, (const T*)o_swa,
                          lse, (const T*)dO, (T*)dq, (T*)dk, (T*)dv, metap, s.T, s.H, s.window,
                          s.n_meta, s.scale, s.mix, per);
-      if (s.n_meta > 0)
-        hipLaunchKernelGGL(swa_meta_reduce<D>, dim3(s.H, (2 * s.n_meta * D + 63) / 64),
-                           dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);
+      // the reduction is left to the caller when it asks (it then runs inside
+      // a later launch, beside that launch's own work)
+      if (s.n_meta > 0) {
+        if (defer)
+          *defer = meta;
+        else
+          hipLaunchKernelGGL(swa_meta_reduce, mgrid, dim3(64 * kMetaGroups), 0, st, meta);
+      }
       return hipGetLastError();
     }
   }
@@ -874,8 +844,7 @@ hipError_t launch_swa_bwd_typed(const Shape& s, const void* q, const void* k, co
                        (const T*)dO, Dws, s.dhk, s.dhv, s.T, s.window, s.scale, s.mix, s.hlen,
                        -s.hlen, (const float*)nullptr, (const float*)nullptr, 0);
   if (s.n_meta > 0)
-    hipLaunchKernelGGL(swa_meta_reduce<D>, dim3(s.H, (2 * s.n_meta * D + 63) / 64),
-                       dim3(64 * kMetaGroups), 0, st, metap, dmk, dmv, s.B, s.H, G, s.n_meta);
+    hipLaunchKernelGGL(swa_meta_reduce, mgrid, dim3(64 * kMetaGroups), 0, st, meta);
   return hipGetLastError();
 }
 
@@ -895,7 +864,7 @@ size_t swa_bwd_workspace_bytes(const Shape& s) {
 hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const void* v,
                           const void* mk, const void* mv, const void* o_swa, const float* lse,
                           const void* dO, void* dq, void* dk, void* dv, float* dmk, float* dmv,
-                          float* Dws, void* ws, hipStream_t st) {
+                          float* Dws, void* ws, MetaReduceArgs* defer, hipStream_t st) {
   const int BH = s.B * s.H;
   const int nqt = (s.T + kT - 1) / kT;
   if (nqt == 0 || BH == 0) return hipSuccess;
@@ -903,15 +872,15 @@ hipError_t launch_swa_bwd(const Shape& s, const void* q, const void* k, const vo
   if (s.dtype == 1) {
     if (s.dk == 128)
       return launch_swa_bwd_typed<bf16, 128>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
-                                             dmv, Dws, metap, st);
+                                             dmv, Dws, metap, defer, st);
     return launch_swa_bwd_typed<bf16, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
-                                          dmv, Dws, metap, st);
+                                          dmv, Dws, metap, defer, st);
   }
   if (s.dk == 128)
     return launch_swa_bwd_typed<float, 128>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk,
-                                            dmv, Dws, metap, st);
+                                            dmv, Dws, metap, defer, st);
   return launch_swa_bwd_typed<float, 64>(s, q, k, v, mk, mv, o_swa, lse, dO, dq, dk, dv, dmk, dmv,
-                                         Dws, metap, st);
+                                         Dws, metap, defer, st);
 }
 
 }  // namespace lz
