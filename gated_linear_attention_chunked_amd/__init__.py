@@ -20,7 +20,7 @@ from . import _abi
 from ._abi import LizardError, lib  # noqa: F401
 
 __all__ = ["gla_fwd", "swa_fwd", "hybrid_fwd", "hybrid_fwd_varlen", "hybrid_bwd", "decode_step",
-           "workspace_bytes", "make_desc", "LizardError", "lib"]
+           "window_cache_fill", "workspace_bytes", "make_desc", "LizardError", "lib"]
 
 _DTYPES = {torch.float32: _abi.LIZARD_F32, torch.bfloat16: _abi.LIZARD_BF16}
 
@@ -338,6 +338,38 @@ def decode_step(q, k, v, log_alpha, state, ring_k, ring_v, pos, meta_k, meta_v, 
         ctypes.byref(d), _p(q), _p(k), _p(v), _p(log_alpha), _p(state), _p(ring_k), _p(ring_v),
         _p(pos), _p(meta_k), _p(meta_v), _p(q_w), _p(k_w), _p(o), _stream()))
     return o
+
+
+def window_cache_fill(k, v, window, pos0, halo_k=None, halo_v=None, ring_k=None,
+                      ring_v=None):
+    """Decode window cache after a prefill run in segments.  k, v [B, H, T, d]:
+    the last segment's window keys (k_w when the window branch has its own) and
+    values, at positions pos0 .. pos0+T-1; halo_k, halo_v [B, H, L, d]: the L
+    tokens before it (L <= window; when T < window at least min(pos0, window - T)
+    of them).  Returns (ring_k, ring_v) [B, H, window, d]: slot p mod window holds
+    token p for the last min(window, pos0 + T) positions, zeros elsewhere."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    _need(k, "k", (B, H, T, dk), dt)
+    _need(v, "v", (B, H, T, dv), dt)
+    if (halo_k is None) != (halo_v is None):
+        raise ValueError("halo_k and halo_v: give both or neither")
+    L = 0
+    if halo_k is not None:
+        L = halo_k.shape[2]
+        _need(halo_k, "halo_k", (B, H, L, dk), dt)
+        _need(halo_v, "halo_v", (B, H, L, dv), dt)
+    dev = k.device
+    rk = torch.empty(B, H, window, dk, device=dev, dtype=dt) if ring_k is None else _need(
+        ring_k, "ring_k", (B, H, window, dk), dt)
+    rv = torch.empty(B, H, window, dv, device=dev, dtype=dt) if ring_v is None else _need(
+        ring_v, "ring_v", (B, H, window, dv), dt)
+    d = make_desc(B, H, T, dk, dv, window, 0, None, 1.0, dt)
+    _abi.check("lizard_window_cache_fill", lib().lizard_window_cache_fill(
+        ctypes.byref(d), _p(k), _p(v), _p(halo_k), _p(halo_v), L, int(pos0), _p(rk), _p(rv),
+        _stream()))
+    return rk, rv
 
 
 def default_scale(dk):

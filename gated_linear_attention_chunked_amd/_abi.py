@@ -53,6 +53,8 @@ _SIGS = {
                                   + [ctypes.c_int32] + [P] * 4 + [ctypes.c_int32]
                                   + [P, ctypes.c_size_t, P]),
     "lizard_decode_step": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 13 + [P]),
+    "lizard_window_cache_fill": (ctypes.c_int, [ctypes.POINTER(Desc)] + [P] * 4
+                                 + [ctypes.c_int32, ctypes.c_int64, P, P, P]),
     "lizard_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "lizard_version": (ctypes.c_int32, []),
 }

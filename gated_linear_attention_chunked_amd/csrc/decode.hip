@@ -185,6 +185,30 @@ __global__ void ring_fill_kernel(const T* __restrict__ k, const T* __restrict__ 
     dst[d] = (p >= 0) ? x[(sr.row0 + p) * D + d] : to_t<T>(0.f);
 }
 
+// Window cache of a sequence prefilled in segments, from its last segment: the
+// segment's T_arg tokens are positions pos0 .. pos0+T_arg-1 and the halo's hlen
+// tokens positions pos0-hlen .. pos0-1 (the host has checked that the halo
+// holds every earlier position the cache keeps).  Slot p mod W <- token p for
+// the last min(W, pos0 + T_arg) positions, zero where no position lands.
+template <typename T>
+__global__ void cache_from_segment_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                          const T* __restrict__ hk, const T* __restrict__ hv,
+                                          T* __restrict__ rk, T* __restrict__ rv, int T_arg,
+                                          int hlen, long long pos0, int W, int D) {
+  const int slot = blockIdx.x, bh = blockIdx.y;
+  const bool val = blockIdx.z != 0;  // z = 0: keys, z = 1: values
+  const long long N = pos0 + T_arg, base = N - W;
+  // the position p = slot (mod W) inside [N - W, N)
+  const long long p = base + ((((long long)slot - base) % W) + W) % W;
+  const T* src = nullptr;
+  if (p >= pos0)
+    src = (val ? v : k) + ((size_t)bh * T_arg + (size_t)(p - pos0)) * D;
+  else if (p >= 0)
+    src = (val ? hv : hk) + ((size_t)bh * hlen + (size_t)(p - (pos0 - hlen))) * D;
+  T* dst = (val ? rv : rk) + ((size_t)bh * W + slot) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) dst[d] = src ? src[d] : to_t<T>(0.f);
+}
+
 template <typename T, int D, typename G>
 hipError_t launch_decode_typed(const Shape& s, const void* q, const void* k, const void* qw,
                                const void* kw, const void* v, const void* la, float* state,
@@ -209,6 +233,22 @@ hipError_t ring_fill_typed(const Shape& s, const void* k, const void* v, void* r
 }
 
 }  // namespace
+
+hipError_t launch_cache_from_segment(const Shape& s, const void* k, const void* v,
+                                     const void* hk, const void* hv, int hlen, long long pos0,
+                                     void* ring_k, void* ring_v, hipStream_t st) {
+  if (s.B * s.H == 0) return hipSuccess;
+  const dim3 grid(s.window, s.B * s.H, 2);  // dk == dv
+  if (s.dtype == 1)
+    hipLaunchKernelGGL(cache_from_segment_kernel<bf16>, grid, dim3(64), 0, st, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)hk, (const bf16*)hv, (bf16*)ring_k,
+                       (bf16*)ring_v, s.T, hlen, pos0, s.window, s.dk);
+  else
+    hipLaunchKernelGGL(cache_from_segment_kernel<float>, grid, dim3(64), 0, st, (const float*)k,
+                       (const float*)v, (const float*)hk, (const float*)hv, (float*)ring_k,
+                       (float*)ring_v, s.T, hlen, pos0, s.window, s.dk);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const Shape& s, const void* q, const void* k, const void* qw,
                          const void* kw, const void* v, const void* la, float* state,

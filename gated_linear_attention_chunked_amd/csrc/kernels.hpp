@@ -71,6 +71,14 @@ hipError_t launch_swa_fwd(const Shape& s, const void* q, const void* k, const vo
 hipError_t launch_ring_fill(const Shape& s, const void* k, const void* v, void* ring_k,
                             void* ring_v, hipStream_t st);
 
+// Window cache from the last segment of a sequence prefilled in segments: its
+// T tokens k, v [B, H, T, d] are positions pos0.., the hlen halo tokens hk, hv
+// [B, H, hlen, d] the positions just before (the host checks that they cover
+// what the cache keeps).
+hipError_t launch_cache_from_segment(const Shape& s, const void* k, const void* v,
+                                     const void* hk, const void* hv, int hlen, long long pos0,
+                                     void* ring_k, void* ring_v, hipStream_t st);
+
 // hT <- h0 (or zeros) for T == 0.
 hipError_t launch_state_copy(const Shape& s, const float* h0, float* hT, hipStream_t st);
 

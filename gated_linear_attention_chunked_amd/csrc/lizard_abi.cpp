@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued; no C++ exception leaves a call.
 #include "../../include/lizard.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -337,6 +338,27 @@ lizard_status_t lizard_hybrid_bwd_segment(
                          dgate, dmeta_k, dmeta_v, dhT, dh0, dmix, q_w, k_w, dq_w, dk_w, halo_k,
                          halo_v, halo_len, dhalo_k, dhalo_v, tail_dk, tail_dv, tail_len, ws,
                          ws_bytes, stream);
+}
+
+lizard_status_t lizard_window_cache_fill(const lizard_desc_t* desc, const void* k,
+                                         const void* v, const void* halo_k, const void* halo_v,
+                                         int32_t halo_len, int64_t pos0, void* ring_k,
+                                         void* ring_v, hipStream_t stream) {
+  lizard_status_t st = check_desc(desc, true);
+  if (st != LIZARD_OK) return st;
+  if (pos0 < 0 || halo_len < 0 || halo_len > desc->window || halo_len > pos0)
+    return LIZARD_E_SHAPE;
+  // positions before the segment that the cache keeps (the last w of pos0 + T)
+  const long long keep =
+      desc->T >= desc->window ? 0 : std::min<long long>(pos0, (long long)desc->window - desc->T);
+  if (halo_len < keep) return LIZARD_E_SHAPE;
+  if ((long long)desc->B * desc->H == 0) return LIZARD_OK;
+  if (!ring_k || !ring_v) return LIZARD_E_NULL;
+  if (desc->T > 0 && (!k || !v)) return LIZARD_E_NULL;
+  if (halo_len > 0 && (!halo_k || !halo_v)) return LIZARD_E_NULL;
+  return hip_status(lz::launch_cache_from_segment(to_shape(desc), k, v, halo_k, halo_v, halo_len,
+                                                  pos0, ring_k, ring_v, stream),
+                    stream);
 }
 
 lizard_status_t lizard_decode_step(const lizard_desc_t* desc, const void* q, const void* k,

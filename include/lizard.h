@@ -263,6 +263,30 @@ lizard_status_t lizard_hybrid_bwd_segment(
     int32_t halo_len, float* dhalo_k, float* dhalo_v, const float* tail_dk,
     const float* tail_dv, int32_t tail_len, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Decode window cache after a prefill run in segments (a chunked prefill that
+ * continues into generation; the anchor window of section 2(a) and the
+ * constant-memory generation of section 4 "Efficiency" of "Lizard: An
+ * Efficient Linearization Framework for Large Language Models", gist.science
+ * summary): ring_k, ring_v [B, H, w, d] (desc->dtype, overwritten) receive the
+ * cache lizard_hybrid_fwd returns for a whole prefill -- slot p mod w holds
+ * token p for the last min(w, pos0 + T) positions p, zeros in the other
+ * slots -- so that lizard_decode_step continues the sequence (pos = pos0 + T,
+ * state = the last segment's hT).
+ *   k, v [B, H, T, d]: the last segment's window keys (k_w when the window
+ *     branch has its own) and values, positions pos0 .. pos0 + T - 1;
+ *   halo_k, halo_v [B, H, halo_len, d]: the halo_len tokens before it,
+ *     positions pos0 - halo_len .. pos0 - 1, oldest first (both non-NULL when
+ *     halo_len > 0);
+ *   0 <= halo_len <= min(w, pos0), and when T < w at least the min(pos0, w - T)
+ *   tokens before the segment that the cache keeps (else LIZARD_E_SHAPE; the
+ *   segment run's own halo of min(w - 1, pos0) tokens is enough unless T = 0).
+ * desc: B, H, T, dk = dv, window and dtype are read (the rest must still be a
+ * valid descriptor).  A copy: no workspace, inputs read once. */
+lizard_status_t lizard_window_cache_fill(const lizard_desc_t* desc, const void* k, const void* v,
+                                         const void* halo_k, const void* halo_v,
+                                         int32_t halo_len, int64_t pos0, void* ring_k,
+                                         void* ring_v, hipStream_t stream);
+
 /* One constant-memory generation step for B sequences (desc->T is ignored): the
  * recurrent form of both branches, as the constant-memory inference of "Lizard:
  * An Efficient Linearization Framework for Large Language Models" (gist.science

@@ -117,6 +117,24 @@ def test_packed_forward_arguments_are_checked():
     assert call(desc(dk=128, dv=128, T=4096, B=0)) == 0       # nothing to do
 
 
+def test_window_cache_fill_arguments_are_checked():
+    # cache from the last segment of a segmented prefill: the halo must hold the
+    # positions before the segment that the last w of pos0 + T keep
+    lib = _abi.lib()
+    call = lambda d, halo_len, pos0, k=FAKE, hk=FAKE, rk=FAKE: lib.lizard_window_cache_fill(
+        ctypes.byref(d), k, FAKE, hk, FAKE, halo_len, pos0, rk, FAKE, None)
+    d = desc(T=50, window=64)                 # T < w: min(pos0, 14) halo tokens needed
+    assert call(d, 13, 100) == 2
+    assert call(d, 10, 10, hk=None) == 1      # enough halo, but no halo pointer
+    assert call(d, 14, 100, rk=None) == 1
+    assert call(d, 5, -1) == 2                # negative start
+    assert call(d, 65, 100) == 2              # more than w halo tokens
+    assert call(d, 6, 5) == 2                 # more halo than tokens before
+    assert call(desc(T=0, window=64), 63, 100) == 2   # an empty segment needs all w
+    assert call(desc(T=70, window=64, B=0), 0, 100, k=None, hk=None, rk=None) == 0
+    assert call(desc(T=70, window=64), 0, 100, k=None) == 1
+
+
 def test_empty_problems_enqueue_nothing():
     # B*H == 0: valid, nothing to do, no HIP call
     assert gla(desc(B=0), q=None, k=None, v=None, la=None, o=None) == 0

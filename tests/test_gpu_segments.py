@@ -9,7 +9,10 @@ gradient to the segment before as its tail gradient.  Every output and
 gradient must equal the unsplit oracle's (meta and mix gradients summed over
 segments).  Cases: three segments with windows crossing both cuts, a halo
 shorter than w-1, d = 128, fp32, separate window queries and keys, gate logits,
-and a 32768-token sequence in eight segments (sampled head).
+and a 32768-token sequence in eight segments (sampled head).  A segmented
+prefill then continues into decoding: lizard_window_cache_fill builds the
+decode window cache from the last segment and its halo (bit for bit the
+oracle's cache after the whole prefill) and decode steps follow the oracle.
 """
 import math
 
@@ -20,7 +23,7 @@ import torch
 import gated_linear_attention_chunked_amd as lz
 import oracle
 from tests._gpu_helpers import assert_close, f64, to_dev
-from workloads import make_inputs
+from workloads import make_decode_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -148,3 +151,64 @@ def test_long_sequence_eight_segments():
     # sequence
     T = 32768
     check(1, 2, T, tuple(range(4096, T, 4096)), 64, 64, 4, seed=9, heads=[1])
+
+
+@pytest.mark.parametrize("T,w,cuts,dtype", [
+    (600, 64, [300], "bf16"),   # last segment longer than the window
+    (300, 128, [250], "bf16"),  # last segment shorter: the cache reaches into the halo
+    (40, 64, [25], "f32"),      # sequence shorter than the window: zero slots
+    (200, 64, [], "bf16"),      # one segment from position 0: the prefill's own cache
+])
+def test_window_cache_after_segments_continues_decoding(T, w, cuts, dtype):
+    """A prefill run in segments, then lizard_window_cache_fill on the last one,
+    then decode steps: the cache equals the oracle's after the whole prefill
+    (bit for bit: a copy) and the decode outputs follow the unsplit oracle."""
+    B, H, d, M = 2, 2, 64, 4
+    print(f"[case] window cache after segments T{T} w{w} cuts{cuts} {dtype}", flush=True)
+    s, mix = 1.0 / math.sqrt(d), 0.8
+    dt = DT[dtype]
+    inp = make_inputs(B, H, T, d, d, M, dtype=dtype, seed=T + w, with_h0=True)
+    x = to_dev(inp)
+    part = lambda t, a, b: t[:, :, a:b].contiguous()
+    bounds = [0] + list(cuts) + [T]
+    h = x["h0"]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        L = min(w - 1, a)
+        halo = dict(halo_k=part(x["k"], a - L, a), halo_v=part(x["v"], a - L, a)) if L else {}
+        f = lz.hybrid_fwd(part(x["q"], a, b), part(x["k"], a, b), part(x["v"], a, b),
+                          part(x["log_alpha"], a, b), x["meta_k"], x["meta_v"], w, scale=s,
+                          mix=mix, h0=h, return_state=True, return_ring=not L, **halo)
+        h = f["hT"]
+    rk, rv = lz.window_cache_fill(part(x["k"], a, T), part(x["v"], a, T), w, a, **halo)
+    torch.cuda.synchronize()
+    r = f64(inp)
+    ref = oracle.hybrid_forward(r["q"], r["k"], r["v"], r["log_alpha"], r["meta_k"], r["meta_v"],
+                                w, s, mix=mix, h0=r["h0"])
+    assert_close("ring_k", rk, ref["ring_k"], dt, tol=0.0)
+    assert_close("ring_v", rv, ref["ring_v"], dt, tol=0.0)
+    if not cuts:  # the same cache as the prefill call itself returned
+        assert torch.equal(rk, f["ring_k"]) and torch.equal(rv, f["ring_v"])
+    assert_close("hT", h, ref["hT"], dt)
+    # an empty last segment: all w cache tokens come from its halo
+    L = min(w, T)
+    rk0, rv0 = lz.window_cache_fill(part(x["k"], T, T), part(x["v"], T, T), w, T,
+                                    halo_k=part(x["k"], T - L, T), halo_v=part(x["v"], T - L, T))
+    torch.cuda.synchronize()
+    assert torch.equal(rk0, rk) and torch.equal(rv0, rv)
+    # decoding continues from the segmented prefill
+    dec = make_decode_inputs(3, B, H, d, d, dtype=dtype, seed=T + 1)
+    rd = f64(dec)
+    state = h.clone()
+    pos = torch.full((B,), T, dtype=torch.int64, device="cuda")
+    st_ref, rk_ref, rv_ref, pos_ref = ref["hT"], ref["ring_k"], ref["ring_v"], np.full(B, T)
+    for i in range(3):
+        o = lz.decode_step(dec["q"][i].cuda(), dec["k"][i].cuda(), dec["v"][i].cuda(),
+                           dec["log_alpha"][i].cuda(), state, rk, rv, pos, x["meta_k"],
+                           x["meta_v"], scale=s, mix=mix)
+        torch.cuda.synchronize()
+        o_ref, st_ref, rk_ref, rv_ref, pos_ref = oracle.decode_step(
+            rd["q"][i], rd["k"][i], rd["v"][i], rd["log_alpha"][i], st_ref, rk_ref, rv_ref,
+            pos_ref, r["meta_k"], r["meta_v"], w, s, mix=mix)
+        assert_close(f"decode[{i}].o", o, o_ref, dt)
+    assert_close("decode.ring_k", rk, rk_ref, dt, tol=0.0)
+    assert_close("decode.state", state, st_ref, dt)
