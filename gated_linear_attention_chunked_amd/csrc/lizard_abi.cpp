@@ -13,7 +13,7 @@ namespace {
 
 using lz::Shape;
 
-constexpr int32_t kVersion = 10100;  // 1.1.0
+constexpr int32_t kVersion = 10200;  // 1.2.0: lizard_window_cache_fill
 
 lizard_status_t check_desc(const lizard_desc_t* d, bool need_T) {
   if (!d) return LIZARD_E_NULL;

@@ -56,7 +56,7 @@ def test_status_strings_and_version():
     for code in range(8):
         assert lib.lizard_status_str(code)
     assert lib.lizard_status_str(99) == b"unknown status"
-    assert lib.lizard_version() == 10100
+    assert lib.lizard_version() == 10200
 
 
 @pytest.mark.parametrize("kw,status", [
