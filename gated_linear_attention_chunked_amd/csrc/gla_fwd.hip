@@ -286,8 +286,8 @@ template <typename T, int DK>
 __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ la, const float* __restrict__ h0, const float* __restrict__ ws_state,
-    const float* __restrict__ ws_gamma, T* __restrict__ o, float* __restrict__ hT, int T_len,
-    int cps, int G) {
+    const float* __restrict__ ws_gamma, T* __restrict__ o, float* __restrict__ hT, int T_arg,
+    int cps, int G, const int* __restrict__ cu, int N, int H) {
   constexpr int NCB = DK / 16;
   constexpr int KS = DK / 32;
   constexpr int NW = DK / 16;
@@ -301,7 +301,9 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
   const int cp = tid % (DK / 2), rg = tid / (DK / 2);
   const int i_sub = rg >> 1;  // 16-row sub-block of this thread's rows
   const int seg = blockIdx.x, bh = blockIdx.y;
-  const size_t off = (size_t)bh * T_len * DK;
+  const SeqRows sr = seq_rows(cu, N, T_arg, H, bh);
+  const int T_len = sr.len;
+  const size_t off = sr.row0 * DK;
   const u32 nbytes = (u32)((size_t)T_len * DK * sizeof(T));
   const Buf bq(q + off, nbytes), bk(k + off, nbytes), bv(v + off, nbytes);
   const Buf bla(la + off, (u32)((size_t)T_len * DK * 4));
@@ -309,6 +311,14 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
   const int c_begin = seg * cps, c_end = min(nc, c_begin + cps);
   const int ncol = 16 * wave;
   const size_t s_base = (size_t)bh * DK * DK;
+  // a packed sequence covers the first Gs of the plan's segments
+  const int Gs = cu ? max(1, (nc + cps - 1) / cps) : G;
+  if (seg >= Gs) return;
+  if (nc == 0) {  // an empty packed sequence: the state passes through unchanged
+    if (hT)
+      for (int e = tid; e < DK * DK; e += 4 * DK) hT[s_base + e] = h0 ? h0[s_base + e] : 0.f;
+    return;
+  }
 
   // state slice S[16cb + 4g + r][ncol + r16] entering the segment: h0 carried
   // through the earlier segments' local end states and decays
@@ -538,7 +548,7 @@ __global__ __launch_bounds__(4 * DK, 1) void gla_output_pass(
     }
   }
 
-  if (hT && seg == G - 1) {
+  if (hT && seg == Gs - 1) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -1083,7 +1093,8 @@ hipError_t launch_typed(const Shape& s, const Plan& pl, const void* q, const voi
   } else {
     static_assert(sizeof(GT) == 4, "fp32 problems take float log gates");
     hipLaunchKernelGGL((gla_output_pass<T, DK>), dim3(pl.G, BH), dim3(4 * DK), 0, st, (const T*)q,
-                       (const T*)k, (const T*)v, la, h0, ws_state, ws_gamma, (T*)o, hT, s.T, pl.cps, pl.G);
+                       (const T*)k, (const T*)v, la, h0, ws_state, ws_gamma, (T*)o, hT, s.T, pl.cps, pl.G,
+                       s.cu, s.n_tokens, s.H);
   }
   return hipGetLastError();
 }

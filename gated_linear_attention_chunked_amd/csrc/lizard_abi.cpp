@@ -239,8 +239,8 @@ lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_
   if ((ring_k == nullptr) != (ring_v == nullptr)) return LIZARD_E_NULL;
   if (desc->n_meta > 0 && desc->H > 0 && (!meta_k || !meta_v)) return LIZARD_E_NULL;
   Shape s = to_shape(desc);
-  // packed batches: bf16 problems (the fp32 output pass has no packed form)
-  if (desc->T < 1 || desc->dtype != LIZARD_BF16) return LIZARD_E_UNSUPPORTED;
+  // the longest length bounds the kernels' grids
+  if (desc->T < 1) return LIZARD_E_UNSUPPORTED;
   // per-head token rows are addressed with 32-bit byte offsets
   if ((long long)n_tokens * desc->dk * 4 >= (1LL << 31)) return LIZARD_E_UNSUPPORTED;
   const size_t need = lz::gla_fwd_workspace_bytes(s);

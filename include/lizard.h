@@ -177,8 +177,8 @@ lizard_status_t lizard_hybrid_fwd(const lizard_desc_t* desc, const void* q, cons
  * Efficient Linearization Framework for Large Language Models", gist.science
  * summary, section 2(a), starts from h0 at each sequence's first token, and no
  * window reaches into another sequence).  Inference outputs only (no lse,
- * o_swa); BF16 only (LIZARD_E_UNSUPPORTED for F32).  ws must hold
- * lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) bytes. */
+ * o_swa); BF16 and F32, desc->T >= 1 (else LIZARD_E_UNSUPPORTED).  ws must
+ * hold lizard_workspace_bytes(desc, LIZARD_OP_HYBRID_FWD) bytes. */
 lizard_status_t lizard_hybrid_fwd_varlen(const lizard_desc_t* desc, const int32_t* cu_seqlens,
                                          int32_t n_tokens, const void* q, const void* k,
                                          const void* v, const void* gate, const void* meta_k,

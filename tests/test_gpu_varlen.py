@@ -5,8 +5,8 @@ Each sequence's o rows, final state and window cache must match the oracle's
 single-sequence forward (its own h0, no window reaching into a neighbour).
 Cases: lengths 0, 1, chunk-aligned and ragged, several state segments, a bound
 max_seqlen larger than every length, d = 64 and windows past 129 (the
-two-kernel path, with the streaming and the tiled window kernels), an initial
-state per sequence, gate logits and separate window inputs, decode continuing
+two-kernel path, with the streaming and the tiled window kernels), fp32, an
+initial state per sequence, gate logits and separate window inputs, decode continuing
 every sequence from its own position, and the serving-mix workload (16
 sequences of 64..8192 tokens, H=32, d=128) on sampled sequences and heads.
 """
@@ -50,17 +50,17 @@ def run(inp, w, s, mix, max_seqlen, sep=False, logits=False):
     return out
 
 
-def check_all(inp, out, w, s, mix, sep=False, logits=False, seqs=None, heads=None):
+def check_all(inp, out, w, s, mix, sep=False, logits=False, seqs=None, heads=None, dt=BF):
     cu = inp["cu_seqlens"].tolist()
     hs = list(range(inp["q"].shape[0])) if heads is None else heads
     for b in (range(len(cu) - 1) if seqs is None else seqs):
         ref = seq_ref(inp, b, w, s, mix, heads, sep, logits)
         L = cu[b + 1] - cu[b]
         if L:
-            assert_close(f"o[seq {b}, len {L}]", out["o"][hs, cu[b]:cu[b + 1]][None], ref["o"], BF)
-        assert_close(f"hT[seq {b}]", out["hT"][b:b + 1, hs], ref["hT"], BF)
-        assert_close(f"ring_k[seq {b}]", out["ring_k"][b:b + 1, hs], ref["ring_k"], BF, tol=0.0)
-        assert_close(f"ring_v[seq {b}]", out["ring_v"][b:b + 1, hs], ref["ring_v"], BF, tol=0.0)
+            assert_close(f"o[seq {b}, len {L}]", out["o"][hs, cu[b]:cu[b + 1]][None], ref["o"], dt)
+        assert_close(f"hT[seq {b}]", out["hT"][b:b + 1, hs], ref["hT"], dt)
+        assert_close(f"ring_k[seq {b}]", out["ring_k"][b:b + 1, hs], ref["ring_k"], dt, tol=0.0)
+        assert_close(f"ring_v[seq {b}]", out["ring_v"][b:b + 1, hs], ref["ring_v"], dt, tol=0.0)
 
 
 @pytest.mark.parametrize("lengths,d,w,M,bound", [
@@ -77,6 +77,20 @@ def test_packed_forward_matches_each_sequence(lengths, d, w, M, bound):
     inp = make_packed_inputs(lengths, 2, d, d, M, seed=sum(lengths) % 97, with_h0=True)
     out = run(inp, w, s, mix, max(max(lengths), bound, 1))
     check_all(inp, out, w, s, mix)
+
+
+@pytest.mark.parametrize("lengths,d,w,M", [
+    ([0, 1, 65, 300, 1300, 64], 64, 64, 4),   # streaming window kernel
+    ([257, 0, 900, 3], 128, 128, 2),           # d = 128: tiled window kernel
+    ([700, 64, 1500], 64, 200, 0),             # tiled window, several state segments
+])
+def test_packed_forward_fp32(lengths, d, w, M):
+    print(f"[case] varlen fp32 lengths {lengths} d{d} w{w} M{M}", flush=True)
+    s, mix = 1.0 / math.sqrt(d), 0.75
+    inp = make_packed_inputs(lengths, 2, d, d, M, dtype="f32", seed=len(lengths) + d,
+                             with_h0=True)
+    out = run(inp, w, s, mix, max(lengths))
+    check_all(inp, out, w, s, mix, dt=torch.float32)
 
 
 @pytest.mark.parametrize("d,w", [(128, 100), (64, 64), (64, 180)])
