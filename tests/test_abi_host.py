@@ -113,6 +113,7 @@ def test_packed_forward_arguments_are_checked():
     assert call(d, qw=FAKE) == 1
     assert call(d, ws_bytes=need - 1) == 5
     assert call(desc(T=4096, dtype=_abi.LIZARD_F32, gate=_abi.LIZARD_GATE_LOGIT)) == 4  # logits: bf16
+    assert call(desc(T=4096, dtype=_abi.LIZARD_F32), cu=None) == 1  # fp32 packed: checked like bf16
     assert call(desc(dk=128, dv=128, T=0)) == 4               # the longest length must be >= 1
     assert call(desc(dk=128, dv=128, T=4096, B=0)) == 0       # nothing to do
 
