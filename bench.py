@@ -55,10 +55,15 @@ def decode_bytes_per_step(B, H, d, w, M, pos):
 
 
 def source_digest(*names):
+    """Digest of the kernel sources and of the per-source build flags they add
+    (a flag change alters the code as a source change does)."""
+    from gated_linear_attention_chunked_amd.build import EXTRA_FLAGS
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "gated_linear_attention_chunked_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        if EXTRA_FLAGS.get(n):
+            h.update(" ".join(EXTRA_FLAGS[n]).encode())
     return h.hexdigest()[:16]
 
 

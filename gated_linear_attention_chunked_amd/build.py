@@ -25,6 +25,18 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The backward kernels are scheduled by LLVM's
+# memory-clause strategy, which groups their loads into clauses: on the
+# B8 H16 T2048 d64 training step the per-chunk gradient kernel went from 130.9
+# to 125.7 us and the step from 0.366 to 0.360 ms.  The forward kernels keep
+# the default schedule (the same strategy made the single-pass prefill kernel
+# about 1.5 us slower there).
+EXTRA_FLAGS = {
+    "gla_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "swa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+}
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -33,7 +45,7 @@ def hipcc():
 
 
 def _compile(src, obj):
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
