@@ -28,12 +28,14 @@ HIPCC_FLAGS = [
 # Per-source additions.  The backward kernels are scheduled by LLVM's
 # memory-clause strategy, which groups their loads into clauses: on the
 # B8 H16 T2048 d64 training step the per-chunk gradient kernel went from 130.9
-# to 125.7 us and the step from 0.366 to 0.360 ms.  The forward kernels keep
-# the default schedule (the same strategy made the single-pass prefill kernel
-# about 1.5 us slower there).
+# to 125.7 us and the step from 0.366 to 0.360 ms.  The decode step takes the
+# ILP strategy (B64 H32 d128: 68.4-68.9 -> 67.9 us per step).  The prefill
+# kernels keep the default schedule (both strategies made the single-pass
+# kernel slower or spill).
 EXTRA_FLAGS = {
     "gla_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "swa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 
