@@ -202,9 +202,12 @@ __device__ __forceinline__ float gate_log2_nofloor(float x, bf16) {
   const float t = x * kLog2e;
   return fminf(t, 0.f) - log2_fast(1.f + exp2_fast(-fabsf(t)));
 }
+// (a compare and select, not fmaxf: a NaN gate stays NaN and reaches the
+// outputs, where fmaxf would return the floor)
 template <typename GT>
 __device__ __forceinline__ float gate_log2(float v, GT) {
-  return fmaxf(gate_log2_nofloor(v, GT()), kMinLog2Gate);
+  const float t = gate_log2_nofloor(v, GT());
+  return t < kMinLog2Gate ? kMinLog2Gate : t;
 }
 // d log(alpha) / dx = sigmoid(-x) = 1 / (1 + 2^{x log2(e)}) for a logit x; 1 for
 // log alpha itself.
