@@ -115,6 +115,7 @@ __device__ __forceinline__ void lds_barrier() {
 // offsets fold into the instruction's immediate field.
 typedef unsigned int u32;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 struct U2 {
   u32 a, b;
 };
@@ -150,6 +151,11 @@ __device__ __forceinline__ float dot2_bf16(u32 x, u32 y, float acc) {
 }
 // bf16 element c (0..7) of a 16-byte word as fp32
 __device__ __forceinline__ float bf_at(const u32x4& v, int c) {
+  const u32 w = v[c >> 1];
+  return (c & 1) ? bf_hi(w) : bf_lo(w);
+}
+// bf16 element c (0..3) of an 8-byte word as fp32
+__device__ __forceinline__ float bf_at(const u32x2& v, int c) {
   const u32 w = v[c >> 1];
   return (c & 1) ? bf_hi(w) : bf_lo(w);
 }
@@ -345,7 +351,6 @@ __device__ __forceinline__ u32 lo2(u32 a, u32 b) { return (a & 0xffffu) | (b << 
 __device__ __forceinline__ u32 hi2(u32 a, u32 b) { return (a >> 16) | (b & 0xffff0000u); }
 __device__ __forceinline__ bf16x8 as_bf8(const u32x4& x) { return __builtin_bit_cast(bf16x8, x); }
 
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 // 8 bytes through a buffer view (elements read out as with Buf::ld128)
 __device__ __forceinline__ u32x2 ld64v(const Buf& b, u32 off) {
   return __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
@@ -368,6 +373,9 @@ struct Gate4 {
       return (r & 1) ? bf_hi(w[r >> 1]) : bf_lo(w[r >> 1]);
   }
   __device__ __forceinline__ float log2_at(int r) const { return gate_log2(raw_at(r), G()); }
+  __device__ __forceinline__ float log2_nofloor_at(int r) const {
+    return gate_log2_nofloor(raw_at(r), G());
+  }
 };
 
 __device__ __forceinline__ int wave_id() {  // wave index as a scalar (uniform) value

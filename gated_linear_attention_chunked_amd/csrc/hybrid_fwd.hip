@@ -26,7 +26,7 @@
 //              values), each scaled by f_h mix / (f_0 l_0 + f_1 l_1) with
 //              f_h = 2^{(m_h - max(m_0, m_1)) scale}; store o; v of chunk c+1
 //              into the V^T ring
-//            producers (D/32 of them, 32 channels each): gate chunk c+1
+//            producers (D/4 channels each): gate chunk c+1
 //              (log2-gate cumsum, gated q and k tiles, k^T for the state
 //              update), raw q and raw k of c+1 into LDS; issue the loads of c+3
 //   ---- barrier
@@ -143,7 +143,12 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   constexpr int CW = D / 4;     // value columns per consumer wave
   constexpr int NCB = D / 16;   // 16-row blocks of the state
   constexpr int KS = D / 32;    // contraction steps over channels
-  constexpr int NPW = D / 32;   // producer waves that gate (32 channels each)
+  // Every producer wave gates D/4 channels, CPL per lane: at D = 128 eight
+  // (16-byte rows of q and k), at D = 64 four, so that all four producers
+  // share the gating instead of two of them taking 32 channels each.
+  constexpr int CPL = D / 16;   // channels per gating lane
+  using RawV = typename std::conditional<CPL == 8, u32x4, u32x2>::type;  // CPL bf16
+  using GateV = typename std::conditional<CPL == 8, Gate8<GT>, Gate4<GT>>::type;
   constexpr int NR0 = (RING + 1) / 2;  // ring chunks in the first key half
   static_assert(D == 64 || D == 128, "head size");
   static_assert(RING == 3 || RING == 5, "ring");
@@ -166,7 +171,6 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   // tiles that stay zero: the intra block above the diagonal, unused meta columns
   for (int e = tid; e < 16 * 16; e += 512) sm.a[at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
   for (int e = tid; e < kC * 16; e += 512) sm.p[kRing][at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
-  if (tid >= NPW && tid < 4) sm.fastw[tid] = 1;  // producers that do not gate: flag 1
   {
     const bf16* mkh = mk + (size_t)h * M * kD;
     const bf16* mvh = mv + (size_t)h * M * kD;
@@ -438,16 +442,27 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     // bf16 logits, which adds a log-sigmoid per element, stays raised (0.152
     // against 0.156 ms lowered).
     __builtin_amdgcn_s_setprio(2);
-    const int pw = wave - 4;                    // gating (pw < NPW): channels 32pw .. 32pw+31
-    const bool gater = pw < NPW;
-    const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+7, rows 2rq, 2rq+1
-    const int ch0 = 32 * pw + 8 * ol;
+    const int pw = wave - 4;                    // gates channels 4 CPL pw .. 4 CPL pw + 4 CPL - 1
+    const int ol = lane >> 4, rq = lane & 15;   // channels ch0 .. ch0+CPL-1, rows 2rq, 2rq+1
+    const int ch0 = 4 * CPL * pw + CPL * ol;
     const int isub = rq >> 3;                   // 16-row sub-block of the rows
     const u32 oe = (u32)(2 * rq * kD + ch0), o2 = oe * 2;
     struct In {
-      u32x4 q[2], k[2];
-      Gate8<GT> la[2];
-      u32x4 wq[2], wk[2];  // window queries and keys (kSep only)
+      RawV q[2], k[2];
+      GateV la[2];
+      RawV wq[2], wk[2];  // window queries and keys (kSep only)
+    };
+    auto ldv = [](const Buf& b, u32 o) -> RawV {
+      if constexpr (CPL == 8)
+        return b.ld128(o);
+      else
+        return ld64v(b, o);
+    };
+    auto packv = [](const u32 (&w)[CPL / 2]) -> RawV {
+      if constexpr (CPL == 8)
+        return u32x4{w[0], w[1], w[2], w[3]};
+      else
+        return u32x2{w[0], w[1]};
     };
     auto issue = [&](int ch, In& x) {
       const size_t e0 = off + (size_t)ch * kC * kD;
@@ -455,16 +470,16 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       const Buf bq(q + e0, rem * 2), bk(k + e0, rem * 2), bl(la + e0, rem * (u32)sizeof(GT));
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        x.q[rr] = bq.ld128(o2 + rr * kD * 2);
-        x.k[rr] = bk.ld128(o2 + rr * kD * 2);
+        x.q[rr] = ldv(bq, o2 + rr * kD * 2);
+        x.k[rr] = ldv(bk, o2 + rr * kD * 2);
         x.la[rr].load(bl, oe + rr * kD);
       }
       if constexpr (kSep) {
         const Buf bwq(qw + e0, rem * 2), bwk(kw + e0, rem * 2);
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
-          x.wq[rr] = bwq.ld128(o2 + rr * kD * 2);
-          x.wk[rr] = bwk.ld128(o2 + rr * kD * 2);
+          x.wq[rr] = ldv(bwq, o2 + rr * kD * 2);
+          x.wk[rr] = ldv(bwk, o2 + rr * kD * 2);
         }
       }
     };
@@ -474,10 +489,10 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       // The sums are first taken without the gate floor; only when some
       // channel's chunk total falls below the floor (then a token may lie
       // below it) are they taken again with it.
-      float b[2][8], inc[8], blast[8], bmin = 0.f;
+      float b[2][CPL], inc[CPL], blast[CPL], bmin = 0.f;
       auto scan = [&](auto floored) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CPL; ++c) {
           float run = 0.f;
 #pragma unroll
           for (int rr = 0; rr < 2; ++rr) {
@@ -488,15 +503,15 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           inc[c] = run;
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<1>(inc[c]);
+        for (int c = 0; c < CPL; ++c) inc[c] += dpp_shr<1>(inc[c]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<2>(inc[c]);
+        for (int c = 0; c < CPL; ++c) inc[c] += dpp_shr<2>(inc[c]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<4>(inc[c]);
+        for (int c = 0; c < CPL; ++c) inc[c] += dpp_shr<4>(inc[c]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) inc[c] += dpp_shr<8>(inc[c]);
+        for (int c = 0; c < CPL; ++c) inc[c] += dpp_shr<8>(inc[c]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CPL; ++c) {
           const float ex = inc[c] - b[1][c];
           b[0][c] += ex;
           b[1][c] += ex;
@@ -508,51 +523,53 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       if (__any(bmin < kMinLog2Gate)) scan(std::true_type());  // uniform over the wave
       const bool fast = !__any(bmin < -kFast);  // uniform over the wave
       if (lane == 0) sm.fastw[pw] = fast ? 1 : 0;
-      float dl[8];  // 2^{b_last}
+      float dl[CPL];  // 2^{b_last}
 #pragma unroll
-      for (int c = 0; c < 8; ++c) dl[c] = exp2_fast(blast[c]);
+      for (int c = 0; c < CPL; ++c) dl[c] = exp2_fast(blast[c]);
       if (rq == 0) {
-        *reinterpret_cast<f32x4*>(&sm.decay[ch0]) = f32x4{dl[0], dl[1], dl[2], dl[3]};
-        *reinterpret_cast<f32x4*>(&sm.decay[ch0 + 4]) = f32x4{dl[4], dl[5], dl[6], dl[7]};
+#pragma unroll
+        for (int c = 0; c < CPL; c += 4)
+          *reinterpret_cast<f32x4*>(&sm.decay[ch0 + c]) = f32x4{dl[c], dl[c + 1], dl[c + 2], dl[c + 3]};
       }
       // references: none (fast) or b at row 16i+7 for sub-block i; eKh = 2^{b_last - R_i}
-      float Ri[8], eKh[8];
+      float Ri[CPL], eKh[CPL];
       if (fast) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CPL; ++c) {
           Ri[c] = 0.f;
           eKh[c] = dl[c];
         }
         if (rq < 3) {  // the sub-block tables read 1 for these channels
           float* dst = rq < 2 ? &sm.eR[rq][ch0] : &sm.vij[ch0];
-          *reinterpret_cast<f32x4*>(dst) = f32x4{1.f, 1.f, 1.f, 1.f};
-          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+          for (int c = 0; c < CPL; c += 4) *reinterpret_cast<f32x4*>(dst + c) = f32x4{1.f, 1.f, 1.f, 1.f};
         }
       } else {
-        float R0[8], R1[8];  // rows 7 and 23: the second row of row pairs 3 and 11
+        float R0[CPL], R1[CPL];  // rows 7 and 23: the second row of row pairs 3 and 11
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < CPL; ++c) {
           R0[c] = dpp_bcast<3>(b[1][c]);
           R1[c] = dpp_bcast<11>(b[1][c]);
           Ri[c] = isub ? R1[c] : R0[c];
           eKh[c] = exp2_fast(blast[c] - Ri[c]);
         }
         if (rq < 3) {
-          float e[8];
+          float e[CPL];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) e[c] = exp2_fast(rq == 0 ? R0[c] : rq == 1 ? R1[c] : R1[c] - R0[c]);
+          for (int c = 0; c < CPL; ++c) e[c] = exp2_fast(rq == 0 ? R0[c] : rq == 1 ? R1[c] : R1[c] - R0[c]);
           float* dst = rq < 2 ? &sm.eR[rq][ch0] : &sm.vij[ch0];
-          *reinterpret_cast<f32x4*>(dst) = f32x4{e[0], e[1], e[2], e[3]};
-          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{e[4], e[5], e[6], e[7]};
+#pragma unroll
+          for (int c = 0; c < CPL; c += 4)
+            *reinterpret_cast<f32x4*>(dst + c) = f32x4{e[c], e[c + 1], e[c + 2], e[c + 3]};
         }
       }
       // gated tiles, rounded to bf16 pairs as they are made (the element loop
       // is specialised on the uniform form: the single reference is 0)
-      u32 qw[2][4], kw[2][4];
+      u32 qw[2][CPL / 2], kw[2][CPL / 2];
       auto tiles = [&](auto single) {
         constexpr bool kSingle = decltype(single)::value;
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
+        for (int c2 = 0; c2 < CPL / 2; ++c2) {
           float kx[2][2];
 #pragma unroll
           for (int rr = 0; rr < 2; ++rr) {
@@ -583,10 +600,10 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int row = 2 * rq + rr;
-        *reinterpret_cast<u32x4*>(&sm.qs[atd<D>(row, ch0)]) = u32x4{qw[rr][0], qw[rr][1], qw[rr][2], qw[rr][3]};
-        *reinterpret_cast<u32x4*>(&sm.ks[atd<D>(row, ch0)]) = u32x4{kw[rr][0], kw[rr][1], kw[rr][2], kw[rr][3]};
-        *reinterpret_cast<u32x4*>(&sm.qr[atd<D>(row, ch0)]) = kSep ? x.wq[rr] : x.q[rr];
-        *reinterpret_cast<u32x4*>(&kring[atd<D>(row, ch0)]) = kSep ? x.wk[rr] : x.k[rr];
+        *reinterpret_cast<RawV*>(&sm.qs[atd<D>(row, ch0)]) = packv(qw[rr]);
+        *reinterpret_cast<RawV*>(&sm.ks[atd<D>(row, ch0)]) = packv(kw[rr]);
+        *reinterpret_cast<RawV*>(&sm.qr[atd<D>(row, ch0)]) = kSep ? x.wq[rr] : x.q[rr];
+        *reinterpret_cast<RawV*>(&kring[atd<D>(row, ch0)]) = kSep ? x.wk[rr] : x.k[rr];
       }
     };
     // Window scores of query rows 16qb..16qb+15 of chunk c over one half of
@@ -684,25 +701,25 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
     // ---- prologue: the raw-K ring before the segment, chunk c_begin gated,
     // c_begin+1 and c_begin+2 in flight
     In I0, I1;
-    if (gater) {
+    {
       issue(c_begin, I0);
       issue(min(c_begin + 1, c_end - 1), I1);
-      u32x4 kp[kRing - 1][2];
+      RawV kp[kRing - 1][2];
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) {
         const int cr = c_begin - (kRing - 1) + r;
         if (cr >= 0) {
           const Buf bk(kw + off + (size_t)cr * kC * kD, (u32)(kC * kD * 2));
-          kp[r][0] = bk.ld128(o2);
-          kp[r][1] = bk.ld128(o2 + kD * 2);
+          kp[r][0] = ldv(bk, o2);
+          kp[r][1] = ldv(bk, o2 + kD * 2);
         }
       }
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r) {
         const int cr = c_begin - (kRing - 1) + r;
         if (cr >= 0) {
-          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][atd<D>(2 * rq, ch0)]) = kp[r][0];
-          *reinterpret_cast<u32x4*>(&sm.kr[cr % kRing][atd<D>(2 * rq + 1, ch0)]) = kp[r][1];
+          *reinterpret_cast<RawV*>(&sm.kr[cr % kRing][atd<D>(2 * rq, ch0)]) = kp[r][0];
+          *reinterpret_cast<RawV*>(&sm.kr[cr % kRing][atd<D>(2 * rq + 1, ch0)]) = kp[r][1];
         }
       }
       gate(c_begin, I0);
@@ -719,10 +736,8 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       if constexpr (D == 128 && sizeof(GT) == 4) __builtin_amdgcn_s_setprio(0);
       // past the segment end this gates an unused copy of the last chunk (no
       // branch around the loads, so their waits stay exact)
-      if (gater) {
-        gate(c + 1, Xn);
-        issue(min(c + 3, c_end - 1), Xn);
-      }
+      gate(c + 1, Xn);
+      issue(min(c + 3, c_end - 1), Xn);
       lds_barrier();  // (B)
       if constexpr (D == 128) __builtin_amdgcn_s_setprio(2);
     };
