@@ -171,6 +171,16 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
   // tiles that stay zero: the intra block above the diagonal, unused meta columns
   for (int e = tid; e < 16 * 16; e += 512) sm.a[at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
   for (int e = tid; e < kC * 16; e += 512) sm.p[kRing][at4(e >> 4, 16 + (e & 15))] = (bf16)0.f;
+  // window blocks no query block reaches (see the producers' window scores):
+  // rows 16..31 x keys 0..15 of the oldest ring chunk, rows 0..15 x keys
+  // 16..31 of chunk c
+  for (int e = tid; e < 2 * 16 * 16; e += 512) {
+    const int x = (e >> 4) & 15, y = e & 15;
+    if (e < 256)
+      sm.p[0][at4(16 + x, y)] = (bf16)0.f;
+    else
+      sm.p[RING - 1][at4(x, 16 + y)] = (bf16)0.f;
+  }
   {
     const bf16* mkh = mk + (size_t)h * M * kD;
     const bf16* mvh = mv + (size_t)h * M * kD;
@@ -354,10 +364,15 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
           }
         }
         const int s0 = (c + 1) % kRing;
+        // ring chunk NR0-1 belongs to half 0 for query rows 16..31; for rows
+        // 0..15 its keys 0..15 (lanes g < 2 of a fragment) are in half 0 and
+        // keys 16..31 in half 1
+        const bool klo = g < 2;
+        const bf16x8 z8 = {};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int r0 = h == 0 ? 0 : NR0, r1 = h == 0 ? NR0 - 1 : kRing;  // ring chunks (kRing: meta)
-          bf16x8 wf[NR0][NT], pf[NR0][2];
+          const int r0 = h == 0 ? 0 : NR0 - 1, r1 = h == 0 ? NR0 - 1 : kRing;  // ring chunks (kRing: meta)
+          bf16x8 wf[NR0 + 1][NT], pf[NR0 + 1][2];
 #pragma unroll
           for (int r = r0; r <= r1; ++r) {
             const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
@@ -367,7 +382,11 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
                              : r == kRing     ? ld8<bf16>(&sm.mvT[atp(CW * cw + 16 * nt + r16, 8 * g)])
                                               : ld8<bf16>(&sm.vT[sl][atp(CW * cw + 16 * nt + r16, 8 * g)]);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) pf[r - r0][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
+            for (int qb = 0; qb < 2; ++qb) {
+              if (h == 1 && r == NR0 - 1 && qb == 1) continue;
+              pf[r - r0][qb] = ld8<bf16>(&sm.p[r][at4(16 * qb + r16, 8 * g)]);
+              if (r == NR0 - 1 && qb == 0) pf[r - r0][qb] = (klo == (h == 0)) ? pf[r - r0][qb] : z8;
+            }
           }
           f32x4 Ow[NT][2];  // this half of the window branch, unnormalised
 #pragma unroll
@@ -379,7 +398,8 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-              for (int qb = 0; qb < 2; ++qb) mma(Ow[nt][qb], wf[r - r0][nt], pf[r - r0][qb]);
+              for (int qb = 0; qb < 2; ++qb)
+                if (!(h == 1 && r == NR0 - 1 && qb == 1)) mma(Ow[nt][qb], wf[r - r0][nt], pf[r - r0][qb]);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -607,14 +627,30 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       }
     };
     // Window scores of query rows 16qb..16qb+15 of chunk c over one half of
-    // the keys: the NR0 oldest ring chunks (half 0) or the newer ones, chunk c
-    // and the meta slots (half 1), one producer per (query block, half).  Each half's
-    // exponentials are taken from its own row maximum; the row maxima and sums
-    // go to LDS, and the consumers combine the two halves.
+    // their keys, one producer per (query block, half).  The 16-key blocks a
+    // query block can reach, oldest first, are every (ring chunk r, key half
+    // kb) but one that is outside every window the ring holds: (0, 0) for
+    // qb = 1 (at least max_window(RING) tokens back) and (RING-1, 1) for
+    // qb = 0 (after every query); with the meta block that is 2 RING blocks,
+    // RING per half.  Half 0 takes the first RING, half 1 the rest and the
+    // meta block, so for qb = 0 the halves meet inside ring chunk NR0-1 (its
+    // first 16 keys in half 0) and the consumers separate them by key lanes.
+    // Block j of half H is block id o + qb (id = 2 r + kb), o = j or RING + j.
+    // Each half's exponentials are taken from its own row maximum; the row
+    // maxima and sums go to LDS, and the consumers combine the two halves.
+    // The probabilities of the unreached blocks are zero from the start.
+    const int qbw = pw & 1;  // this producer's query block
+    int kq[KS], kn[KS];      // raw-K tile offsets of key rows 16kb + r16: kb = qb, kb = 1 - qb
+#pragma unroll
+    for (int p = 0; p < KS; ++p) {
+      kq[p] = atd<D>(16 * qbw + r16, 32 * p + 8 * g);
+      kn[p] = atd<D>(16 * (1 - qbw) + r16, 32 * p + 8 * g);
+    }
+    const int prow = 16 * qbw + r16;
+    const int pq = at4(prow, 16 * qbw + 4 * g), pn = at4(prow, 16 * (1 - qbw) + 4 * g);
     auto window = [&](int c, int qb, auto half) {
       constexpr int H = decltype(half)::value;
-      constexpr int R0 = H == 0 ? 0 : NR0, NR = H == 0 ? NR0 : kRing - NR0;  // ring chunks R0 .. R0+NR-1
-      constexpr int NB = 2 * NR + H;                           // 16-key blocks (+ the meta block)
+      constexpr int NB = kRing;  // blocks of this half (in half 1 the last is the meta block)
       bf16x8 qf[KS];
 #pragma unroll
       for (int p = 0; p < KS; ++p) qf[p] = ld8<bf16>(&sm.qr[atd<D>(16 * qb + r16, 32 * p + 8 * g)]);
@@ -622,48 +658,51 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       // every slot is multiplied (slots before the sequence start hold stale
       // data); the mask below selects -inf for every key outside the window
       const int s0 = (c + 1) % kRing;  // slot of chunk c-RING+1
+      // ring chunk of block j (kb = qb for even o, 1 - qb for odd o)
+      auto chunk_of = [&](int j) {
+        const int o = H == 0 ? j : kRing + j;
+        return (o >> 1) + ((o & 1) ? qb : 0);
+      };
       f32x4 L[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) L[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NB; ++j) L[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < NR + H; ++x) {
-        const bool meta = x == NR;
-        const int r = R0 + x;
-        const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
-        bf16x8 kf[2][KS];
+      for (int j = 0; j < NB; ++j) {
+        const bool meta = H == 1 && j == NB - 1;
+        const bool odd = ((H == 0 ? j : kRing + j) & 1) != 0;
+        bf16x8 kf[KS];
+        if (meta) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int p = 0; p < KS; ++p) kf[p] = ld8<bf16>(&sm.mk[atd<D>(r16, 32 * p + 8 * g)]);
+        } else {
+          const int r = chunk_of(j);
+          const int sl = s0 + r < kRing ? s0 + r : s0 + r - kRing;
 #pragma unroll
-          for (int p = 0; p < KS; ++p)
-            if (!meta || kb == 0)
-              kf[kb][p] = ld8<bf16>(meta ? &sm.mk[atd<D>(r16, 32 * p + 8 * g)]
-                                         : &sm.kr[sl][atd<D>(16 * kb + r16, 32 * p + 8 * g)]);
+          for (int p = 0; p < KS; ++p) kf[p] = ld8<bf16>(&sm.kr[sl][odd ? kn[p] : kq[p]]);
+        }
 #pragma unroll
-        for (int p = 0; p < KS; ++p)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (!meta || kb == 0) mma(L[2 * x + kb], kf[kb][p], qf[p]);
+        for (int p = 0; p < KS; ++p) mma(L[j], kf[p], qf[p]);
       }
       // keys outside the window -> -inf; a 16-key block inside the window of
       // all 16 rows (uniform test) needs no per-key test
       const int tlo = c * kC + 16 * qb;
 #pragma unroll
-      for (int x = 0; x < NR; ++x)
+      for (int j = 0; j < NB - H; ++j) {
+        const bool odd = ((H == 0 ? j : kRing + j) & 1) != 0;
+        const int kb = odd ? 1 - qb : qb;
+        const int slo = (c - (kRing - 1) + chunk_of(j)) * kC + 16 * kb;
+        const bool full = slo >= 0 && slo + 15 <= tlo && slo > tlo + 15 - W;
+        if (!full) {
+          // key s inside the window of query t: 0 <= t - s < W (one unsigned
+          // compare); keys before the sequence start only in its first chunks
+          const int dt = t - slo - 4 * g;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int slo = (c - (kRing - 1) + R0 + x) * kC + 16 * kb;
-          const bool full = slo >= 0 && slo + 15 <= tlo && slo > tlo + 15 - W;
-          if (!full) {
-            // key s inside the window of query t: 0 <= t - s < W (one unsigned
-            // compare); keys before the sequence start only in its first chunks
-            const int dt = t - slo - 4 * g;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const bool ok = (u32)(dt - i) < (u32)W && (slo >= 0 || slo + 4 * g + i >= 0);
-              L[2 * x + kb][i] = ok ? L[2 * x + kb][i] : -INFINITY;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = (u32)(dt - i) < (u32)W && (slo >= 0 || slo + 4 * g + i >= 0);
+            L[j][i] = ok ? L[j][i] : -INFINITY;
           }
         }
+      }
       if (H == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) L[NB - 1][i] = (4 * g + i < M) ? L[NB - 1][i] : -INFINITY;
@@ -673,28 +712,28 @@ __global__ __launch_bounds__(512, 1) void hybrid_fwd_fused(
       // the consumers' factor 2^{(m_h - m) s} underflows to 0
       float m = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, L[b][i]);
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, L[j][i]);
       m = fmaxf(swap_max16(m), -1e30f);
       const int row = 16 * qb + r16;
       if (g == 0) sm.pmax[H][row] = m;
       const float ms = -m * scale_log2;
       float l = 0.f;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          L[b][i] = exp2_fast(fmaf(L[b][i], scale_log2, ms));
-          l += L[b][i];
+          L[j][i] = exp2_fast(fmaf(L[j][i], scale_log2, ms));
+          l += L[j][i];
         }
       l = swap_sum16(l);
       if (g == 0) sm.psum[H][row] = l;
 #pragma unroll
-      for (int x = 0; x < NR; ++x)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          st4<bf16>(&sm.p[R0 + x][at4(row, 16 * kb + 4 * g)], L[2 * x + kb]);
+      for (int j = 0; j < NB - H; ++j) {
+        const bool odd = ((H == 0 ? j : kRing + j) & 1) != 0;
+        st4<bf16>(&sm.p[chunk_of(j)][odd ? pn : pq], L[j]);
+      }
       if (H == 1) st4<bf16>(&sm.p[kRing][at4(row, 4 * g)], L[NB - 1]);
     };
 
