@@ -18,9 +18,9 @@
 //              S_{c+1} = diag(2^{b_last}) S_c + (k 2^{b_last - b})^T V, and
 //              (waves 0-2, one 16x16 block each) the masked intra scores
 //            producers (waves 4-7): window scores of query rows 16(p&1).. over
-//              one half of the keys (the older ring chunks, or the newer ones
-//              with chunk c and the meta slots); exponentials from that half's
-//              own row maxima; maxima, row sums and exponentials -> LDS
+//              one half of the 16-key blocks they reach (the older blocks, or
+//              the newer ones with the meta slots); exponentials from that
+//              half's own row maxima; maxima, row sums and exponentials -> LDS
 //   ---- barrier
 //   phase 2  consumers: O += A V (intra) + the two halves' P V (V^T ring, meta
 //              values), each scaled by f_h mix / (f_0 l_0 + f_1 l_1) with
