@@ -274,7 +274,7 @@ def main():
                                                       stream), args.steps, args.warmup)
     hbytes = hybrid_bytes(B, H, T, d, w, M)
     achieved = hbytes / (ms / 1e3) / 1e9
-    traffic = counter_traffic(name, source_digest("gla_fwd.hip", "hybrid_fwd.hip", "common.hpp"))
+    traffic = counter_traffic(name, source_digest("gla_fwd.hip", "hybrid_fwd.hip", "hybrid_fwd.hpp", "common.hpp"))
 
     out = {
         "metric": "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW",
@@ -477,7 +477,7 @@ def train_bytes(B, H, T, d):
 
 
 TRAIN_SOURCES = ("common.hpp", "gla_fwd.hip", "swa_fwd.hip", "gla_bwd.hip", "swa_bwd.hip",
-                 "hybrid_bwd.hip", "hybrid_fwd.hip")
+                 "hybrid_bwd.hip", "hybrid_fwd.hip", "hybrid_fwd.hpp", "hybrid_fwd_d64.hip")
 
 
 def bench_train(lz, torch, dev, args):

@@ -29,13 +29,16 @@ HIPCC_FLAGS = [
 # memory-clause strategy, which groups their loads into clauses: on the
 # B8 H16 T2048 d64 training step the per-chunk gradient kernel went from 130.9
 # to 125.7 us and the step from 0.366 to 0.360 ms.  The decode step takes the
-# ILP strategy (B64 H32 d128: 68.4-68.9 -> 67.9 us per step).  The prefill
-# kernels keep the default schedule (both strategies made the single-pass
-# kernel slower or spill).
+# ILP strategy (B64 H32 d128: 68.4-68.9 -> 67.9 us per step).  The d = 64
+# instances of the single-pass hybrid forward take the ILP strategy too (no
+# spills; the B8 H16 T2048 training step 0.3468 -> 0.3438 ms); the d = 128
+# instances and the other prefill kernels keep the default schedule (both
+# strategies make the d = 128 single-pass kernel spill).
 EXTRA_FLAGS = {
     "gla_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "swa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "hybrid_fwd_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 
